@@ -1,0 +1,201 @@
+"""Block-quantized verify GEMM for MI355X (gfx950): thin Python binding of libvq.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libvq.so`` (built in-tree by ``block_quantized_gemm_amd.build``).
+There is no fallback: if the library is missing, every call raises.
+
+The C ABI is declared and documented in ``include/vq.h``.  The functions here
+take torch tensors on the current ROCm device, check their dtypes, shapes and
+contiguity, and pass raw pointers plus the current torch stream to the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvq.so")
+
+VQ_OK = 0
+VQ_ERR_NULL_POINTER = -1
+VQ_ERR_BAD_SHAPE = -2
+VQ_ERR_MISALIGNED = -3
+VQ_ERR_BAD_DTYPE = -4
+VQ_ERR_DEVICE = -5
+VQ_ERR_LAUNCH = -6
+VQ_ERR_BAD_CONFIG = -7
+
+DTYPE_F16 = 1
+DTYPE_BF16 = 2
+DTYPE_F32 = 3
+DTYPE_I8 = 4
+
+# Every symbol include/vq.h declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+SIGNATURES = {
+    "vq_gemm_q4_0": (_I, [_P, _P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _F, _P]),
+    "vq_gemm_fp8_blk128": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P]),
+    "vq_hadamard32_quant_int8": (_I, [_P, _I, _P, _P, _I64, _I64, _P]),
+    "vq_gemm_q4_0_ex": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _F, _I, _I, _P]),
+    "vq_gemm_fp8_blk128_ex": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _I, _I, _P]),
+    "vq_default_launch_shape": (_I, [_I, _I64, _I64, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "vq_status_string": (ctypes.c_char_p, [_I]),
+    "vq_version": (_I, []),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class VqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libvq.so.  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libvq.so is not built (run python -m block_quantized_gemm_amd.build); "
+                                   "there is no fallback path")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = handle
+        return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().vq_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != VQ_OK:
+        raise VqError(status, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32,
+         torch.int8: DTYPE_I8}
+    if t.dtype not in m:
+        raise TypeError("unsupported dtype %s" % t.dtype)
+    return m[t.dtype]
+
+
+def _dev_ptr(t, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _check_2d(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def gemm_q4_0(codes, scales, x, out, *, x_scales=None, alpha: float = 1.0, stream=None,
+              tiles_per_wave: int = 0, waves_k: int = 0):
+    """out[N][M] = alpha * x[N][K] @ dequant(codes, scales)[M][K]^T.
+
+    codes: uint8 [M][K/2]; scales: float16 [M][K/32]; x: float16 / bfloat16 [N][K]
+    or int8 [N][K] with x_scales float16 [N][K/32]; out: float16 / bfloat16 /
+    float32 [N][M].  tiles_per_wave / waves_k select an explicit launch shape
+    (float activations only; 0 = library default)."""
+    N, K = x.shape
+    M = codes.shape[0]
+    _check_2d(codes, "codes", (M, K // 2))
+    _check_2d(scales, "scales", (M, K // 32))
+    _check_2d(out, "out", (N, M))
+    act_dtype = _dtype_code(x)
+    L = lib()
+    if act_dtype == DTYPE_I8:
+        if x_scales is None:
+            raise ValueError("int8 activations need x_scales")
+        _check_2d(x_scales, "x_scales", (N, K // 32))
+        st = L.vq_gemm_q4_0(_dev_ptr(codes, "codes"), _dev_ptr(scales, "scales"), _dev_ptr(x, "x"),
+                            act_dtype, _dev_ptr(x_scales, "x_scales"), _dev_ptr(out, "out"),
+                            _dtype_code(out), N, M, K, float(alpha), _stream(stream))
+        _check(st, "vq_gemm_q4_0")
+        return out
+    if x_scales is not None:
+        raise ValueError("x_scales only go with int8 activations")
+    if tiles_per_wave or waves_k:
+        st = L.vq_gemm_q4_0_ex(_dev_ptr(codes, "codes"), _dev_ptr(scales, "scales"), _dev_ptr(x, "x"),
+                               act_dtype, _dev_ptr(out, "out"), _dtype_code(out), N, M, K,
+                               float(alpha), int(tiles_per_wave), int(waves_k), _stream(stream))
+        _check(st, "vq_gemm_q4_0_ex")
+    else:
+        st = L.vq_gemm_q4_0(_dev_ptr(codes, "codes"), _dev_ptr(scales, "scales"), _dev_ptr(x, "x"),
+                            act_dtype, None, _dev_ptr(out, "out"), _dtype_code(out), N, M, K,
+                            float(alpha), _stream(stream))
+        _check(st, "vq_gemm_q4_0")
+    return out
+
+
+def gemm_fp8_blk128(w, tile_scales, x, out, *, stream=None, tiles_per_wave: int = 0, waves_k: int = 0):
+    """out[N][M] = x[N][K] @ (e4m3(w) * tile_scales[m/128][k/128])^T.
+
+    w: uint8 [M][K] (E4M3FN bits); tile_scales: float32 [ceil(M/128)][K/128];
+    x: float16 / bfloat16 [N][K]; out: float16 / bfloat16 / float32 [N][M]."""
+    N, K = x.shape
+    M = w.shape[0]
+    _check_2d(w, "w", (M, K))
+    _check_2d(tile_scales, "tile_scales", ((M + 127) // 128, K // 128))
+    _check_2d(out, "out", (N, M))
+    L = lib()
+    if tiles_per_wave or waves_k:
+        st = L.vq_gemm_fp8_blk128_ex(_dev_ptr(w, "w"), _dev_ptr(tile_scales, "tile_scales"), _dev_ptr(x, "x"),
+                                     _dtype_code(x), _dev_ptr(out, "out"), _dtype_code(out), N, M, K,
+                                     int(tiles_per_wave), int(waves_k), _stream(stream))
+        _check(st, "vq_gemm_fp8_blk128_ex")
+    else:
+        st = L.vq_gemm_fp8_blk128(_dev_ptr(w, "w"), _dev_ptr(tile_scales, "tile_scales"), _dev_ptr(x, "x"),
+                                  _dtype_code(x), _dev_ptr(out, "out"), _dtype_code(out), N, M, K,
+                                  _stream(stream))
+        _check(st, "vq_gemm_fp8_blk128")
+    return out
+
+
+def hadamard32_quant_int8(x, q_out, scales_out, *, stream=None):
+    """Per 32-block: u = H32 x (fp32), d = fp16(amax/127), q = clamp(rint(u/d), +-127).
+
+    x: float16 / bfloat16 [N][K]; q_out: int8 [N][K]; scales_out: float16 [N][K/32]."""
+    N, K = x.shape
+    _check_2d(q_out, "q_out", (N, K))
+    _check_2d(scales_out, "scales_out", (N, K // 32))
+    st = lib().vq_hadamard32_quant_int8(_dev_ptr(x, "x"), _dtype_code(x), _dev_ptr(q_out, "q_out"),
+                                        _dev_ptr(scales_out, "scales_out"), N, K, _stream(stream))
+    _check(st, "vq_hadamard32_quant_int8")
+    return q_out, scales_out
+
+
+def default_launch_shape(kind: str, m: int, k: int):
+    """(tiles_per_wave, waves_k) the library picks for an (M, K) verify GEMM."""
+    t = ctypes.c_int(0)
+    w = ctypes.c_int(0)
+    _check(lib().vq_default_launch_shape(1 if kind == "fp8" else 0, m, k, ctypes.byref(t), ctypes.byref(w)),
+           "vq_default_launch_shape")
+    return t.value, w.value

@@ -1,0 +1,221 @@
+// vq_device.h -- device-side building blocks shared by the gfx950 kernels.
+//
+// Everything here is written for CDNA4 (gfx950) wave64: the 16x16x32 16-bit
+// MFMA, the 16x16x32 int8 MFMA, the v_permlane16/32_swap lane exchanges and
+// the OCP-FP8 conversion instructions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "vq.h"
+
+namespace vq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// 16-bit activation formats.  A Q4_0 code q becomes the exact 16-bit value
+// MAGIC + q by placing the nibble in the low mantissa bits under a fixed
+// exponent byte: bf16 0x43nn = 128 + q, fp16 0x64nn = 1024 + q.  The offset
+// (MAGIC + 8) is removed through the MFMA accumulator input (see the verify
+// kernel), so every product and the per-block dot are exact.
+// ---------------------------------------------------------------------------
+template <int ACT>
+struct Act16;
+
+template <>
+struct Act16<VQ_DTYPE_BF16> {
+    static constexpr uint32_t kMagicByte = 0x43434343u;  // bf16 128 + q
+    static constexpr uint32_t kNegOffset = 0xC308C308u;  // bf16 -136, twice
+    static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    // two E4M3 codes (a 16-bit word of `w`) -> two exact bf16 values
+    template <bool HI>
+    static __device__ __forceinline__ uint32_t fp8x2(uint32_t w) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+    }
+};
+
+template <>
+struct Act16<VQ_DTYPE_F16> {
+    static constexpr uint32_t kMagicByte = 0x64646464u;  // fp16 1024 + q
+    static constexpr uint32_t kNegOffset = 0xE408E408u;  // fp16 -1032, twice
+    static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    template <bool HI>
+    static __device__ __forceinline__ uint32_t fp8x2(uint32_t w) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+    }
+};
+
+// ---------------------------------------------------------------------------
+// 4x4 transpose across the four 16-lane groups of a wave.
+// On entry lane group G holds in r[t] the dword t of "its" 16-byte record;
+// on exit lane group G holds in r[t] the dword G of lane group t's record.
+// Two v_permlane32_swap then two v_permlane16_swap: one VALU op per dword.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void transpose_lane_groups(uint32_t &r0, uint32_t &r1, uint32_t &r2,
+                                                      uint32_t &r3) {
+    auto a = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+    auto b = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+    auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    r0 = c[0];
+    r1 = c[1];
+    r2 = d[0];
+    r3 = d[1];
+}
+
+// ---------------------------------------------------------------------------
+// One dword of Q4_0 codes (block bytes 4g..4g+3) -> the 8 exact 16-bit
+// operands MAGIC + q for k = 4g..4g+3 (low nibbles) and 16+4g..16+4g+3 (high
+// nibbles), in that k order, two per register.  2 ANDs, 1 shift, 4 byte
+// permutes; the permute puts each masked byte under the exponent byte.
+// ---------------------------------------------------------------------------
+template <uint32_t MAGIC>
+__device__ __forceinline__ u32x4 q4_operand(uint32_t v) {
+    const uint32_t lo = v & 0x0F0F0F0Fu;
+    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
+    u32x4 r;
+    // __builtin_amdgcn_perm(s0, s1, sel): selector byte 0..3 picks a byte of
+    // s1, 4..7 a byte of s0.
+    r[0] = __builtin_amdgcn_perm(MAGIC, lo, 0x04010400u);  // (k=4g,   4g+1)
+    r[1] = __builtin_amdgcn_perm(MAGIC, lo, 0x04030402u);  // (k=4g+2, 4g+3)
+    r[2] = __builtin_amdgcn_perm(MAGIC, hi, 0x04010400u);  // (k=16+4g, 17+4g)
+    r[3] = __builtin_amdgcn_perm(MAGIC, hi, 0x04030402u);  // (k=18+4g, 19+4g)
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Raw buffer loads.  A buffer resource carries a byte size; the hardware
+// returns zeros for any lane whose offset falls outside it, which is how rows
+// past M or N are masked without divergent branches.  Offsets: a per-lane
+// VGPR part and a wave-uniform SGPR part.  Weight bytes are read once, so they
+// use the non-temporal policy (aux = 2).
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kAuxStream = 2;  // nt
+constexpr int kAuxCached = 0;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    // word 3 = 0x00020000: raw (untyped) dword data format for the gfx9 family
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <int AUX>
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ u32x2 bload8(rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ uint32_t bload2(rsrc_t r, int voff, int soff) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, AUX));
+}
+
+// ---------------------------------------------------------------------------
+// Software pipeline over a wave's `ns` steps with PF stage buffers.
+//   load(U, i)          -- issue the loads of step i into stage buffer U
+//   compute(U, i, full) -- consume stage U holding step i (full: no K tail)
+// U is a std::integral_constant so buffers are indexed at compile time.
+// When the wave has at least 2 PF steps, the prologue and the steady-state
+// loop issue every load unconditionally: the compiler's wait-count insertion
+// then knows how many newer loads are in flight and waits only for the stage
+// it is about to use.  Shorter runs (and the tail) use guarded loads.
+// ---------------------------------------------------------------------------
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, F, I + 1>(static_cast<F &&>(f));
+    }
+}
+
+template <int PF, typename LoadF, typename ComputeF>
+__device__ __forceinline__ void pipeline(int ns, LoadF &&load, ComputeF &&compute) {
+    int i = 0;
+    if (ns >= 2 * PF) {
+        static_for<PF>([&](auto U) { load(U, U.value); });
+        do {
+            static_for<PF>([&](auto U) {
+                compute(U, i + U.value, true);
+                // keep the refill of this stage right here: the scheduler would
+                // otherwise sink it below later compute and drain the pipeline
+                __builtin_amdgcn_sched_barrier(0);
+                load(U, i + U.value + PF);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            i += PF;
+        } while (i + 2 * PF <= ns);
+    } else {
+        static_for<PF>([&](auto U) {
+            if (U.value < ns)
+                load(U, U.value);
+        });
+    }
+    static_for<PF>([&](auto U) {
+        if (i + U.value < ns) {
+            compute(U, i + U.value, false);
+            if (i + U.value + PF < ns)
+                load(U, i + U.value + PF);
+        }
+    });
+    static_for<PF>([&](auto U) {
+        if (i + PF + U.value < ns)
+            compute(U, i + PF + U.value, false);
+    });
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// ---------------------------------------------------------------------------
+// Plain global loads (used where a buffer resource does not pay).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 ld_stream16(const uint8_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ u32x2 ld8(const void *p) {
+    return *reinterpret_cast<const u32x2 *>(p);
+}
+
+// fp16 bits -> float (exact)
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+// ---------------------------------------------------------------------------
+// Output rounding: fp32 -> out dtype, round to nearest even.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_out(void *out, int out_dtype, size_t idx, float v) {
+    if (out_dtype == VQ_DTYPE_F32) {
+        reinterpret_cast<float *>(out)[idx] = v;
+    } else if (out_dtype == VQ_DTYPE_BF16) {
+        reinterpret_cast<__bf16 *>(out)[idx] = static_cast<__bf16>(v);
+    } else {
+        reinterpret_cast<_Float16 *>(out)[idx] = static_cast<_Float16>(v);
+    }
+}
+
+}  // namespace vq

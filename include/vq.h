@@ -1,0 +1,170 @@
+/*
+ * vq.h -- C ABI of the block-quantized verify GEMM library (libvq.so), gfx950.
+ *
+ * The operation is the speculative-decoding verification matmul: a draft block
+ * of N activation rows (normally 1..16) times block-quantized weights, reading
+ * every weight byte from HBM once whatever N is.  Sources, by page title and
+ * section:
+ *   [P1] "Qwen3.8-27B on the AMD R9700: up to 227 tok/s", sections
+ *        "A block-diffusion drafter, verified exactly" (one batched target
+ *        forward checks the whole draft block and reads the weights once) and
+ *        "What 'lossless' means here, precisely" (batched and one-row paths
+ *        sum in different orders; outputs are compared byte for byte across
+ *        block widths).
+ *   [P3] "r9k: a from-scratch inference engine for Qwen3.8-27B on two Radeon AI
+ *        PRO R9700", opening paragraph (FP8 E4M3 weights in 128 x 128 scale
+ *        blocks) and its list of correctness checks (GEMM rounding depends on
+ *        the row count).
+ *   [P4] "Qwen3.8-27B at 45.7 tok/s: DFlash2 in 1bit serve, and 4-bit
+ *        activations with a Hadamard rotation", section "Prompt processing:
+ *        4-bit activations, rotated first" (Q4_0 = 4-bit codes with offset 8 in
+ *        blocks of 32; top-bit flip = two's complement; a 32-point
+ *        Walsh-Hadamard rotation inside the int8 activation quantizer, weights
+ *        rotated the same way offline; an exact int8 matmul path).
+ *
+ * Conventions shared by every entry point
+ *  - All pointers are DEVICE pointers on the current HIP device, owned by the
+ *    caller, 16-byte aligned, to contiguous row-major arrays.  The library
+ *    never allocates, frees or synchronises, and keeps no per-call state, so
+ *    calls from several host threads are safe.  Outputs must not alias inputs.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *    enqueued on it and the call returns at once.
+ *  - Every argument is checked before anything is enqueued.  On any non-zero
+ *    return nothing was enqueued.  Faults during execution surface at the
+ *    caller's next synchronisation, like any asynchronous HIP call.
+ *  - Numerics: fp32 accumulation; outputs rounded to nearest-even.  For a given
+ *    (M, K) the arithmetic of one output row depends only on that activation
+ *    row and the weights: it is bit-identical whatever N is, whatever the other
+ *    rows hold, and from run to run.
+ */
+#ifndef VQ_H
+#define VQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (0 = success, negative = error; nothing enqueued on error). */
+#define VQ_OK 0
+#define VQ_ERR_NULL_POINTER (-1)   /* a required pointer is NULL */
+#define VQ_ERR_BAD_SHAPE (-2)      /* a size is out of range or not a multiple of its block */
+#define VQ_ERR_MISALIGNED (-3)     /* a pointer is not 16-byte aligned */
+#define VQ_ERR_BAD_DTYPE (-4)      /* dtype code unknown or not allowed here */
+#define VQ_ERR_DEVICE (-5)         /* current device is not gfx950, or no device */
+#define VQ_ERR_LAUNCH (-6)         /* the HIP launch itself reported an error */
+#define VQ_ERR_BAD_CONFIG (-7)     /* explicit launch shape not supported */
+
+/* Element type codes. */
+#define VQ_DTYPE_F16 1             /* IEEE binary16 */
+#define VQ_DTYPE_BF16 2            /* bfloat16 */
+#define VQ_DTYPE_F32 3             /* IEEE binary32 */
+#define VQ_DTYPE_I8 4              /* int8 */
+
+/* Largest M, K or N accepted by any entry point (indices stay in 32 bits). */
+#define VQ_MAX_DIM (1 << 24)
+
+/*
+ * vq_gemm_q4_0 -- out[n][m] = alpha * sum_k x[n][k] * w[m][k], Q4_0 weights.
+ *
+ * Weights [P4]: w[m][k] = d[m][k/32] * (q[m][k] - 8), q in 0..15.
+ *   w_codes  u8  [M][K/2].  Within each 32-weight block (16 bytes) byte j holds
+ *            the code of k = 32b + j in its low nibble and of k = 32b + 16 + j
+ *            in its high nibble (GGUF Q4_0 in-block order; the pages do not fix
+ *            an order, this is the library's reading).
+ *   w_scales f16 [M][K/32], the block scales d.
+ * Activations:
+ *   act_dtype F16 or BF16: x = act, [N][K].  N may exceed 16: rows are then
+ *            processed in groups of 16 by the same kernel (weights are re-read
+ *            per group), which keeps every row's arithmetic independent of N.
+ *            act_scales must be NULL.
+ *   act_dtype I8: the W4A8 path [P4, "exact int8 path"].  act is int8 q_x
+ *            [N][K] and act_scales is f16 [N][K/32] (as written by
+ *            vq_hadamard32_quant_int8); x[n][k] = act_scales[n][k/32] *
+ *            q_x[n][k].  Each 32-block dot sum (q - 8) * q_x is formed exactly
+ *            in int32 before the fp32 scale products.  For weights and
+ *            activations both rotated by the unnormalised H32, pass
+ *            alpha = 1/32 to restore the unrotated product.
+ * Output: out [N][M], out_dtype F16, BF16 or F32.
+ * Sizes: 1 <= N, M <= VQ_MAX_DIM; 32 <= K <= VQ_MAX_DIM, K % 32 == 0.
+ * Returns VQ_OK or a VQ_ERR_* code.
+ */
+int vq_gemm_q4_0(const void *w_codes, const void *w_scales,
+                 const void *act, int act_dtype, const void *act_scales,
+                 void *out, int out_dtype,
+                 int64_t n_rows, int64_t m, int64_t k,
+                 float alpha, void *stream);
+
+/*
+ * vq_gemm_fp8_blk128 -- out[n][m] = sum_k x[n][k] * w[m][k], FP8 weights with
+ * one fp32 scale per 128 x 128 tile [P3]:
+ *   w_e4m3        u8  [M][K], OCP E4M3FN bit patterns (bias 7, max 448, no
+ *                 infinities; the pages say only "FP8 E4M3", the variant is the
+ *                 library's reading).  NaN codes (0x7F, 0xFF) are outside the
+ *                 contract.
+ *   w_tile_scales f32 [ceil(M/128)][K/128]; w[m][k] = e4m3(w_e4m3[m][k]) *
+ *                 w_tile_scales[m/128][k/128].
+ *   act           [N][K], act_dtype F16 or BF16 (rows in groups of 16 as above).
+ *   out           [N][M], out_dtype F16, BF16 or F32.
+ * Sizes: 1 <= N, M <= VQ_MAX_DIM; 128 <= K <= VQ_MAX_DIM, K % 128 == 0.
+ */
+int vq_gemm_fp8_blk128(const void *w_e4m3, const float *w_tile_scales,
+                       const void *act, int act_dtype,
+                       void *out, int out_dtype,
+                       int64_t n_rows, int64_t m, int64_t k, void *stream);
+
+/*
+ * vq_hadamard32_quant_int8 -- per (row n, 32-block b) of x [N][K] [P4]:
+ *   u   = H32 x_b in fp32, H32 the +-1 Sylvester Walsh-Hadamard matrix applied
+ *         as radix-2 butterflies h = 1, 2, 4, 8, 16 in that order
+ *         (unnormalised: the matching GEMM takes alpha = 1/32);
+ *   d   = fp16_rne(fp32(max_j |u_j|) / 127)          -> scales_out [N][K/32] f16
+ *   q_j = clamp(rint_half_even(u_j / d), -127, 127)   -> q_out [N][K] int8
+ *   A block of zeros gives d = 0 and q = 0.  A block whose d overflows fp16
+ *   gets d = +inf and q = 0 (outside any realistic input).
+ * Every division is IEEE fp32, correctly rounded, so codes and scales are
+ * reproducible bit for bit.
+ * x_dtype F16 or BF16.  Sizes: 1 <= N <= VQ_MAX_DIM, 32 <= K <= VQ_MAX_DIM,
+ * K % 32 == 0.
+ */
+int vq_hadamard32_quant_int8(const void *x, int x_dtype,
+                             int8_t *q_out, void *scales_out,
+                             int64_t n_rows, int64_t k, void *stream);
+
+/*
+ * vq_gemm_q4_0_ex / vq_gemm_fp8_blk128_ex -- the same operations with an
+ * explicit launch shape, for tuning: `tiles_per_wave` output tiles of 16
+ * features per wavefront (1, 2 or 4) and `waves_k` wavefronts splitting K
+ * inside one workgroup (1, 2, 4, 8 or 16); 0 for either picks the default for
+ * (M, K).  Results are bit-identical across N for a fixed launch shape; a
+ * different launch shape may round differently.  Float activations only.
+ */
+int vq_gemm_q4_0_ex(const void *w_codes, const void *w_scales,
+                    const void *act, int act_dtype,
+                    void *out, int out_dtype,
+                    int64_t n_rows, int64_t m, int64_t k, float alpha,
+                    int tiles_per_wave, int waves_k, void *stream);
+int vq_gemm_fp8_blk128_ex(const void *w_e4m3, const float *w_tile_scales,
+                          const void *act, int act_dtype,
+                          void *out, int out_dtype,
+                          int64_t n_rows, int64_t m, int64_t k,
+                          int tiles_per_wave, int waves_k, void *stream);
+
+/* The launch shape the library picks by default for an (M, K) verify GEMM:
+ * kind 0 = Q4_0, 1 = FP8.  Writes tiles_per_wave and waves_k; returns VQ_OK. */
+int vq_default_launch_shape(int kind, int64_t m, int64_t k,
+                            int *tiles_per_wave, int *waves_k);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *vq_status_string(int status);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int vq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VQ_H */

@@ -1,0 +1,220 @@
+"""Q4_0 verify GEMM on the GPU, through the C ABI, against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_gemm_amd as vq
+import oracle
+import workloads as W
+from helpers import bits_u16, out_to_f64, parity, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+ORACLE_DT = {"bf16": oracle.BF16, "f16": oracle.F16}
+
+
+def _to_act_bits(x, act_dtype):
+    return W.f32_to_bf16_bits(x) if act_dtype == "bf16" else W.f32_to_f16_bits(x)
+
+
+class Q4:
+    """A Q4_0 weight matrix resident on the device."""
+
+    def __init__(self, codes, scales):
+        self.codes_np, self.scales_np = codes, scales
+        self.M, self.K = codes.shape[0], codes.shape[1] * 2
+        self.codes = to_dev(codes)
+        self.scales = to_dev(scales, torch.float16)
+
+    def run(self, act_bits, act_dtype="bf16", out_dtype="bf16", alpha=1.0, **kw):
+        x = to_dev(act_bits, TORCH_DT[act_dtype])
+        out = torch.empty((x.shape[0], self.M), dtype=TORCH_DT[out_dtype], device="cuda")
+        vq.gemm_q4_0(self.codes, self.scales, x, out, alpha=alpha, **kw)
+        torch.cuda.synchronize()
+        return out
+
+    def oracle(self, act_bits, act_dtype="bf16", cols=None, alpha=1.0):
+        N = act_bits.shape[0]
+        return oracle.gemm_q4_0(self.codes_np, self.scales_np, act_bits, ORACLE_DT[act_dtype],
+                                N, self.M, self.K, cols=cols, alpha=alpha)
+
+
+def _sample_cols(M, n, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    edge = np.array([0, 1, 15, 16, M // 2, M - 17, M - 16, M - 1])
+    return np.unique(np.concatenate([edge[(edge >= 0) & (edge < M)], g.choice(M, size=min(n, M), replace=False)]))
+
+
+# ------------------------------------------------------------------ parity
+
+
+def test_tiny_config_parity():
+    t = W.tiny()
+    q = Q4(t["codes"], t["scales"])
+    y = q.run(t["act"], "f16", "f16")
+    ref = q.oracle(t["act"], "f16")
+    fro, worst, ulps = parity(out_to_f64(y), ref, "f16")
+    print("tiny: relF %.3e worst %.3e max %.2f ulp" % (fro, worst, ulps))
+
+
+@pytest.fixture(scope="module")
+def ffn():
+    t = W.ffn(N=16)
+    return Q4(t["codes"], t["scales"]), t["act"]
+
+
+@pytest.mark.parametrize("n_rows", [1, 8, 16])
+def test_ffn_config_parity_sampled(ffn, n_rows):
+    q, act = ffn
+    a = np.ascontiguousarray(act[:n_rows])
+    y = out_to_f64(q.run(a))
+    cols = _sample_cols(q.M, 768, 5 + n_rows)
+    fro, worst, ulps = parity(y[:, cols], q.oracle(a, cols=cols), "bf16")
+    print("ffn N=%d: relF %.3e worst %.3e max %.2f ulp" % (n_rows, fro, worst, ulps))
+
+
+@pytest.mark.parametrize("act_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16", "f32"])
+def test_dtype_combinations_parity(act_dtype, out_dtype):
+    g = np.random.Generator(np.random.PCG64(101))
+    M, K, N = 272, 1024, 11
+    q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_uniform(M, K, g))
+    a = _to_act_bits(g.standard_normal((N, K)), act_dtype)
+    parity(out_to_f64(q.run(a, act_dtype, out_dtype)), q.oracle(a, act_dtype), out_dtype)
+
+
+# ------------------------------------------------------------------ bit-exact probes
+
+
+@pytest.mark.parametrize("act_dtype", ["bf16", "f16"])
+def test_integer_case_bit_exact(act_dtype):
+    """Unit scales and small-integer activations: every partial sum is an integer
+    below 2^24, so the fp32 output must equal the exact oracle bit for bit."""
+    g = np.random.Generator(np.random.PCG64(102))
+    M, K, N = 160, 2048, 16
+    q = Q4(W.q4_0_codes(M, K, g), np.full((M, K // 32), 0x3C00, dtype=np.uint16))
+    a = _to_act_bits(g.integers(-4, 5, size=(N, K)), act_dtype)
+    y = out_to_f64(q.run(a, act_dtype, "f32"))
+    assert np.array_equal(y, q.oracle(a, act_dtype))
+
+
+@pytest.mark.parametrize("act_dtype", ["bf16", "f16"])
+def test_one_hot_unpack_every_code(act_dtype):
+    """Row n of X = e_k: Y[n][m] = q[m][k] - 8 exactly.  K/16 calls cover every
+    code of the matrix (code unpacking must be bit-exact)."""
+    t = W.tiny()
+    M, K = t["M"], t["K"]
+    q = Q4(t["codes"], np.full((M, K // 32), 0x3C00, dtype=np.uint16))
+    ref = oracle.q4_0_dequant(t["codes"], np.full((M, K // 32), 0x3C00, dtype=np.uint16), M, K)
+    for k0 in range(0, K, 16):
+        x = np.zeros((16, K), dtype=np.float32)
+        x[np.arange(16), k0 + np.arange(16)] = 1.0
+        y = out_to_f64(q.run(_to_act_bits(x, act_dtype), act_dtype, "f32"))
+        assert np.array_equal(y, ref[:, k0:k0 + 16].T), k0
+
+
+def test_block_scales_bit_exact():
+    """Distinct power-of-two block scales with integer activations: checks that
+    every block picks up its own scale (exact in fp32)."""
+    g = np.random.Generator(np.random.PCG64(103))
+    M, K, N = 48, 512, 16
+    sc = np.array([[2.0 ** -((m + b) % 9) for b in range(K // 32)] for m in range(M)])
+    q = Q4(W.q4_0_codes(M, K, g), W.f32_to_f16_bits(sc))
+    a = W.f32_to_bf16_bits(g.integers(-3, 4, size=(N, K)))
+    assert np.array_equal(out_to_f64(q.run(a, "bf16", "f32")), q.oracle(a))
+
+
+def test_alpha_power_of_two_is_exact():
+    t = W.tiny()
+    q = Q4(t["codes"], t["scales"])
+    y1 = q.run(t["act"], "f16", "f32").cpu().numpy()
+    y4 = q.run(t["act"], "f16", "f32", alpha=0.25).cpu().numpy()
+    assert np.array_equal(y4, y1 * np.float32(0.25))
+
+
+# ------------------------------------------------------------------ width invariance
+
+
+@pytest.mark.parametrize("act_dtype,shape", [("bf16", (17408, 5120)), ("f16", (256, 512)),
+                                              ("bf16", (5120, 17408)), ("bf16", (300, 480))])
+def test_rows_bit_identical_across_widths(act_dtype, shape):
+    """Each output row is bit-identical whether the call has 1, 8 or 16 rows,
+    under row permutation and with junk neighbours (the pages compare verify
+    outputs byte for byte across draft widths)."""
+    M, K = shape
+    g = np.random.Generator(np.random.PCG64(104))
+    q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_lognormal(M, K, g))
+    x = _to_act_bits(0.5 * g.standard_t(3, size=(16, K)), act_dtype)
+    full = bits_u16(q.run(x, act_dtype, "bf16"))
+    for h in (0, 8):
+        eight = bits_u16(q.run(np.ascontiguousarray(x[h:h + 8]), act_dtype, "bf16"))
+        assert np.array_equal(eight, full[h:h + 8])
+    for n in range(16):
+        one = bits_u16(q.run(np.ascontiguousarray(x[n:n + 1]), act_dtype, "bf16"))
+        assert np.array_equal(one[0], full[n]), n
+    perm = g.permutation(16)
+    permuted = bits_u16(q.run(np.ascontiguousarray(x[perm]), act_dtype, "bf16"))
+    assert np.array_equal(permuted, full[perm])
+    junk = _to_act_bits(100.0 * g.standard_normal((16, K)), act_dtype)
+    junk[5] = x[5]
+    assert np.array_equal(bits_u16(q.run(junk, act_dtype, "bf16"))[5], full[5])
+
+
+def test_repeat_calls_bit_identical(ffn):
+    q, act = ffn
+    first = bits_u16(q.run(act))
+    for _ in range(3):
+        assert np.array_equal(bits_u16(q.run(act)), first)
+
+
+# ------------------------------------------------------------------ edges and launch shapes
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 32, 1), (17, 96, 3), (300, 480, 5), (64, 160, 40),
+                                   (33, 4128, 17), (4096, 32, 16), (16, 8192, 2)])
+def test_ragged_shapes_parity(M, K, N):
+    g = np.random.Generator(np.random.PCG64(M * 7 + K + N))
+    q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_uniform(M, K, g))
+    a = W.f32_to_bf16_bits(g.standard_normal((N, K)))
+    parity(out_to_f64(q.run(a)), q.oracle(a), "bf16")
+
+
+@pytest.mark.parametrize("tpw", [1, 2, 4])
+@pytest.mark.parametrize("kw", [1, 2, 4, 8, 16])
+def test_every_launch_shape_parity_and_exact_integers(tpw, kw):
+    g = np.random.Generator(np.random.PCG64(105))
+    M, K, N = 272, 1056, 16          # 17 tiles, 33 blocks: partial tiles-per-wave and a partial K step
+    codes = W.q4_0_codes(M, K, g)
+    q = Q4(codes, W.fp16_scales_uniform(M, K, g))
+    a = W.f32_to_bf16_bits(g.standard_normal((N, K)))
+    parity(out_to_f64(q.run(a, tiles_per_wave=tpw, waves_k=kw)), q.oracle(a), "bf16")
+    qi = Q4(codes, np.full((M, K // 32), 0x3C00, dtype=np.uint16))
+    ai = W.f32_to_bf16_bits(g.integers(-4, 5, size=(N, K)))
+    assert np.array_equal(out_to_f64(qi.run(ai, "bf16", "f32", tiles_per_wave=tpw, waves_k=kw)), qi.oracle(ai))
+
+
+def test_many_row_groups():
+    """N > 16 is processed as groups of 16 rows; each row matches its 16-row call."""
+    g = np.random.Generator(np.random.PCG64(106))
+    M, K, N = 200, 640, 50
+    q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_uniform(M, K, g))
+    a = W.f32_to_bf16_bits(g.standard_normal((N, K)))
+    y = bits_u16(q.run(a))
+    parity(out_to_f64(q.run(a)), q.oracle(a), "bf16")
+    for r0 in (0, 16, 32):
+        assert np.array_equal(bits_u16(q.run(np.ascontiguousarray(a[r0:r0 + 16]))), y[r0:r0 + 16])
+    assert np.array_equal(bits_u16(q.run(np.ascontiguousarray(a[48:50]))), y[48:50])
+
+
+def test_full_stream_layer_sampled():
+    """One synthetic layer of the per-token weight stream at full size, in the
+    library's default launch shapes, 16 rows, sampled outputs vs the oracle."""
+    for idx in range(len(W.STREAM_LAYER_SHAPES)):
+        m = W.stream_matrix(layer=3, idx=idx)
+        q = Q4(m["codes"], m["scales"])
+        a = W.stream_act(3, q.K)
+        y = out_to_f64(q.run(a))
+        cols = _sample_cols(q.M, 256, idx)
+        fro, worst, ulps = parity(y[:, cols], q.oracle(a, cols=cols), "bf16")
+        print("stream %dx%d: relF %.3e worst %.3e max %.2f ulp" % (q.M, q.K, fro, worst, ulps))
