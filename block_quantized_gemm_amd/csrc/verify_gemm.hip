@@ -4,385 +4,425 @@
 // drafter, verified exactly": the target checks a whole draft block in one
 // batched forward that reads the weights once, so 16 rows cost about what one
 // row costs.  This file is that product for two weight formats:
-//   Q4_0   -- "Qwen3.8-27B at 45.7 tok/s ...", section "Prompt processing":
-//             4-bit codes, offset 8, blocks of 32, one fp16 scale per block;
-//   FP8    -- "r9k: a from-scratch inference engine ...", opening paragraph:
-//             E4M3 weights with one scale per 128 x 128 tile.
+//   Q4_0 -- "Qwen3.8-27B at 45.7 tok/s ...", section "Prompt processing":
+//           4-bit codes with offset 8 in blocks of 32, one fp16 scale per block;
+//   FP8  -- "r9k: a from-scratch inference engine ...", opening paragraph:
+//           E4M3 weights with one scale per 128 x 128 tile.
 //
-// Design (gfx950, wave64):
-//  * One MFMA 16x16x32 (bf16 or fp16) per (16 output features x 32 k).  The
-//    A operand is the activation block (rows zero-padded to 16), the B operand
-//    the dequantised weights.  The same instruction sequence runs for every
-//    N <= 16, so an output row's arithmetic never depends on N (the pages
-//    compare outputs byte for byte across block widths; "What 'lossless' means
-//    here, precisely").
-//  * Q4_0: each lane streams one whole 16-byte block of one feature with a
-//    128-bit load; a 4x4 lane-group transpose (permlane swaps) hands every
-//    lane its 4-byte slice of each block.  Codes become the exact 16-bit
-//    values MAGIC + q; an extra MFMA with constant -(MAGIC + 8) computes the
-//    per-row offset term, which enters the block MFMA as its accumulator, so
-//    the MFMA result is the exact block dot sum (q - 8) x in fp32.  The fp16
-//    block scale is then applied with one fp32 FMA per output.
+// Arithmetic (gfx950, wave64):
+//  * One MFMA 16x16x32 (bf16 or fp16) per (16 output features x 32 k); A is
+//    the activation block (rows zero-padded to 16), B the weights.  The same
+//    instruction sequence runs for every N <= 16, so an output row never
+//    depends on N (the pages compare outputs byte for byte across block
+//    widths, "What 'lossless' means here, precisely").
+//  * Q4_0: every lane streams one 16-byte block of one feature; a 4x4
+//    lane-group transpose (permlane swaps) hands each lane its 4-byte slice of
+//    each block; codes become the exact 16-bit values MAGIC + q; an MFMA with
+//    the constant -(MAGIC + 8) forms the per-row offset term, which enters the
+//    block MFMA as its accumulator, so the MFMA returns the exact block sum
+//    (q - 8) x in fp32.  The fp16 block scale is one fp32 FMA per output.
 //  * FP8: 32 contiguous bytes per lane per 128-wide chunk, hardware E4M3 ->
-//    16-bit conversion (exact), 4 MFMAs per chunk accumulated from zero, then
-//    one FMA with the chunk's fp32 tile scale.
-//  * A workgroup is `KW` waves that split K (wave w takes steps w, w+KW, ...)
-//    over the same `T` feature tiles; partial sums are combined through LDS in
-//    the fixed order w = 0, 1, ..., KW-1.  No atomics: results are the same on
-//    every run.
-//  * Loads are raw buffer loads against resources sized to the workgroup's
-//    rows, so rows past M (weights) or N (activations) read as zeros without
-//    any divergent branch, and the step offset is a wave-uniform SGPR.  Each
-//    wave keeps PF steps of loads in flight ahead of the one it computes:
-//    HBM latency is hidden by memory-level parallelism, not by occupancy.
+//    16-bit conversion (exact), 4 MFMAs per chunk, one FMA with the fp32 tile
+//    scale.
+//
+// Data movement (the kernel is bound by what reaches the CUs):
+//  * A workgroup is FG x KW waves.  The FG waves of one K-group work on FG
+//    different 16-feature tiles at the same K step; the KW K-groups split K
+//    into contiguous ranges.  Per 128-wide step, a K-group's 16 x 128
+//    activation tile is read from memory once (one contiguous 16-byte load per
+//    lane and piece, whole cache lines), scattered into LDS in MFMA operand
+//    order and read back by all FG waves, so activation traffic per weight
+//    byte falls by FG.  With FG = 1 the tile is private to its wave and needs
+//    no barrier; with FG > 1 it is double-buffered with one barrier per step.
+//  * The workgroup's Q4_0 block scales are staged into LDS once.
+//  * Weight bytes are streamed with 16-byte raw buffer loads (rows past M read
+//    as zeros) PF steps ahead of the compute in a register pipeline.
+//  * K-group partial sums are combined through LDS in the fixed order
+//    0, 1, ..., KW-1: no atomics, the same result on every run.
 #include "vq_device.h"
 #include "vq_internal.h"
 
 namespace vq {
 
-// --------------------------------------------------------------------------
-// Shared epilogue: fixed-order cross-wave reduction, alpha, rounding, store.
-// acc[t][r] of lane (j = lane & 15, g = lane >> 4) is output row 4g + r of
-// feature 16 * (tile0 + t) + j.
-// --------------------------------------------------------------------------
-template <int T, int KW>
-__device__ __forceinline__ void reduce_store(f32x4 (&acc)[T], void *__restrict__ out, int out_dtype,
-                                             int M, int row0, int nrows, int tile0, float alpha) {
-    const int lane = threadIdx.x & 63;
-    if constexpr (KW == 1) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int f = (tile0 + t) * 16 + (lane & 15);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 4 * (lane >> 4) + r;
-                if (row < nrows && f < M)
-                    store_out(out, out_dtype, (size_t)(row0 + row) * M + f, alpha * acc[t][r]);
-            }
-        }
+constexpr int kStepK = 128;                      // k per step: 4 Q4_0 blocks or one FP8 chunk
+constexpr int kActTileBytes = 16 * kStepK * 2;   // one step of 16 activation rows (bf16/fp16)
+
+// LDS position of activation piece p (k = 8p .. 8p+7 of the step) of row r, in
+// the operand layout [32-k group q][lane = 16 g + r][16 bytes]:
+//  Q4_0: lane (r, g)'s operand for block q is x[4g .. 4g+3] (first 8 bytes)
+//        and x[16+4g .. 16+4g+3] (last 8 bytes) of that block, the order in
+//        which q4_operand lays out the codes.  A piece splits over two lanes.
+//  FP8:  lane (r, g)'s operand for MFMA u is x[32g + 8u .. +8]: piece p is one
+//        whole operand (g = p / 4, u = p % 4).
+template <bool FP8>
+__device__ __forceinline__ void act_piece_to_lds(uint8_t *tile, int r, int p, u32x4 v) {
+    if constexpr (FP8) {
+        *reinterpret_cast<u32x4 *>(tile + ((p & 3) * 64 + 16 * (p >> 2) + r) * 16) = v;
     } else {
-        __shared__ float red[KW][T * 4 * kWave];
-        const int wave = threadIdx.x >> 6;
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                red[wave][(t * 4 + r) * kWave + lane] = acc[t][r];
-        __syncthreads();
-        for (int o = threadIdx.x; o < T * 4 * kWave; o += KW * kWave) {
-            float s = red[0][o];
-#pragma unroll
-            for (int w = 1; w < KW; ++w)
-                s += red[w][o];
-            const int ln = o & 63;
-            const int tr = o >> 6;
-            const int t = tr >> 2, r = tr & 3;
-            const int f = (tile0 + t) * 16 + (ln & 15);
-            const int row = 4 * (ln >> 4) + r;
-            if (row < nrows && f < M)
-                store_out(out, out_dtype, (size_t)(row0 + row) * M + f, alpha * s);
-        }
+        const int blk = p >> 2, q = p & 3;
+        const int g0 = 2 * (q & 1), half = q >> 1;
+        uint8_t *base = tile + blk * 1024 + half * 8;
+        *reinterpret_cast<u32x2 *>(base + (16 * g0 + r) * 16) = u32x2{v[0], v[1]};
+        *reinterpret_cast<u32x2 *>(base + (16 * (g0 + 1) + r) * 16) = u32x2{v[2], v[3]};
     }
 }
 
-// --------------------------------------------------------------------------
-// Q4_0 verify kernel.  grid = (ceil(tiles / T), row groups), block = 64 * KW.
-//
-// One "step" is 4 consecutive 32-blocks (128 k).  Wave w of the workgroup
-// takes steps w, w + KW, w + 2 KW, ...; PF steps of loads are kept in flight
-// ahead of the step being computed (software pipeline).
-// --------------------------------------------------------------------------
-template <int T>
-struct Q4Stage {
-    uint32_t c[T][4];   // codes: lane group g holds block 4s+g, 16 bytes
-    uint32_t sc[T][4];  // the lane's 4 block scales of the step: fp16 pairs in [0], [1]
-                        // (8-byte path) or one fp16 per entry (2-byte path)
-    u32x4 a[4];         // activation operand of each of the 4 blocks
+template <bool FP8>
+struct WStage;
+template <>
+struct WStage<false> {
+    u32x4 c;  // 16 code bytes: block 4s + g of the lane's feature
+};
+template <>
+struct WStage<true> {
+    u32x4 w0, w1;  // 32 E4M3 bytes: k = 32g .. 32g + 31 of the step
 };
 
-template <int T, bool SVEC>
-__device__ __forceinline__ void q4_load(Q4Stage<T> &st, int s, rsrc_t rc, rsrc_t rs, rsrc_t ra, int vc, int vs,
-                                        int va, int tile_cbytes, int tile_sbytes) {
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const u32x4 v = bload16<kAuxStream>(rc, vc, 64 * s + t * tile_cbytes);
-        st.c[t][0] = v[0]; st.c[t][1] = v[1]; st.c[t][2] = v[2]; st.c[t][3] = v[3];
-        if constexpr (SVEC) {
-            const u32x2 w = bload8<kAuxStream>(rs, vs, 8 * s + t * tile_sbytes);
-            st.sc[t][0] = w[0]; st.sc[t][1] = w[1];
-        } else {
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-                st.sc[t][tb] = bload2<kAuxStream>(rs, vs + 2 * tb, 8 * s + t * tile_sbytes);
-        }
-    }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        const u32x2 lo = bload8<kAuxCached>(ra, va + 64 * tb, 256 * s);
-        const u32x2 hi = bload8<kAuxCached>(ra, va + 64 * tb + 32, 256 * s);
-        st.a[tb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
-}
-
-template <int ACT, int T, bool SVEC, bool FULL>
-__device__ __forceinline__ void q4_compute(Q4Stage<T> &st, int nblk, f32x4 (&acc)[T]) {
+// One Q4_0 step (4 blocks) for one 16-feature tile.
+template <int ACT, bool FULL>
+__device__ __forceinline__ void q4_step(u32x4 c, const u32x4 (&a)[4], const uint32_t (&sc)[4], int nblk,
+                                        f32x4 &acc) {
     using A16 = Act16<ACT>;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     const u32x4 negc = {A16::kNegOffset, A16::kNegOffset, A16::kNegOffset, A16::kNegOffset};
-    // lane group g gets dword g of each of the 4 blocks
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-        transpose_lane_groups(st.c[t][0], st.c[t][1], st.c[t][2], st.c[t][3]);
+    uint32_t d[4] = {c[0], c[1], c[2], c[3]};
+    transpose_lane_groups(d[0], d[1], d[2], d[3]);  // lane group g: dword g of blocks 0..3
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-        if (FULL || tb < nblk) {  // wave-uniform: only the last step of a ragged K is partial
-            // -(MAGIC + 8) * (sum of the block's activations), per row
-            const f32x4 corr = A16::mfma(st.a[tb], negc, zero4);
+        if (FULL || tb < nblk) {
+            const f32x4 corr = A16::mfma(a[tb], negc, zero4);  // -(MAGIC + 8) * sum x, per row
+            const f32x4 dot = A16::mfma(a[tb], q4_operand<A16::kMagicByte>(d[tb]), corr);
+            const float s = h2f(sc[tb]);
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const u32x4 bop = q4_operand<A16::kMagicByte>(st.c[t][tb]);
-                const f32x4 d = A16::mfma(st.a[tb], bop, corr);  // exact sum (q - 8) x
-                float dsc;
-                if constexpr (SVEC) {
-                    const uint32_t pair = st.sc[t][tb >> 1];
-                    dsc = h2f((tb & 1) ? (pair >> 16) : (pair & 0xFFFFu));
-                } else {
-                    dsc = h2f(st.sc[t][tb]);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[t][r] = __builtin_fmaf(dsc, d[r], acc[t][r]);
-            }
+            for (int r = 0; r < 4; ++r)
+                acc[r] = __builtin_fmaf(s, dot[r], acc[r]);
         }
     }
 }
 
-template <int ACT, int T, int KW, int PF, bool SVEC>
-__global__ __launch_bounds__(64 * KW) void q4_0_verify_kernel(
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
-    const uint16_t *__restrict__ act, void *__restrict__ out, int out_dtype, int N, int M, int K,
-    float alpha) {
-    const int lane = threadIdx.x & 63;
-    const int wave = wave_id();
-    const int j = lane & 15;  // A row (activation row) and B/D column (feature)
-    const int g = lane >> 4;  // k-slot group
-    const int NB = K >> 5;    // 32-blocks per row
-    const int S = (NB + 3) >> 2;
-    const int tile0 = blockIdx.x * T;
-    const int row0 = blockIdx.y * 16;
-    const int nrows = min(16, N - row0);
-    const int frows = min(M - tile0 * 16, T * 16);  // feature rows owned by this workgroup
-
-    // buffer resources sized to this workgroup's rows: anything past them reads as 0
-    const rsrc_t rc = make_rsrc(codes + (size_t)tile0 * 16 * (size_t)(K >> 1), (uint32_t)frows * (uint32_t)(K >> 1));
-    const rsrc_t rs = make_rsrc(scales + (size_t)tile0 * 16 * NB, (uint32_t)frows * (uint32_t)NB * 2u);
-    const rsrc_t ra = make_rsrc(act + (size_t)row0 * K, (uint32_t)nrows * (uint32_t)K * 2u);
-    const int vc = j * (K >> 1) + 16 * g;
-    const int vs = j * NB * 2;
-    const int va = j * K * 2 + 8 * g;
-    const int tile_cbytes = 16 * (K >> 1);
-    const int tile_sbytes = 16 * NB * 2;
-
-    f32x4 acc[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Steps of this wave: wave, wave + KW, ...; only the very last step of K can
-    // be partial, and the pipeline's steady state never computes it.
-    // When every step is full (K % 128 == 0), workgroup b walks its steps in an
-    // order rotated by b, so the thousands of concurrently running waves read
-    // different activation lines instead of all hitting the same ones.  The
-    // order is a function of the launch shape only, never of N.
-    const int ns = (S - wave + KW - 1) / KW;
-    const int rot = (SVEC && ns > 0) ? (int)(blockIdx.x % (unsigned)ns) : 0;
-    auto step_of = [&](int i) {
-        int r = i + rot;
-        r = r >= ns ? r - ns : r;
-        return wave + r * KW;
-    };
-    Q4Stage<T> st[PF];
-    pipeline<PF>(
-        ns,
-        [&](auto U, int i) {
-            q4_load<T, SVEC>(st[U.value], step_of(i), rc, rs, ra, vc, vs, va, tile_cbytes, tile_sbytes);
-        },
-        [&](auto U, int i, bool full) {
-            if (full)
-                q4_compute<ACT, T, SVEC, true>(st[U.value], 4, acc);
-            else
-                q4_compute<ACT, T, SVEC, false>(st[U.value], min(4, NB - 4 * step_of(i)), acc);
-        });
-    reduce_store<T, KW>(acc, out, out_dtype, M, row0, nrows, tile0, alpha);
-}
-
-// --------------------------------------------------------------------------
-// FP8 E4M3 + 128x128 fp32 tile scales.  K % 128 == 0.  One "chunk" = 128 k.
-// --------------------------------------------------------------------------
-template <int T>
-struct F8Stage {
-    u32x4 w[T][2];  // 32 weight bytes per lane per tile
-    u32x4 a[4];     // 4 activation operands (8 values each)
-};
-
-template <int T>
-__device__ __forceinline__ void f8_load(F8Stage<T> &st, int c, rsrc_t rw, rsrc_t ra, int vw, int va,
-                                        int tile_bytes) {
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        st.w[t][0] = bload16<kAuxStream>(rw, vw, 128 * c + t * tile_bytes);
-        st.w[t][1] = bload16<kAuxStream>(rw, vw + 16, 128 * c + t * tile_bytes);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-        st.a[u] = bload16<kAuxCached>(ra, va + 16 * u, 256 * c);
-}
-
-template <int ACT, int T>
-__device__ __forceinline__ void f8_compute(F8Stage<T> &st, int c, const float *const (&srow)[T],
-                                           f32x4 (&acc)[T]) {
+// One FP8 chunk (128 k) for one 16-feature tile.
+template <int ACT>
+__device__ __forceinline__ void fp8_step(const WStage<true> &w, const u32x4 (&a)[4], float ts, f32x4 &acc) {
     using A16 = Act16<ACT>;
+    f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        f32x4 part = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t d0 = st.w[t][q >> 1][2 * (q & 1)];
-            const uint32_t d1 = st.w[t][q >> 1][2 * (q & 1) + 1];
-            const u32x4 bop = {A16::template fp8x2<false>(d0), A16::template fp8x2<true>(d0),
-                               A16::template fp8x2<false>(d1), A16::template fp8x2<true>(d1)};
-            part = A16::mfma(st.a[q], bop, part);
-        }
-        const float ts = srow[t][c];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            acc[t][r] = __builtin_fmaf(ts, part[r], acc[t][r]);
+    for (int u = 0; u < 4; ++u) {
+        const u32x4 src = u < 2 ? w.w0 : w.w1;
+        const uint32_t e0 = src[2 * (u & 1)], e1 = src[2 * (u & 1) + 1];
+        const u32x4 bop = {A16::template fp8x2<false>(e0), A16::template fp8x2<true>(e0),
+                           A16::template fp8x2<false>(e1), A16::template fp8x2<true>(e1)};
+        part = A16::mfma(a[u], bop, part);
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        acc[r] = __builtin_fmaf(ts, part[r], acc[r]);
 }
 
-template <int ACT, int T, int KW, int PF>
-__global__ __launch_bounds__(64 * KW) void fp8_verify_kernel(
-    const uint8_t *__restrict__ w, const float *__restrict__ tscales,
-    const uint16_t *__restrict__ act, void *__restrict__ out, int out_dtype, int N, int M, int K) {
+// ---------------------------------------------------------------------------
+// The verify kernel.  grid = (ceil(tiles / FG), groups of 16 rows), block =
+// 64 * FG * KW.  Dynamic LDS: the K-groups' activation tiles (two buffers
+// each when FG > 1, one otherwise), then the Q4_0 block scales of the
+// workgroup's FG * 16 feature rows.
+// ---------------------------------------------------------------------------
+template <int ACT, bool FP8, int FG, int KW, int PF, bool SVEC>
+__global__ __launch_bounds__(64 * FG * KW) void verify_kernel(
+    const uint8_t *__restrict__ wts, const void *__restrict__ scales, const uint16_t *__restrict__ act,
+    void *__restrict__ out, int out_dtype, int N, int M, int K, float alpha) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    static_assert(FG == 1 || FG == 2 || FG == 4, "FG");
+    constexpr int NW = FG * KW;
+    constexpr int AP = 4 / FG;          // 16-byte activation pieces per lane per step
+    constexpr bool SHARED = FG > 1;     // tile shared across waves: double buffer + barriers
+    constexpr int NBUF = SHARED ? 2 : 1;
+
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
+    const int fw = wave % FG;  // this wave's feature tile in the workgroup
+    const int kg = wave / FG;  // this wave's K-group
     const int j = lane & 15;
     const int g = lane >> 4;
-    const int C = K >> 7;  // 128-wide chunks
-    const int tile0 = blockIdx.x * T;
+
+    const int NB = K >> 5;
+    const int S = FP8 ? (K >> 7) : (NB + 3) >> 2;  // steps; the last Q4_0 step may be partial
+    // K-group kg takes steps kg, kg + KW, kg + 2 KW, ...: the KW waves of a tile
+    // read neighbouring 64-byte pieces of each weight row, so the workgroup
+    // sweeps every row in 64 KW-byte runs (DRAM pages are visited once, not
+    // once per piece).  Group sizes differ by at most one, so only a group's
+    // final iteration can be empty and only the final step of K can be
+    // partial; the steady-state loop reaches neither.
+    const int n_iter = (S + KW - 1) / KW;
+    const int n_mine = (S - kg + KW - 1) / KW;
+    auto step_of = [&](int it) { return kg + it * KW; };
+    const int feat0 = blockIdx.x * FG * 16;
+    const int frows = min(M - feat0, FG * 16);
     const int row0 = blockIdx.y * 16;
     const int nrows = min(16, N - row0);
-    const int frows = min(M - tile0 * 16, T * 16);
 
-    const rsrc_t rw = make_rsrc(w + (size_t)tile0 * 16 * (size_t)K, (uint32_t)frows * (uint32_t)K);
+    // Buffer resources sized to the workgroup's rows: reads past them return 0.
+    const int wrow = FP8 ? K : (K >> 1);  // weight bytes per feature row
+    const rsrc_t rw = make_rsrc(wts + (size_t)feat0 * wrow, (uint32_t)frows * (uint32_t)wrow);
     const rsrc_t ra = make_rsrc(act + (size_t)row0 * K, (uint32_t)nrows * (uint32_t)K * 2u);
-    const int vw = j * K + 32 * g;
-    const int va = j * K * 2 + 64 * g;
-    const int tile_bytes = 16 * K;
+    const int vw = (fw * 16 + j) * wrow + (FP8 ? 32 : 16) * g;
+    const int wstep = FP8 ? 128 : 64;  // weight bytes per row per step
 
-    // all 16 features of a tile share one 128-row scale group
-    const float *srow[T];
+    // Activation pieces this lane stages: piece c = fw * 64 + lane + FG * 64 * a
+    // of its K-group's tile; row c / 16, 16-byte piece c % 16 of that row.
+    int va[AP], ar[AP], ap[AP];
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-        srow[t] = tscales + (size_t)(min((tile0 + t) * 16, M - 1) >> 7) * C;
+    for (int a = 0; a < AP; ++a) {
+        const int c = fw * 64 + lane + FG * 64 * a;
+        ar[a] = c >> 4;
+        ap[a] = c & 15;
+        va[a] = ar[a] * K * 2 + 16 * ap[a];
+    }
+    auto tile_ptr = [&](int buf) { return lds + (size_t)(kg * NBUF + buf) * kActTileBytes; };
 
-    f32x4 acc[T];
+    const uint16_t *sc_lds = reinterpret_cast<const uint16_t *>(lds + (size_t)KW * NBUF * kActTileBytes);
+    const uint16_t *my_sc = sc_lds + (fw * 16 + j) * NB;
+    const float *tsrow = nullptr;
+    if constexpr (FP8)
+        tsrow = static_cast<const float *>(scales) + (size_t)(min(feat0 + fw * 16, M - 1) >> 7) * S;
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+    // ---- register pipeline: PF steps of weights and activation pieces in flight
+    WStage<FP8> ws[PF];
+    u32x4 ax[PF][AP];
+    auto issue = [&](auto U, int i) {
+        const int s = step_of(i);
+        if constexpr (FP8) {
+            ws[U.value].w0 = bload16<kAuxCached>(rw, vw, wstep * s);
+            ws[U.value].w1 = bload16<kAuxCached>(rw, vw + 16, wstep * s);
+        } else {
+            ws[U.value].c = bload16<kAuxCached>(rw, vw, wstep * s);
+        }
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int ns = (C - wave + KW - 1) / KW;
-    const int rot = ns > 0 ? (int)(blockIdx.x % (unsigned)ns) : 0;  // see the Q4_0 kernel
-    auto chunk_of = [&](int i) {
-        int r = i + rot;
-        r = r >= ns ? r - ns : r;
-        return wave + r * KW;
+        for (int a = 0; a < AP; ++a)
+            ax[U.value][a] = bload16<kAuxCached>(ra, va[a], 256 * s);
     };
-    F8Stage<T> st[PF];
-    pipeline<PF>(
-        ns, [&](auto U, int i) { f8_load<T>(st[U.value], chunk_of(i), rw, ra, vw, va, tile_bytes); },
-        [&](auto U, int i, bool) { f8_compute<ACT, T>(st[U.value], chunk_of(i), srow, acc); });
-    reduce_store<T, KW>(acc, out, out_dtype, M, row0, nrows, tile0, 1.0f);
+    auto stage_act = [&](auto U, int buf) {
+        uint8_t *tp = tile_ptr(buf);
+#pragma unroll
+        for (int a = 0; a < AP; ++a)
+            act_piece_to_lds<FP8>(tp, ar[a], ap[a], ax[U.value][a]);
+    };
+    // One iteration: read this step's operands from LDS, stage the next step's
+    // activations, then the math (the reads come first: with one buffer the
+    // next step overwrites the tile).  FULL: a whole step of K inside this
+    // K-group's range, no runtime checks at all.
+    auto iterate = [&](auto U, int it, bool stage_next, auto Full) {
+        constexpr bool FULL = decltype(Full)::value;
+        constexpr int NEXT = (decltype(U)::value + 1) % PF;
+        const int s = step_of(it);
+        const uint8_t *tp = tile_ptr(it % NBUF);
+        u32x4 a[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            a[q] = *reinterpret_cast<const u32x4 *>(tp + (q * 64 + lane) * 16);
+        uint32_t sc[4] = {0u, 0u, 0u, 0u};
+        int nblk = 4;
+        if constexpr (!FP8) {
+            if constexpr (!FULL)
+                nblk = it < n_mine ? min(4, NB - 4 * s) : 0;
+            if (FULL || nblk == 4) {
+                if constexpr (SVEC) {
+                    const u32x2 p = *reinterpret_cast<const u32x2 *>(my_sc + 4 * s);
+                    sc[0] = p[0] & 0xFFFFu; sc[1] = p[0] >> 16; sc[2] = p[1] & 0xFFFFu; sc[3] = p[1] >> 16;
+                } else {
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb)
+                        sc[tb] = my_sc[4 * s + tb];
+                }
+            } else {
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    sc[tb] = tb < nblk ? (uint32_t)my_sc[4 * s + tb] : 0u;
+            }
+        }
+        if (stage_next)
+            stage_act(std::integral_constant<int, NEXT>{}, (it + 1) % NBUF);
+        if constexpr (FULL) {
+            if constexpr (FP8)
+                fp8_step<ACT>(ws[U.value], a, tsrow[s], acc);
+            else
+                q4_step<ACT, true>(ws[U.value].c, a, sc, 4, acc);
+        } else if (it < n_mine) {
+            if constexpr (FP8)
+                fp8_step<ACT>(ws[U.value], a, tsrow[s], acc);
+            else if (nblk == 4)
+                q4_step<ACT, true>(ws[U.value].c, a, sc, 4, acc);
+            else
+                q4_step<ACT, false>(ws[U.value].c, a, sc, nblk, acc);
+        }
+    };
+    using Full = std::true_type;
+    using Guarded = std::false_type;
+
+    // ---- prologue: first PF steps in flight, then the scales, then tile 0
+    const bool steady = n_iter - 1 >= 2 * PF;
+    if (steady) {
+        static_for<PF>([&](auto U) { issue(U, U.value); });
+    } else {
+        static_for<PF>([&](auto U) {
+            if (U.value < n_iter)
+                issue(U, U.value);
+        });
+    }
+    if constexpr (!FP8) {
+        // the workgroup's scale rows are contiguous in memory
+        const uint32_t sbytes = (uint32_t)frows * (uint32_t)NB * 2u;
+        const rsrc_t rs = make_rsrc(static_cast<const uint16_t *>(scales) + (size_t)feat0 * NB, sbytes);
+        uint8_t *dst = lds + (size_t)KW * NBUF * kActTileBytes;
+        // whole 16-byte chunks, then the remainder one scale at a time: the
+        // buffer range check works per dword, so a load ending mid-dword past
+        // the resource would read that dword as 0
+        const uint32_t full = sbytes & ~15u;
+        for (uint32_t o = threadIdx.x * 16u; o < full; o += 64u * NW * 16u)
+            *reinterpret_cast<u32x4 *>(dst + o) = bload16<kAuxCached>(rs, (int)o, 0);
+        for (uint32_t o = full + threadIdx.x * 2u; o < sbytes; o += 64u * NW * 2u)
+            *reinterpret_cast<uint16_t *>(dst + o) = (uint16_t)bload2<kAuxCached>(rs, (int)o, 0);
+    }
+    if (n_iter > 0)
+        stage_act(std::integral_constant<int, 0>{}, 0);
+    __syncthreads();
+
+    // ---- steady state: loads issued unconditionally, so the compiler counts
+    // them and waits only for the slot it is about to use
+    int i = 0;
+    if (steady) {
+        do {
+            static_for<PF>([&](auto U) {
+                const int it = i + U.value;
+                iterate(U, it, true, Full{});
+                __builtin_amdgcn_sched_barrier(0);
+                issue(U, it + PF);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (SHARED)
+                    __syncthreads();
+            });
+            i += PF;
+        } while (i + 2 * PF <= n_iter - 1);
+    }
+    // ---- tail: the last n_iter - i (<= 2 PF) iterations
+    static_for<2 * PF + 1>([&](auto V) {
+        constexpr int U = V.value % PF;
+        const int it = i + V.value;
+        if (it < n_iter) {
+            iterate(std::integral_constant<int, U>{}, it, it + 1 < n_iter, Guarded{});
+            if (it + PF < n_iter)
+                issue(std::integral_constant<int, U>{}, it + PF);
+        }
+        if constexpr (SHARED)
+            __syncthreads();
+    });
+    if constexpr (!SHARED)
+        __syncthreads();
+
+    // ---- combine the K-groups in fixed order, scale, round, store
+    float *red = reinterpret_cast<float *>(lds);  // reuses the activation tiles
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        red[((kg * FG + fw) * 4 + r) * 64 + lane] = acc[r];
+    __syncthreads();
+    for (int o = threadIdx.x; o < FG * 4 * 64; o += NW * 64) {
+        float s = red[o];
+#pragma unroll
+        for (int w = 1; w < KW; ++w)
+            s += red[w * FG * 4 * 64 + o];
+        const int ln = o & 63, r = (o >> 6) & 3, f = o >> 8;
+        const int feat = feat0 + f * 16 + (ln & 15);
+        const int row = 4 * (ln >> 4) + r;
+        if (row < nrows && feat < M)
+            store_out(out, out_dtype, (size_t)(row0 + row) * M + feat, alpha * s);
+    }
 }
 
-// --------------------------------------------------------------------------
-// Host-side launchers.
-// --------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
 namespace {
 
 constexpr int kMaxGridY = 65535;
 
-template <int ACT, int T, int KW>
-hipError_t launch_q4(const VerifyArgs &p) {
+template <bool FP8, int FG>
+constexpr int pipeline_depth() {
+    return FP8 ? (FG == 1 ? 3 : 4) : (FG == 1 ? 4 : 6);
+}
+
+template <int ACT, bool FP8, int FG, int KW>
+hipError_t launch_one(const VerifyArgs &p) {
+    constexpr int PF = pipeline_depth<FP8, FG>();
     const int tiles = (p.M + 15) / 16;
-    const int gx = (tiles + T - 1) / T;
+    const int gx = (tiles + FG - 1) / FG;
     const int groups = (p.N + 15) / 16;
+    const size_t shm = verify_lds_bytes(FP8, FG, KW, p.K);
+    auto kern = (FP8 || (p.K / 32) % 4 == 0) ? verify_kernel<ACT, FP8, FG, KW, PF, true>
+                                              : verify_kernel<ACT, FP8, FG, KW, PF, false>;
+    if (shm > 64 * 1024 &&
+        hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)shm) != hipSuccess)
+        return hipErrorInvalidValue;
     for (int g0 = 0; g0 < groups; g0 += kMaxGridY) {
         const int gy = std::min(kMaxGridY, groups - g0);
         const uint16_t *act = reinterpret_cast<const uint16_t *>(p.act) + (size_t)g0 * 16 * p.K;
         void *out = static_cast<char *>(p.out) + (size_t)g0 * 16 * p.M * out_elem_bytes(p.out_dtype);
         const int n = std::min(p.N - g0 * 16, gy * 16);
-        constexpr int PF = T == 1 ? 4 : (T == 2 ? 3 : 2);
-        if ((p.K / 32) % 4 == 0)
-            hipLaunchKernelGGL((q4_0_verify_kernel<ACT, T, KW, PF, true>), dim3(gx, gy), dim3(64 * KW), 0,
-                               p.stream, reinterpret_cast<const uint8_t *>(p.w),
-                               reinterpret_cast<const uint16_t *>(p.scales), act, out, p.out_dtype, n, p.M,
-                               p.K, p.alpha);
-        else
-            hipLaunchKernelGGL((q4_0_verify_kernel<ACT, T, KW, PF, false>), dim3(gx, gy), dim3(64 * KW), 0,
-                               p.stream, reinterpret_cast<const uint8_t *>(p.w),
-                               reinterpret_cast<const uint16_t *>(p.scales), act, out, p.out_dtype, n, p.M,
-                               p.K, p.alpha);
+        hipLaunchKernelGGL(kern, dim3(gx, gy), dim3(64 * FG * KW), shm, p.stream,
+                           reinterpret_cast<const uint8_t *>(p.w), p.scales, act, out, p.out_dtype, n, p.M, p.K,
+                           p.alpha);
     }
     return hipGetLastError();
 }
 
-template <int ACT, int T, int KW>
-hipError_t launch_fp8(const VerifyArgs &p) {
-    const int tiles = (p.M + 15) / 16;
-    const int gx = (tiles + T - 1) / T;
-    const int groups = (p.N + 15) / 16;
-    for (int g0 = 0; g0 < groups; g0 += kMaxGridY) {
-        const int gy = std::min(kMaxGridY, groups - g0);
-        const uint16_t *act = reinterpret_cast<const uint16_t *>(p.act) + (size_t)g0 * 16 * p.K;
-        void *out = static_cast<char *>(p.out) + (size_t)g0 * 16 * p.M * out_elem_bytes(p.out_dtype);
-        const int n = std::min(p.N - g0 * 16, gy * 16);
-        constexpr int PF = T == 1 ? 4 : (T == 2 ? 3 : 2);
-        hipLaunchKernelGGL((fp8_verify_kernel<ACT, T, KW, PF>), dim3(gx, gy), dim3(64 * KW), 0, p.stream,
-                           reinterpret_cast<const uint8_t *>(p.w), reinterpret_cast<const float *>(p.scales),
-                           act, out, p.out_dtype, n, p.M, p.K);
-    }
-    return hipGetLastError();
-}
-
-template <int ACT, int T>
-hipError_t dispatch_kw(const VerifyArgs &p, int kw, bool fp8) {
-    switch (kw) {
-    case 1: return fp8 ? launch_fp8<ACT, T, 1>(p) : launch_q4<ACT, T, 1>(p);
-    case 2: return fp8 ? launch_fp8<ACT, T, 2>(p) : launch_q4<ACT, T, 2>(p);
-    case 4: return fp8 ? launch_fp8<ACT, T, 4>(p) : launch_q4<ACT, T, 4>(p);
-    case 8: return fp8 ? launch_fp8<ACT, T, 8>(p) : launch_q4<ACT, T, 8>(p);
-    case 16: return fp8 ? launch_fp8<ACT, T, 16>(p) : launch_q4<ACT, T, 16>(p);
+template <int ACT, bool FP8, int FG>
+hipError_t dispatch_kw(const VerifyArgs &p) {
+    switch (p.waves_k) {
+    case 1: return launch_one<ACT, FP8, FG, 1>(p);
+    case 2: return launch_one<ACT, FP8, FG, 2>(p);
+    case 4: return launch_one<ACT, FP8, FG, 4>(p);
+    case 8:
+        if constexpr (FG <= 2)
+            return launch_one<ACT, FP8, FG, 8>(p);
+        return hipErrorInvalidValue;
+    case 16:
+        if constexpr (FG == 1)
+            return launch_one<ACT, FP8, FG, 16>(p);
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
 
-template <int ACT>
-hipError_t dispatch_t(const VerifyArgs &p, int t, int kw, bool fp8) {
-    switch (t) {
-    case 1: return dispatch_kw<ACT, 1>(p, kw, fp8);
-    case 2: return dispatch_kw<ACT, 2>(p, kw, fp8);
-    case 4: return dispatch_kw<ACT, 4>(p, kw, fp8);
+template <int ACT, bool FP8>
+hipError_t dispatch_fg(const VerifyArgs &p) {
+    switch (p.tiles_per_wg) {
+    case 1: return dispatch_kw<ACT, FP8, 1>(p);
+    case 2: return dispatch_kw<ACT, FP8, 2>(p);
+    case 4: return dispatch_kw<ACT, FP8, 4>(p);
     default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
+size_t verify_lds_bytes(bool fp8, int fg, int kw, int K) {
+    const size_t nbuf = fg > 1 ? 2 : 1;
+    const size_t act_b = (size_t)kw * nbuf * kActTileBytes;
+    const size_t sc_b = fp8 ? 0 : ((((size_t)fg * 16 * (K / 32) * 2) + 15) & ~(size_t)15);
+    return act_b + sc_b;  // the final reduction (kw * fg KB) fits in act_b
+}
+
+bool verify_shape_ok(bool fp8, int fg, int kw, int K) {
+    if (!(fg == 1 || fg == 2 || fg == 4) || !(kw == 1 || kw == 2 || kw == 4 || kw == 8 || kw == 16))
+        return false;
+    if (fg * kw > 16)
+        return false;
+    return verify_lds_bytes(fp8, fg, kw, K) <= kMaxLdsBytes;
+}
+
 hipError_t launch_verify(const VerifyArgs &p, bool fp8) {
     if (p.act_dtype == VQ_DTYPE_BF16)
-        return dispatch_t<VQ_DTYPE_BF16>(p, p.tiles_per_wave, p.waves_k, fp8);
-    return dispatch_t<VQ_DTYPE_F16>(p, p.tiles_per_wave, p.waves_k, fp8);
+        return fp8 ? dispatch_fg<VQ_DTYPE_BF16, true>(p) : dispatch_fg<VQ_DTYPE_BF16, false>(p);
+    return fp8 ? dispatch_fg<VQ_DTYPE_F16, true>(p) : dispatch_fg<VQ_DTYPE_F16, false>(p);
 }
 
 }  // namespace vq

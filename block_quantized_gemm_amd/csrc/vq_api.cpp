@@ -44,25 +44,28 @@ bool float_act(int d) { return d == VQ_DTYPE_F16 || d == VQ_DTYPE_BF16; }
 bool out_ok(int d) { return d == VQ_DTYPE_F16 || d == VQ_DTYPE_BF16 || d == VQ_DTYPE_F32; }
 bool dim_ok(int64_t v) { return v >= 1 && v <= VQ_MAX_DIM; }
 
-int pow2_floor(int v) {
-    int p = 1;
-    while (p * 2 <= v)
-        p *= 2;
-    return p;
-}
+// Default launch shape for an (M, K) verify GEMM: FG feature tiles per
+// workgroup share each staged activation tile (activation traffic per weight
+// byte falls by FG) while keeping about one workgroup per CU or more on the
+// 256-CU part; then KW K-groups per workgroup for ~2-2.5k waves in flight,
+// keeping at least 4 steps of 128 k per K-group.  A function of (M, K) only.
+constexpr int64_t kMinWorkgroups = 240;
+constexpr int64_t kTargetWaves = 2600;
 
-// Default launch shape for an (M, K) verify GEMM.  Aim for ~10 waves per CU
-// on the 256-CU part with at least two K-steps per wave; take two feature
-// tiles per wave once there are enough tiles, to halve activation re-reads.
-void default_shape(bool fp8, int64_t m, int64_t k, int *t_out, int *kw_out) {
+void default_shape(bool fp8, int64_t m, int64_t k, int *fg_out, int *kw_out) {
     const int64_t tiles = (m + 15) / 16;
     const int64_t steps = fp8 ? k / 128 : (k / 32 + 3) / 4;
-    const int t = tiles >= 1024 ? 2 : 1;
-    const int64_t cols = (tiles + t - 1) / t;
+    int fg = 1;
+    if ((tiles + 3) / 4 >= kMinWorkgroups)
+        fg = 4;
+    else if ((tiles + 1) / 2 >= kMinWorkgroups)
+        fg = 2;
+    const int64_t wgs = (tiles + fg - 1) / fg;
     int kw = 1;
-    while (kw < 16 && cols * (kw * 2) <= 2560 && steps >= 2 * (kw * 2))
+    while (fg * kw * 2 <= 16 && wgs * fg * kw * 2 <= kTargetWaves && (steps + kw * 2 - 1) / (kw * 2) >= 4 &&
+           vq::verify_shape_ok(fp8, fg, kw * 2, (int)k))
         kw *= 2;
-    *t_out = t;
+    *fg_out = fg;
     *kw_out = kw;
 }
 
@@ -83,7 +86,7 @@ int run_verify(bool fp8, const void *w, const void *scales, const void *act, int
         tpw = dt;
     if (kw == 0)
         kw = dk;
-    if (!(tpw == 1 || tpw == 2 || tpw == 4) || !(kw == 1 || kw == 2 || kw == 4 || kw == 8 || kw == 16))
+    if (!vq::verify_shape_ok(fp8, tpw, kw, (int)k))
         return VQ_ERR_BAD_CONFIG;
     const int dev = check_device();
     if (dev != VQ_OK)

@@ -135,11 +135,14 @@ int vq_hadamard32_quant_int8(const void *x, int x_dtype,
 
 /*
  * vq_gemm_q4_0_ex / vq_gemm_fp8_blk128_ex -- the same operations with an
- * explicit launch shape, for tuning: `tiles_per_wave` output tiles of 16
- * features per wavefront (1, 2 or 4) and `waves_k` wavefronts splitting K
- * inside one workgroup (1, 2, 4, 8 or 16); 0 for either picks the default for
- * (M, K).  Results are bit-identical across N for a fixed launch shape; a
- * different launch shape may round differently.  Float activations only.
+ * explicit launch shape, for tuning: `tiles_per_wave` is the number of
+ * 16-feature tiles per workgroup that share each staged activation tile
+ * (1, 2 or 4; one wave per tile and K-group) and `waves_k` the number of
+ * K-groups per workgroup (1, 2, 4, 8 or 16), with tiles_per_wave * waves_k <=
+ * 16 and the workgroup's LDS within 160 KiB (VQ_ERR_BAD_CONFIG otherwise);
+ * 0 for either picks the default for (M, K).  Results are bit-identical across
+ * N for a fixed launch shape; a different launch shape may round differently.
+ * Float activations only.
  */
 int vq_gemm_q4_0_ex(const void *w_codes, const void *w_scales,
                     const void *act, int act_dtype,

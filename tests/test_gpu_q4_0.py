@@ -184,14 +184,34 @@ def test_ragged_shapes_parity(M, K, N):
 @pytest.mark.parametrize("kw", [1, 2, 4, 8, 16])
 def test_every_launch_shape_parity_and_exact_integers(tpw, kw):
     g = np.random.Generator(np.random.PCG64(105))
-    M, K, N = 272, 1056, 16          # 17 tiles, 33 blocks: partial tiles-per-wave and a partial K step
+    M, K, N = 272, 1056, 16          # 17 tiles, 33 blocks: partial workgroups and a partial last K step
     codes = W.q4_0_codes(M, K, g)
     q = Q4(codes, W.fp16_scales_uniform(M, K, g))
     a = W.f32_to_bf16_bits(g.standard_normal((N, K)))
+    if tpw * kw > 16:
+        with pytest.raises(vq.VqError) as e:
+            q.run(a, tiles_per_wave=tpw, waves_k=kw)
+        assert e.value.status == vq.VQ_ERR_BAD_CONFIG
+        return
     parity(out_to_f64(q.run(a, tiles_per_wave=tpw, waves_k=kw)), q.oracle(a), "bf16")
     qi = Q4(codes, np.full((M, K // 32), 0x3C00, dtype=np.uint16))
     ai = W.f32_to_bf16_bits(g.integers(-4, 5, size=(N, K)))
     assert np.array_equal(out_to_f64(qi.run(ai, "bf16", "f32", tiles_per_wave=tpw, waves_k=kw)), qi.oracle(ai))
+
+
+@pytest.mark.parametrize("tpw,kw", [(1, 16), (2, 8), (4, 4), (4, 2), (2, 1)])
+def test_launch_shapes_rows_bit_identical_across_widths(tpw, kw):
+    """Width invariance holds in every launch shape, not only the default one."""
+    g = np.random.Generator(np.random.PCG64(107))
+    M, K = 400, 2080
+    q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_lognormal(M, K, g))
+    x = W.f32_to_bf16_bits(0.5 * g.standard_t(3, size=(16, K)))
+    full = bits_u16(q.run(x, tiles_per_wave=tpw, waves_k=kw))
+    for n in (0, 7, 15):
+        one = bits_u16(q.run(np.ascontiguousarray(x[n:n + 1]), tiles_per_wave=tpw, waves_k=kw))
+        assert np.array_equal(one[0], full[n])
+    assert np.array_equal(bits_u16(q.run(np.ascontiguousarray(x[3:11]), tiles_per_wave=tpw, waves_k=kw)),
+                          full[3:11])
 
 
 def test_many_row_groups():
