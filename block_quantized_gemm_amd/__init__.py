@@ -25,6 +25,10 @@ VQ_ERR_BAD_DTYPE = -4
 VQ_ERR_DEVICE = -5
 VQ_ERR_LAUNCH = -6
 VQ_ERR_BAD_CONFIG = -7
+VQ_ERR_WORKSPACE = -8
+
+KIND_Q4_0 = 0
+KIND_FP8_BLK128 = 1
 
 DTYPE_F16 = 1
 DTYPE_BF16 = 2
@@ -36,19 +40,30 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _I64 = ctypes.c_int64
 _F = ctypes.c_float
+_SZ = ctypes.c_size_t
 SIGNATURES = {
-    "vq_gemm_q4_0": (_I, [_P, _P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _F, _P]),
-    "vq_gemm_fp8_blk128": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P]),
+    "vq_gemm_q4_0": (_I, [_P, _P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _F, _P, _SZ, _P]),
+    "vq_gemm_fp8_blk128": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
     "vq_hadamard32_quant_int8": (_I, [_P, _I, _P, _P, _I64, _I64, _P]),
-    "vq_gemm_q4_0_ex": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _F, _I, _I, _P]),
-    "vq_gemm_fp8_blk128_ex": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _I, _I, _P]),
-    "vq_default_launch_shape": (_I, [_I, _I64, _I64, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "vq_workspace_bytes": (_SZ, [_I, _I64, _I64]),
+    "vq_gemm_q4_0_ex": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _F, _I, _I, _I, _P, _SZ, _P]),
+    "vq_gemm_fp8_blk128_ex": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _I, _I, _I, _P, _SZ, _P]),
+    "vq_default_launch_shape": (_I, [_I, _I64, _I64, _SZ, ctypes.POINTER(_I), ctypes.POINTER(_I),
+                                     ctypes.POINTER(_I), ctypes.POINTER(_SZ)]),
+    "vq_gemm_q4_0_grouped": (_I, [_P, _I, _I, _I, _I64, _F, _P, _SZ, _P]),
+    "vq_gemm_fp8_blk128_grouped": (_I, [_P, _I, _I, _I, _I64, _P, _SZ, _P]),
+    "vq_workspace_bytes_grouped": (_SZ, [_I, _P, _I]),
     "vq_status_string": (ctypes.c_char_p, [_I]),
     "vq_version": (_I, []),
 }
 
 _lock = threading.Lock()
 _lib = None
+
+
+class VerifyProblem(ctypes.Structure):
+    """Mirror of vq_verify_problem."""
+    _fields_ = [("w", _P), ("scales", _P), ("act", _P), ("out", _P), ("m", _I64), ("k", _I64)]
 
 
 class VqError(RuntimeError):
@@ -116,14 +131,65 @@ def _check_2d(t, name, shape):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
 
 
-def gemm_q4_0(codes, scales, x, out, *, x_scales=None, alpha: float = 1.0, stream=None,
-              tiles_per_wave: int = 0, waves_k: int = 0):
+class Workspace:
+    """A zero-filled device buffer for the verify GEMMs' split-K partial sums.
+
+    The library leaves it ready for the next call, so it is zeroed once.
+    Calls sharing one workspace must be ordered (one stream)."""
+
+    def __init__(self, nbytes: int, device=None):
+        torch = _torch()
+        self.tensor = torch.zeros(max(int(nbytes), 16), dtype=torch.uint8,
+                                  device=device if device is not None else "cuda")
+
+    @property
+    def nbytes(self) -> int:
+        return self.tensor.numel()
+
+    def ptr(self) -> int:
+        return self.tensor.data_ptr()
+
+
+_auto_ws = {}
+_auto_lock = threading.Lock()
+
+
+def _workspace_args(workspace, kind: int, m: int, k: int, device, stream_handle: int):
+    """(pointer, bytes) for a call: a Workspace, None (no split), or "auto" = a
+    workspace cached per (device, stream), grown to what the default shape uses."""
+    if workspace is None:
+        return None, 0
+    if isinstance(workspace, Workspace):
+        return workspace.ptr(), workspace.nbytes
+    if workspace != "auto":
+        raise TypeError("workspace must be a Workspace, None or 'auto'")
+    need = int(lib().vq_workspace_bytes(kind, m, k))
+    if need == 0:
+        return None, 0
+    key = (str(device), stream_handle)
+    with _auto_lock:
+        ws = _auto_ws.get(key)
+        if ws is None or ws.nbytes < need:
+            ws = Workspace(need, device)
+            _auto_ws[key] = ws
+    return ws.ptr(), ws.nbytes
+
+
+def workspace_bytes(kind: str, m: int, k: int) -> int:
+    """Workspace bytes the default launch shape of an (M, K) verify GEMM uses."""
+    return int(lib().vq_workspace_bytes(KIND_FP8_BLK128 if kind == "fp8" else KIND_Q4_0, m, k))
+
+
+def gemm_q4_0(codes, scales, x, out, *, x_scales=None, alpha: float = 1.0, workspace="auto", stream=None,
+              tiles_per_wave: int = 0, waves_per_group: int = 0, k_slices: int = 0):
     """out[N][M] = alpha * x[N][K] @ dequant(codes, scales)[M][K]^T.
 
     codes: uint8 [M][K/2]; scales: float16 [M][K/32]; x: float16 / bfloat16 [N][K]
     or int8 [N][K] with x_scales float16 [N][K/32]; out: float16 / bfloat16 /
-    float32 [N][M].  tiles_per_wave / waves_k select an explicit launch shape
-    (float activations only; 0 = library default)."""
+    float32 [N][M].  workspace: "auto" (a cached per-stream Workspace), a
+    Workspace, or None (K is not split).  tiles_per_wave / waves_per_group /
+    k_slices select an explicit launch shape (float activations only; 0 =
+    library default)."""
     N, K = x.shape
     M = codes.shape[0]
     _check_2d(codes, "codes", (M, K // 2))
@@ -131,31 +197,35 @@ def gemm_q4_0(codes, scales, x, out, *, x_scales=None, alpha: float = 1.0, strea
     _check_2d(out, "out", (N, M))
     act_dtype = _dtype_code(x)
     L = lib()
+    sh = _stream(stream)
     if act_dtype == DTYPE_I8:
         if x_scales is None:
             raise ValueError("int8 activations need x_scales")
         _check_2d(x_scales, "x_scales", (N, K // 32))
         st = L.vq_gemm_q4_0(_dev_ptr(codes, "codes"), _dev_ptr(scales, "scales"), _dev_ptr(x, "x"),
                             act_dtype, _dev_ptr(x_scales, "x_scales"), _dev_ptr(out, "out"),
-                            _dtype_code(out), N, M, K, float(alpha), _stream(stream))
+                            _dtype_code(out), N, M, K, float(alpha), None, 0, sh)
         _check(st, "vq_gemm_q4_0")
         return out
     if x_scales is not None:
         raise ValueError("x_scales only go with int8 activations")
-    if tiles_per_wave or waves_k:
+    wp, wn = _workspace_args(workspace, KIND_Q4_0, M, K, codes.device, sh)
+    if tiles_per_wave or waves_per_group or k_slices:
         st = L.vq_gemm_q4_0_ex(_dev_ptr(codes, "codes"), _dev_ptr(scales, "scales"), _dev_ptr(x, "x"),
                                act_dtype, _dev_ptr(out, "out"), _dtype_code(out), N, M, K,
-                               float(alpha), int(tiles_per_wave), int(waves_k), _stream(stream))
+                               float(alpha), int(tiles_per_wave), int(waves_per_group), int(k_slices),
+                               wp, wn, sh)
         _check(st, "vq_gemm_q4_0_ex")
     else:
         st = L.vq_gemm_q4_0(_dev_ptr(codes, "codes"), _dev_ptr(scales, "scales"), _dev_ptr(x, "x"),
                             act_dtype, None, _dev_ptr(out, "out"), _dtype_code(out), N, M, K,
-                            float(alpha), _stream(stream))
+                            float(alpha), wp, wn, sh)
         _check(st, "vq_gemm_q4_0")
     return out
 
 
-def gemm_fp8_blk128(w, tile_scales, x, out, *, stream=None, tiles_per_wave: int = 0, waves_k: int = 0):
+def gemm_fp8_blk128(w, tile_scales, x, out, *, workspace="auto", stream=None, tiles_per_wave: int = 0,
+                    waves_per_group: int = 0, k_slices: int = 0):
     """out[N][M] = x[N][K] @ (e4m3(w) * tile_scales[m/128][k/128])^T.
 
     w: uint8 [M][K] (E4M3FN bits); tile_scales: float32 [ceil(M/128)][K/128];
@@ -166,17 +236,90 @@ def gemm_fp8_blk128(w, tile_scales, x, out, *, stream=None, tiles_per_wave: int 
     _check_2d(tile_scales, "tile_scales", ((M + 127) // 128, K // 128))
     _check_2d(out, "out", (N, M))
     L = lib()
-    if tiles_per_wave or waves_k:
+    sh = _stream(stream)
+    wp, wn = _workspace_args(workspace, KIND_FP8_BLK128, M, K, w.device, sh)
+    if tiles_per_wave or waves_per_group or k_slices:
         st = L.vq_gemm_fp8_blk128_ex(_dev_ptr(w, "w"), _dev_ptr(tile_scales, "tile_scales"), _dev_ptr(x, "x"),
                                      _dtype_code(x), _dev_ptr(out, "out"), _dtype_code(out), N, M, K,
-                                     int(tiles_per_wave), int(waves_k), _stream(stream))
+                                     int(tiles_per_wave), int(waves_per_group), int(k_slices), wp, wn, sh)
         _check(st, "vq_gemm_fp8_blk128_ex")
     else:
         st = L.vq_gemm_fp8_blk128(_dev_ptr(w, "w"), _dev_ptr(tile_scales, "tile_scales"), _dev_ptr(x, "x"),
-                                  _dtype_code(x), _dev_ptr(out, "out"), _dtype_code(out), N, M, K,
-                                  _stream(stream))
+                                  _dtype_code(x), _dev_ptr(out, "out"), _dtype_code(out), N, M, K, wp, wn, sh)
         _check(st, "vq_gemm_fp8_blk128")
     return out
+
+
+class GroupedCall:
+    """A prepared grouped verify GEMM: the problem table is built once, so a
+    repeated call (a decode step) costs one C call.
+
+    problems: list of (w, scales, x, out) device tensors, all with the same
+    x dtype, out dtype and row count; kind "q4_0" (w uint8 [M][K/2], scales
+    float16 [M][K/32]) or "fp8" (w uint8 [M][K], scales float32
+    [ceil(M/128)][K/128]).  workspace: a Workspace (grown here to what the
+    group needs), "auto" (a new one of that size) or None (K not split)."""
+
+    def __init__(self, kind: str, problems, *, alpha: float = 1.0, workspace="auto"):
+        if kind not in ("q4_0", "fp8"):
+            raise ValueError("kind must be 'q4_0' or 'fp8'")
+        if not problems:
+            raise ValueError("empty group")
+        self.kind = KIND_FP8_BLK128 if kind == "fp8" else KIND_Q4_0
+        self.alpha = float(alpha)
+        x0, o0 = problems[0][2], problems[0][3]
+        self.n_rows = x0.shape[0]
+        self.act_dtype, self.out_dtype = _dtype_code(x0), _dtype_code(o0)
+        self.table = (VerifyProblem * len(problems))()
+        self._keep = []
+        for i, (w, sc, x, out) in enumerate(problems):
+            N, K = x.shape
+            M = w.shape[0]
+            if N != self.n_rows or _dtype_code(x) != self.act_dtype or _dtype_code(out) != self.out_dtype:
+                raise ValueError("problem %d: row count and dtypes must match the first problem" % i)
+            if self.kind == KIND_Q4_0:
+                _check_2d(w, "w", (M, K // 2))
+                _check_2d(sc, "scales", (M, K // 32))
+            else:
+                _check_2d(w, "w", (M, K))
+                _check_2d(sc, "scales", ((M + 127) // 128, K // 128))
+            _check_2d(out, "out", (N, M))
+            self.table[i] = VerifyProblem(_dev_ptr(w, "w"), _dev_ptr(sc, "scales"), _dev_ptr(x, "x"),
+                                          _dev_ptr(out, "out"), M, K)
+            self._keep.append((w, sc, x, out))
+        self.count = len(problems)
+        need = int(lib().vq_workspace_bytes_grouped(self.kind, self.table, self.count))
+        if workspace is None:
+            self.ws = None
+        elif isinstance(workspace, Workspace):
+            self.ws = workspace if workspace.nbytes >= need else Workspace(need, x0.device)
+        elif workspace == "auto":
+            self.ws = Workspace(need, x0.device) if need else None
+        else:
+            raise TypeError("workspace must be a Workspace, None or 'auto'")
+        self.workspace_bytes = need
+
+    def __call__(self, stream=None):
+        L = lib()
+        wp, wn = (self.ws.ptr(), self.ws.nbytes) if self.ws is not None else (None, 0)
+        if self.kind == KIND_Q4_0:
+            st = L.vq_gemm_q4_0_grouped(self.table, self.count, self.act_dtype, self.out_dtype, self.n_rows,
+                                        self.alpha, wp, wn, _stream(stream))
+            _check(st, "vq_gemm_q4_0_grouped")
+        else:
+            st = L.vq_gemm_fp8_blk128_grouped(self.table, self.count, self.act_dtype, self.out_dtype,
+                                              self.n_rows, wp, wn, _stream(stream))
+            _check(st, "vq_gemm_fp8_blk128_grouped")
+
+
+def gemm_q4_0_grouped(problems, *, alpha: float = 1.0, workspace="auto", stream=None):
+    """Grouped Q4_0 verify GEMMs: problems = [(codes, scales, x, out), ...]."""
+    GroupedCall("q4_0", problems, alpha=alpha, workspace=workspace)(stream)
+
+
+def gemm_fp8_blk128_grouped(problems, *, workspace="auto", stream=None):
+    """Grouped FP8 verify GEMMs: problems = [(w, tile_scales, x, out), ...]."""
+    GroupedCall("fp8", problems, workspace=workspace)(stream)
 
 
 def hadamard32_quant_int8(x, q_out, scales_out, *, stream=None):
@@ -192,10 +335,13 @@ def hadamard32_quant_int8(x, q_out, scales_out, *, stream=None):
     return q_out, scales_out
 
 
-def default_launch_shape(kind: str, m: int, k: int):
-    """(tiles_per_wave, waves_k) the library picks for an (M, K) verify GEMM."""
-    t = ctypes.c_int(0)
-    w = ctypes.c_int(0)
-    _check(lib().vq_default_launch_shape(1 if kind == "fp8" else 0, m, k, ctypes.byref(t), ctypes.byref(w)),
+def default_launch_shape(kind: str, m: int, k: int, workspace_bytes=None):
+    """(tiles_per_wave, waves_per_group, k_slices, workspace_used) the library
+    picks for an (M, K) verify GEMM given workspace_bytes (None = unlimited)."""
+    t, w, s = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    used = ctypes.c_size_t(0)
+    cap = (1 << 64) - 1 if workspace_bytes is None else int(workspace_bytes)
+    _check(lib().vq_default_launch_shape(KIND_FP8_BLK128 if kind == "fp8" else KIND_Q4_0, m, k, cap,
+                                         ctypes.byref(t), ctypes.byref(w), ctypes.byref(s), ctypes.byref(used)),
            "vq_default_launch_shape")
-    return t.value, w.value
+    return t.value, w.value, s.value, used.value

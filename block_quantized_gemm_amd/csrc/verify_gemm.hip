@@ -18,34 +18,63 @@
 //  * Q4_0: every lane streams one 16-byte block of one feature; a 4x4
 //    lane-group transpose (permlane swaps) hands each lane its 4-byte slice of
 //    each block; codes become the exact 16-bit values MAGIC + q; an MFMA with
-//    the constant -(MAGIC + 8) forms the per-row offset term, which enters the
-//    block MFMA as its accumulator, so the MFMA returns the exact block sum
-//    (q - 8) x in fp32.  The fp16 block scale is one fp32 FMA per output.
-//  * FP8: 32 contiguous bytes per lane per 128-wide chunk, hardware E4M3 ->
-//    16-bit conversion (exact), 4 MFMAs per chunk, one FMA with the fp32 tile
+//    the constant -(MAGIC + 8) forms the per-row offset term (once per block,
+//    shared by all of the wave's tiles), which enters the block MFMA as its
+//    accumulator, so the MFMA returns the block sum (q - 8) x in fp32.  The
+//    fp16 block scale is one fp32 FMA per output.
+//  * FP8: 32 contiguous bytes per lane per 128-wide step, hardware E4M3 ->
+//    16-bit conversion (exact), 4 MFMAs per step, one FMA with the fp32 tile
 //    scale.
 //
-// Data movement (the kernel is bound by what reaches the CUs):
-//  * A workgroup is FG x KW waves.  The FG waves of one K-group work on FG
-//    different 16-feature tiles at the same K step; the KW K-groups split K
-//    into contiguous ranges.  Per 128-wide step, a K-group's 16 x 128
-//    activation tile is read from memory once (one contiguous 16-byte load per
-//    lane and piece, whole cache lines), scattered into LDS in MFMA operand
-//    order and read back by all FG waves, so activation traffic per weight
-//    byte falls by FG.  With FG = 1 the tile is private to its wave and needs
-//    no barrier; with FG > 1 it is double-buffered with one barrier per step.
-//  * The workgroup's Q4_0 block scales are staged into LDS once.
+// Work decomposition (the kernel is bound by HBM and by what reaches the CUs):
+//  * A workgroup is W waves; each wave owns T tiles of 16 features, so the
+//    workgroup covers TG = T * W tiles.  K is cut into S slices of `sl` steps
+//    of 128; workgroup (tile group, slice) computes its TG tiles over its
+//    slice.  The grid is sized so that all workgroups are resident at once
+//    and every wave has the same work.
+//  * The slice's 16 activation rows (and, for Q4_0, the workgroup's block
+//    scales) are staged into LDS in MFMA operand order with whole-line loads;
+//    afterwards the waves only read LDS (no barrier inside a chunk).  Each
+//    staged activation element serves TG tiles, so activation traffic is
+//    1/TG of what a per-tile read would cost.
 //  * Weight bytes are streamed with 16-byte raw buffer loads (rows past M read
 //    as zeros) PF steps ahead of the compute in a register pipeline.
-//  * K-group partial sums are combined through LDS in the fixed order
-//    0, 1, ..., KW-1: no atomics, the same result on every run.
+//  * Slices of one tile group are combined through a caller workspace: each
+//    workgroup writes its fp32 partial tiles, then counts itself in; the last
+//    to arrive adds the S partials in the fixed order 0, 1, ..., S-1 and
+//    stores the output.  No value is combined by atomics, so the result is
+//    the same on every run and whichever workgroup finishes last.
+//  * A slice longer than one LDS chunk (always the case without a workspace,
+//    S = 1) is walked chunk by chunk, re-staging the activations.
 #include "vq_device.h"
 #include "vq_internal.h"
 
 namespace vq {
 
-constexpr int kStepK = 128;                      // k per step: 4 Q4_0 blocks or one FP8 chunk
-constexpr int kActTileBytes = 16 * kStepK * 2;   // one step of 16 activation rows (bf16/fp16)
+constexpr int kStepK = 128;                    // k per step: 4 Q4_0 blocks or one FP8 chunk
+constexpr int kActStepBytes = 16 * kStepK * 2;  // one step of 16 activation rows (bf16/fp16)
+
+// One problem of a launch (kernel arguments, by value).
+struct KProblem {
+    const uint8_t *w;     // Q4_0 codes [M][K/2] or E4M3 bytes [M][K]
+    const void *scales;   // Q4_0 f16 [M][K/32] or FP8 f32 [ceil(M/128)][K/128]
+    const uint16_t *act;  // this row group's [<=16][K] activations
+    void *out;            // this row group's [<=16][M] outputs
+    float *part;          // split: fp32 partial tiles [tile groups][S][TG][64 lanes][4]
+    uint32_t *cnt;        // split: arrival counters [tile groups], zero between calls
+    int M, K;
+    int S, sl, chunk;     // slices, steps per slice, steps per LDS chunk
+    int item0;            // first workgroup of this problem in the launch
+};
+
+// A launch: up to kGroupPerLaunch problems sharing the launch shape, the row
+// count (<= 16), the output dtype and alpha.  Workgroup b works on item
+// b - item0 of the last problem whose item0 <= b.
+struct KGroup {
+    KProblem p[kGroupPerLaunch];
+    int count, N, out_dtype;
+    float alpha;
+};
 
 // LDS position of activation piece p (k = 8p .. 8p+7 of the step) of row r, in
 // the operand layout [32-k group q][lane = 16 g + r][16 bytes]:
@@ -67,273 +96,317 @@ __device__ __forceinline__ void act_piece_to_lds(uint8_t *tile, int r, int p, u3
     }
 }
 
-template <bool FP8>
-struct WStage;
-template <>
-struct WStage<false> {
-    u32x4 c;  // 16 code bytes: block 4s + g of the lane's feature
-};
-template <>
-struct WStage<true> {
-    u32x4 w0, w1;  // 32 E4M3 bytes: k = 32g .. 32g + 31 of the step
-};
+// Most steps per LDS chunk for a workgroup of W waves: bounded so that all
+// staging loads of a chunk (<= 8 per thread for activations, 2 T for scales)
+// can be in flight at once.
+__host__ __device__ constexpr int max_chunk_steps(int W) { return W >= 4 ? 8 : 4; }
 
-// One Q4_0 step (4 blocks) for one 16-feature tile.
-template <int ACT, bool FULL>
-__device__ __forceinline__ void q4_step(u32x4 c, const u32x4 (&a)[4], const uint32_t (&sc)[4], int nblk,
-                                        f32x4 &acc) {
-    using A16 = Act16<ACT>;
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    const u32x4 negc = {A16::kNegOffset, A16::kNegOffset, A16::kNegOffset, A16::kNegOffset};
-    uint32_t d[4] = {c[0], c[1], c[2], c[3]};
-    transpose_lane_groups(d[0], d[1], d[2], d[3]);  // lane group g: dword g of blocks 0..3
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        if (FULL || tb < nblk) {
-            const f32x4 corr = A16::mfma(a[tb], negc, zero4);  // -(MAGIC + 8) * sum x, per row
-            const f32x4 dot = A16::mfma(a[tb], q4_operand<A16::kMagicByte>(d[tb]), corr);
-            const float s = h2f(sc[tb]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[r] = __builtin_fmaf(s, dot[r], acc[r]);
-        }
-    }
-}
+__host__ __device__ inline int verify_tile_groups_dev(int M, int tg) { return ((M + 15) / 16 + tg - 1) / tg; }
 
-// One FP8 chunk (128 k) for one 16-feature tile.
-template <int ACT>
-__device__ __forceinline__ void fp8_step(const WStage<true> &w, const u32x4 (&a)[4], float ts, f32x4 &acc) {
-    using A16 = Act16<ACT>;
-    f32x4 part = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const u32x4 src = u < 2 ? w.w0 : w.w1;
-        const uint32_t e0 = src[2 * (u & 1)], e1 = src[2 * (u & 1) + 1];
-        const u32x4 bop = {A16::template fp8x2<false>(e0), A16::template fp8x2<true>(e0),
-                           A16::template fp8x2<false>(e1), A16::template fp8x2<true>(e1)};
-        part = A16::mfma(a[u], bop, part);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        acc[r] = __builtin_fmaf(ts, part[r], acc[r]);
-}
+// Pipeline depth: stages of weight loads in flight per wave.
+__host__ __device__ constexpr int pipeline_depth(bool fp8, int T) { return ((fp8 ? 2 * T : T) >= 4) ? 2 : 4; }
 
-// ---------------------------------------------------------------------------
-// The verify kernel.  grid = (ceil(tiles / FG), groups of 16 rows), block =
-// 64 * FG * KW.  Dynamic LDS: the K-groups' activation tiles (two buffers
-// each when FG > 1, one otherwise), then the Q4_0 block scales of the
-// workgroup's FG * 16 feature rows.
-// ---------------------------------------------------------------------------
-template <int ACT, bool FP8, int FG, int KW, int PF, bool SVEC>
-__global__ __launch_bounds__(64 * FG * KW) void verify_kernel(
-    const uint8_t *__restrict__ wts, const void *__restrict__ scales, const uint16_t *__restrict__ act,
-    void *__restrict__ out, int out_dtype, int N, int M, int K, float alpha) {
+template <int ACT, bool FP8, int T, int W, int PF>
+__global__ __launch_bounds__(64 * W) void verify_kernel(const KGroup grp) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    static_assert(FG == 1 || FG == 2 || FG == 4, "FG");
-    constexpr int NW = FG * KW;
-    constexpr int AP = 4 / FG;          // 16-byte activation pieces per lane per step
-    constexpr bool SHARED = FG > 1;     // tile shared across waves: double buffer + barriers
-    constexpr int NBUF = SHARED ? 2 : 1;
+    using A16 = Act16<ACT>;
+    constexpr int TG = T * W;                   // tiles per workgroup
+    constexpr int NT = 64 * W;                  // threads per workgroup
+    constexpr int WB = FP8 ? 2 : 1;             // 16-byte weight loads per lane, tile and step
+    constexpr int kStepBytes = FP8 ? 128 : 64;  // weight bytes per feature row per step
+    constexpr int CH = max_chunk_steps(W);
+    constexpr int kOut = 0x7FFFFFF0;            // an offset past every buffer: the load returns zeros
+    static_assert(CH % PF == 0, "chunks hold whole pipeline rounds");
 
+    // ---- this workgroup's problem and item (wave-uniform scalar work)
+    int pi = 0;
+    for (int q = 1; q < grp.count; ++q)
+        if ((int)blockIdx.x >= grp.p[q].item0)
+            pi = q;
+    const KProblem &a = grp.p[pi];
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
-    const int fw = wave % FG;  // this wave's feature tile in the workgroup
-    const int kg = wave / FG;  // this wave's K-group
     const int j = lane & 15;
     const int g = lane >> 4;
-
+    const int M = a.M, K = a.K, S = a.S;
     const int NB = K >> 5;
-    const int S = FP8 ? (K >> 7) : (NB + 3) >> 2;  // steps; the last Q4_0 step may be partial
-    // K-group kg takes steps kg, kg + KW, kg + 2 KW, ...: the KW waves of a tile
-    // read neighbouring 64-byte pieces of each weight row, so the workgroup
-    // sweeps every row in 64 KW-byte runs (DRAM pages are visited once, not
-    // once per piece).  Group sizes differ by at most one, so only a group's
-    // final iteration can be empty and only the final step of K can be
-    // partial; the steady-state loop reaches neither.
-    const int n_iter = (S + KW - 1) / KW;
-    const int n_mine = (S - kg + KW - 1) / KW;
-    auto step_of = [&](int it) { return kg + it * KW; };
-    const int feat0 = blockIdx.x * FG * 16;
-    const int frows = min(M - feat0, FG * 16);
-    const int row0 = blockIdx.y * 16;
-    const int nrows = min(16, N - row0);
+    const int steps = FP8 ? (K >> 7) : ((NB + 3) >> 2);  // the last Q4_0 step may be partial
+    const int item = (int)blockIdx.x - a.item0;
+    const int tg = item / S;
+    const int sidx = item - tg * S;
+    const int s0 = sidx * a.sl;
+    const int ns = min(a.sl, steps - s0);  // >= 1: the host never makes an empty slice
+    const int nrows = grp.N;               // <= 16
+    const int fwg = tg * TG * 16;          // first feature of the workgroup
+    const int fwv = fwg + wave * T * 16;   // first feature of this wave
+    const int wrow = FP8 ? K : (K >> 1);   // weight bytes per feature row
+    const int chunk = a.chunk;             // <= CH, a multiple of PF
 
-    // Buffer resources sized to the workgroup's rows: reads past them return 0.
-    const int wrow = FP8 ? K : (K >> 1);  // weight bytes per feature row
-    const rsrc_t rw = make_rsrc(wts + (size_t)feat0 * wrow, (uint32_t)frows * (uint32_t)wrow);
-    const rsrc_t ra = make_rsrc(act + (size_t)row0 * K, (uint32_t)nrows * (uint32_t)K * 2u);
-    const int vw = (fw * 16 + j) * wrow + (FP8 ? 32 : 16) * g;
-    const int wstep = FP8 ? 128 : 64;  // weight bytes per row per step
+    uint8_t *act_lds = lds;
+    uint16_t *sc_lds = reinterpret_cast<uint16_t *>(lds + (size_t)chunk * kActStepBytes);
+    const int scrow = 4 * chunk;  // staged scales per feature
 
-    // Activation pieces this lane stages: piece c = fw * 64 + lane + FG * 64 * a
-    // of its K-group's tile; row c / 16, 16-byte piece c % 16 of that row.
-    int va[AP], ar[AP], ap[AP];
+    // ---- weights of this wave's T tiles; rows past M read as zeros
+    const int wfeat = max(0, min(M - fwv, T * 16));
+    const rsrc_t rw = make_rsrc(a.w + (size_t)min(fwv, M) * wrow, (uint32_t)wfeat * (uint32_t)wrow);
+    const int vw = j * wrow + (FP8 ? 32 : 16) * g;
+    const float *tsrow[T];
+    if constexpr (FP8) {
 #pragma unroll
-    for (int a = 0; a < AP; ++a) {
-        const int c = fw * 64 + lane + FG * 64 * a;
-        ar[a] = c >> 4;
-        ap[a] = c & 15;
-        va[a] = ar[a] * K * 2 + 16 * ap[a];
+        for (int t = 0; t < T; ++t)
+            tsrow[t] = static_cast<const float *>(a.scales) + (size_t)(min(fwv + 16 * t, M - 1) >> 7) * steps + s0;
     }
-    auto tile_ptr = [&](int buf) { return lds + (size_t)(kg * NBUF + buf) * kActTileBytes; };
 
-    const uint16_t *sc_lds = reinterpret_cast<const uint16_t *>(lds + (size_t)KW * NBUF * kActTileBytes);
-    const uint16_t *my_sc = sc_lds + (fw * 16 + j) * NB;
-    const float *tsrow = nullptr;
-    if constexpr (FP8)
-        tsrow = static_cast<const float *>(scales) + (size_t)(min(feat0 + fw * 16, M - 1) >> 7) * S;
-
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-
-    // ---- register pipeline: PF steps of weights and activation pieces in flight
-    WStage<FP8> ws[PF];
-    u32x4 ax[PF][AP];
-    auto issue = [&](auto U, int i) {
-        const int s = step_of(i);
-        if constexpr (FP8) {
-            ws[U.value].w0 = bload16<kAuxCached>(rw, vw, wstep * s);
-            ws[U.value].w1 = bload16<kAuxCached>(rw, vw + 16, wstep * s);
-        } else {
-            ws[U.value].c = bload16<kAuxCached>(rw, vw, wstep * s);
+    u32x4 wb[PF][T][WB];
+    float tsb[PF][T];
+    // The step offset goes into the per-lane offset, which the buffer range
+    // check covers: the partial last Q4_0 step of the last row then reads zeros
+    // instead of bytes past the end of the array.
+    auto issue = [&](auto U, int st) {
+        const int koff = vw + kStepBytes * (s0 + st);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+#pragma unroll
+            for (int h = 0; h < WB; ++h)
+                wb[U.value][t][h] = bload16<kAuxCached>(rw, koff + t * 16 * wrow + 16 * h, 0);
+            if constexpr (FP8)
+                tsb[U.value][t] = tsrow[t][st];
         }
-#pragma unroll
-        for (int a = 0; a < AP; ++a)
-            ax[U.value][a] = bload16<kAuxCached>(ra, va[a], 256 * s);
     };
-    auto stage_act = [&](auto U, int buf) {
-        uint8_t *tp = tile_ptr(buf);
+
+    // ---- staging of one chunk of the slice: activations (and Q4_0 scales).
+    // Loads and LDS stores are separate steps so that the loads can be issued
+    // before the first weight loads: the wait for them then leaves the weight
+    // loads in flight.  Every load is issued (out-of-range ones read zeros),
+    // which keeps the compiler's wait counts exact.
+    constexpr int LR = NT / 16;                        // threads per activation row
+    constexpr int APT = (16 * CH + LR - 1) / LR;       // 16-byte pieces per thread
+    constexpr int SPT = FP8 ? 1 : (TG * 16 * 8 + NT - 1) / NT;  // scale loads per thread
+    const rsrc_t ra = make_rsrc(a.act, (uint32_t)nrows * (uint32_t)K * 2u);
+    const int wgfeat = max(0, min(M - fwg, TG * 16));
+    const uint8_t *sbase = FP8 ? nullptr : static_cast<const uint8_t *>(a.scales) + (size_t)min(fwg, M) * NB * 2;
+    const rsrc_t rs = make_rsrc(sbase, FP8 ? 0u : (uint32_t)wgfeat * (uint32_t)NB * 2u);
+    const int ar = threadIdx.x / LR;  // activation row staged by this thread
+    const int alt = threadIdx.x % LR;
+    u32x4 sa[APT];
+    u32x2 ss[SPT];
+    auto stage_load = [&](int c0, int nc) {
+        // row ar: consecutive 16-byte pieces (whole cache lines) of the row's
+        // nc * 256 contiguous bytes; pieces past K are zeros, rows past N read
+        // as zeros
+        const int kb = (s0 + c0) * kStepK;
 #pragma unroll
-        for (int a = 0; a < AP; ++a)
-            act_piece_to_lds<FP8>(tp, ar[a], ap[a], ax[U.value][a]);
-    };
-    // One iteration: read this step's operands from LDS, stage the next step's
-    // activations, then the math (the reads come first: with one buffer the
-    // next step overwrites the tile).  FULL: a whole step of K inside this
-    // K-group's range, no runtime checks at all.
-    auto iterate = [&](auto U, int it, bool stage_next, auto Full) {
-        constexpr bool FULL = decltype(Full)::value;
-        constexpr int NEXT = (decltype(U)::value + 1) % PF;
-        const int s = step_of(it);
-        const uint8_t *tp = tile_ptr(it % NBUF);
-        u32x4 a[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            a[q] = *reinterpret_cast<const u32x4 *>(tp + (q * 64 + lane) * 16);
-        uint32_t sc[4] = {0u, 0u, 0u, 0u};
-        int nblk = 4;
+        for (int i = 0; i < APT; ++i) {
+            const int p = alt + LR * i;
+            const bool ok = p < 16 * nc && kb + 8 * p < K;
+            sa[i] = bload16<kAuxCached>(ra, ok ? ar * K * 2 + 2 * kb + 16 * p : kOut, 0);
+        }
         if constexpr (!FP8) {
-            if constexpr (!FULL)
-                nblk = it < n_mine ? min(4, NB - 4 * s) : 0;
-            if (FULL || nblk == 4) {
-                if constexpr (SVEC) {
-                    const u32x2 p = *reinterpret_cast<const u32x2 *>(my_sc + 4 * s);
-                    sc[0] = p[0] & 0xFFFFu; sc[1] = p[0] >> 16; sc[2] = p[1] & 0xFFFFu; sc[3] = p[1] >> 16;
+            // scales: 8 threads per feature row, one step (4 blocks) each
+            const bool vec = (NB & 3) == 0;
+#pragma unroll
+            for (int i = 0; i < SPT; ++i) {
+                const int e = threadIdx.x + NT * i;
+                const int fi = e >> 3, st = e & 7;
+                const int blk = 4 * (s0 + c0 + st);
+                const bool ok = st < nc && fi < TG * 16;
+                const int off = (fi * NB + blk) * 2;
+                if (vec) {
+                    ss[i] = bload8<kAuxCached>(rs, ok ? off : kOut, 0);
                 } else {
+                    uint32_t h[4];
 #pragma unroll
-                    for (int tb = 0; tb < 4; ++tb)
-                        sc[tb] = my_sc[4 * s + tb];
+                    for (int b = 0; b < 4; ++b)
+                        h[b] = bload2<kAuxCached>(rs, ok && blk + b < NB ? off + 2 * b : kOut, 0);
+                    ss[i] = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
                 }
-            } else {
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-                    sc[tb] = tb < nblk ? (uint32_t)my_sc[4 * s + tb] : 0u;
             }
         }
-        if (stage_next)
-            stage_act(std::integral_constant<int, NEXT>{}, (it + 1) % NBUF);
-        if constexpr (FULL) {
-            if constexpr (FP8)
-                fp8_step<ACT>(ws[U.value], a, tsrow[s], acc);
-            else
-                q4_step<ACT, true>(ws[U.value].c, a, sc, 4, acc);
-        } else if (it < n_mine) {
-            if constexpr (FP8)
-                fp8_step<ACT>(ws[U.value], a, tsrow[s], acc);
-            else if (nblk == 4)
-                q4_step<ACT, true>(ws[U.value].c, a, sc, 4, acc);
-            else
-                q4_step<ACT, false>(ws[U.value].c, a, sc, nblk, acc);
+    };
+    auto stage_store = [&](int nc) {
+#pragma unroll
+        for (int i = 0; i < APT; ++i) {
+            const int p = alt + LR * i;
+            if (p < 16 * nc)
+                act_piece_to_lds<FP8>(act_lds + (p >> 4) * kActStepBytes, ar, p & 15, sa[i]);
+        }
+        if constexpr (!FP8) {
+#pragma unroll
+            for (int i = 0; i < SPT; ++i) {
+                const int e = threadIdx.x + NT * i;
+                const int fi = e >> 3, st = e & 7;
+                if (st < nc && fi < TG * 16)
+                    *reinterpret_cast<u32x2 *>(sc_lds + fi * scrow + 4 * st) = ss[i];
+            }
         }
     };
-    using Full = std::true_type;
-    using Guarded = std::false_type;
 
-    // ---- prologue: first PF steps in flight, then the scales, then tile 0
-    const bool steady = n_iter - 1 >= 2 * PF;
-    if (steady) {
+    // ---- the math of one step (st counted from the slice start, c0 = its chunk's start)
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](auto U, int st, int c0) {
+        const uint8_t *tp = act_lds + (st - c0) * kActStepBytes;
+        u32x4 av[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            av[q] = *reinterpret_cast<const u32x4 *>(tp + (q * 64 + lane) * 16);
+        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (FP8) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                f32x4 part = zero4;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const u32x4 src = wb[U.value][t][u >> 1];
+                    const uint32_t e0 = src[2 * (u & 1)], e1 = src[2 * (u & 1) + 1];
+                    const u32x4 bop = {A16::template fp8x2<false>(e0), A16::template fp8x2<true>(e0),
+                                       A16::template fp8x2<false>(e1), A16::template fp8x2<true>(e1)};
+                    part = A16::mfma(av[u], bop, part);
+                }
+                const float ts = tsb[U.value][t];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[t][r] = __builtin_fmaf(ts, part[r], acc[t][r]);
+            }
+        } else {
+            const u32x4 negc = {A16::kNegOffset, A16::kNegOffset, A16::kNegOffset, A16::kNegOffset};
+            f32x4 corr[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                corr[q] = A16::mfma(av[q], negc, zero4);  // -(MAGIC + 8) * sum x, per row
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const u32x2 scp =
+                    *reinterpret_cast<const u32x2 *>(sc_lds + ((wave * T + t) * 16 + j) * scrow + 4 * (st - c0));
+                uint32_t d[4] = {wb[U.value][t][0][0], wb[U.value][t][0][1], wb[U.value][t][0][2],
+                                 wb[U.value][t][0][3]};
+                transpose_lane_groups(d[0], d[1], d[2], d[3]);  // lane group g: dword g of blocks 0..3
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 dot = A16::mfma(av[q], q4_operand<A16::kMagicByte>(d[q]), corr[q]);
+                    const float s = h2f((q & 1) ? (scp[q >> 1] >> 16) : (scp[q >> 1] & 0xFFFFu));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[t][r] = __builtin_fmaf(s, dot[r], acc[t][r]);
+                }
+            }
+        }
+    };
+
+    // ---- prologue: staging loads of the first chunk, the first PF steps of
+    // weights, then the staged chunk into LDS
+    const int nc0 = min(chunk, ns);
+    stage_load(0, nc0);
+    if (ns >= PF) {
         static_for<PF>([&](auto U) { issue(U, U.value); });
     } else {
         static_for<PF>([&](auto U) {
-            if (U.value < n_iter)
+            if (U.value < ns)
                 issue(U, U.value);
         });
     }
-    if constexpr (!FP8) {
-        // the workgroup's scale rows are contiguous in memory
-        const uint32_t sbytes = (uint32_t)frows * (uint32_t)NB * 2u;
-        const rsrc_t rs = make_rsrc(static_cast<const uint16_t *>(scales) + (size_t)feat0 * NB, sbytes);
-        uint8_t *dst = lds + (size_t)KW * NBUF * kActTileBytes;
-        // whole 16-byte chunks, then the remainder one scale at a time: the
-        // buffer range check works per dword, so a load ending mid-dword past
-        // the resource would read that dword as 0
-        const uint32_t full = sbytes & ~15u;
-        for (uint32_t o = threadIdx.x * 16u; o < full; o += 64u * NW * 16u)
-            *reinterpret_cast<u32x4 *>(dst + o) = bload16<kAuxCached>(rs, (int)o, 0);
-        for (uint32_t o = full + threadIdx.x * 2u; o < sbytes; o += 64u * NW * 2u)
-            *reinterpret_cast<uint16_t *>(dst + o) = (uint16_t)bload2<kAuxCached>(rs, (int)o, 0);
-    }
-    if (n_iter > 0)
-        stage_act(std::integral_constant<int, 0>{}, 0);
+    stage_store(nc0);
     __syncthreads();
 
-    // ---- steady state: loads issued unconditionally, so the compiler counts
-    // them and waits only for the slot it is about to use
-    int i = 0;
-    if (steady) {
-        do {
+    // ---- chunks of the slice; weight loads run PF steps ahead across chunks
+    for (int c0 = 0; c0 < ns; c0 += chunk) {
+        const int c1 = min(ns, c0 + chunk);
+        if (c0 > 0) {
+            __syncthreads();
+            stage_load(c0, c1 - c0);
+            stage_store(c1 - c0);
+            __syncthreads();
+        }
+        int i = c0;
+        // steady state: every load unconditional, so the compiler counts them
+        // and waits only for the stage it is about to use
+        while (i + 2 * PF <= c1) {
             static_for<PF>([&](auto U) {
-                const int it = i + U.value;
-                iterate(U, it, true, Full{});
+                compute(U, i + U.value, c0);
                 __builtin_amdgcn_sched_barrier(0);
-                issue(U, it + PF);
+                issue(U, i + U.value + PF);
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (SHARED)
-                    __syncthreads();
             });
             i += PF;
-        } while (i + 2 * PF <= n_iter - 1);
-    }
-    // ---- tail: the last n_iter - i (<= 2 PF) iterations
-    static_for<2 * PF + 1>([&](auto V) {
-        constexpr int U = V.value % PF;
-        const int it = i + V.value;
-        if (it < n_iter) {
-            iterate(std::integral_constant<int, U>{}, it, it + 1 < n_iter, Guarded{});
-            if (it + PF < n_iter)
-                issue(std::integral_constant<int, U>{}, it + PF);
         }
-        if constexpr (SHARED)
-            __syncthreads();
-    });
-    if constexpr (!SHARED)
-        __syncthreads();
+        static_for<2 * PF>([&](auto V) {
+            constexpr int U = V.value % PF;
+            const int st = i + V.value;
+            if (st < c1) {
+                compute(std::integral_constant<int, U>{}, st, c0);
+                if (st + PF < ns)
+                    issue(std::integral_constant<int, U>{}, st + PF);
+            }
+        });
+    }
 
-    // ---- combine the K-groups in fixed order, scale, round, store
-    float *red = reinterpret_cast<float *>(lds);  // reuses the activation tiles
+    // ---- epilogue
+    auto store_tile = [&](int t, f32x4 v) {
+        const int feat = fwv + t * 16 + j;
+        if (feat < M) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-        red[((kg * FG + fw) * 4 + r) * 64 + lane] = acc[r];
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * g + r;
+                if (row < nrows)
+                    store_out(a.out, grp.out_dtype, (size_t)row * M + feat, grp.alpha * v[r]);
+            }
+        }
+    };
+    if (S == 1) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            store_tile(t, acc[t]);
+        return;
+    }
+    // Split K: publish this slice's partial tiles, count in, and let the last
+    // workgroup of the tile group add the slices in order.  The partial tiles
+    // are written and read with agent-coherent (sc1) accesses, which go
+    // through to memory rather than stopping in one die's L2, so no cache
+    // writeback or invalidation is needed; the wait before the barrier makes
+    // every store complete before the count is taken.
+    constexpr int kCoherent = 0x10;  // sc1
+    const int ntg = verify_tile_groups_dev(M, TG);
+    const rsrc_t rp = make_rsrc(a.part, (uint32_t)ntg * (uint32_t)S * TG * 1024u);
+    const int mine = ((tg * S + sidx) * TG + wave * T) * 1024 + lane * 16;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[t]), rp, mine + t * 1024, 0, kCoherent);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int o = threadIdx.x; o < FG * 4 * 64; o += NW * 64) {
-        float s = red[o];
+    int *flag = reinterpret_cast<int *>(lds);  // the activation tiles are no longer read
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(a.cnt + tg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == (uint32_t)(S - 1);
+        if (last)  // every slice has arrived: leave the counter at zero for the next call
+            __hip_atomic_store(a.cnt + tg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last;
+    }
+    __syncthreads();
+    if (*flag == 0)
+        return;
+    const int base = (tg * S * TG + wave * T) * 1024 + lane * 16;
 #pragma unroll
-        for (int w = 1; w < KW; ++w)
-            s += red[w * FG * 4 * 64 + o];
-        const int ln = o & 63, r = (o >> 6) & 3, f = o >> 8;
-        const int feat = feat0 + f * 16 + (ln & 15);
-        const int row = 4 * (ln >> 4) + r;
-        if (row < nrows && feat < M)
-            store_out(out, out_dtype, (size_t)(row0 + row) * M + feat, alpha * s);
+    for (int t = 0; t < T; ++t) {
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+        for (int s8 = 0; s8 < S; s8 += 8) {
+            f32x4 v[8];  // eight slices' loads in flight at once
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rp, s8 + u < S ? base + (s8 + u) * TG * 1024 + t * 1024 : kOut, 0,
+                                                     kCoherent));
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int s2 = s8 + u;
+                if (s2 < S) {
+                    const f32x4 w = s2 == sidx ? acc[t] : v[u];
+                    sum = s2 == 0 ? w : sum + w;
+                }
+            }
+        }
+        store_tile(t, sum);
     }
 }
 
@@ -342,87 +415,135 @@ __global__ __launch_bounds__(64 * FG * KW) void verify_kernel(
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr int kMaxGridY = 65535;
-
-template <bool FP8, int FG>
-constexpr int pipeline_depth() {
-    return FP8 ? (FG == 1 ? 3 : 4) : (FG == 1 ? 4 : 6);
-}
-
-template <int ACT, bool FP8, int FG, int KW>
-hipError_t launch_one(const VerifyArgs &p) {
-    constexpr int PF = pipeline_depth<FP8, FG>();
-    const int tiles = (p.M + 15) / 16;
-    const int gx = (tiles + FG - 1) / FG;
-    const int groups = (p.N + 15) / 16;
-    const size_t shm = verify_lds_bytes(FP8, FG, KW, p.K);
-    auto kern = (FP8 || (p.K / 32) % 4 == 0) ? verify_kernel<ACT, FP8, FG, KW, PF, true>
-                                              : verify_kernel<ACT, FP8, FG, KW, PF, false>;
+template <int ACT, bool FP8, int T, int W>
+hipError_t launch_tw(const VerifyLaunch &l) {
+    constexpr int PF = pipeline_depth(FP8, T);
+    auto kern = verify_kernel<ACT, FP8, T, W, PF>;
+    size_t shm = 0;
+    for (int i = 0; i < l.count; ++i)
+        shm = std::max(shm, verify_lds_bytes(FP8, T, W, l.probs[i].plan.chunk));
     if (shm > 64 * 1024 &&
         hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)shm) != hipSuccess)
         return hipErrorInvalidValue;
-    for (int g0 = 0; g0 < groups; g0 += kMaxGridY) {
-        const int gy = std::min(kMaxGridY, groups - g0);
-        const uint16_t *act = reinterpret_cast<const uint16_t *>(p.act) + (size_t)g0 * 16 * p.K;
-        void *out = static_cast<char *>(p.out) + (size_t)g0 * 16 * p.M * out_elem_bytes(p.out_dtype);
-        const int n = std::min(p.N - g0 * 16, gy * 16);
-        hipLaunchKernelGGL(kern, dim3(gx, gy), dim3(64 * FG * KW), shm, p.stream,
-                           reinterpret_cast<const uint8_t *>(p.w), p.scales, act, out, p.out_dtype, n, p.M, p.K,
-                           p.alpha);
+    KGroup grp{};
+    grp.count = l.count;
+    grp.out_dtype = l.out_dtype;
+    grp.alpha = l.alpha;
+    int items = 0;
+    size_t cnt_off = 0, part_off = verify_counter_bytes();
+    for (int i = 0; i < l.count; ++i) {
+        const VerifyProblem &q = l.probs[i];
+        KProblem &k = grp.p[i];
+        const int ntg = verify_tile_groups(q.M, T * W);
+        k.w = static_cast<const uint8_t *>(q.w);
+        k.scales = q.scales;
+        k.M = q.M;
+        k.K = q.K;
+        k.S = q.plan.slices;
+        k.sl = q.plan.sl;
+        k.chunk = q.plan.chunk;
+        k.item0 = items;
+        items += ntg * q.plan.slices;
+        if (q.plan.slices > 1) {
+            k.cnt = reinterpret_cast<uint32_t *>(static_cast<char *>(l.workspace) + cnt_off);
+            k.part = reinterpret_cast<float *>(static_cast<char *>(l.workspace) + part_off);
+            cnt_off += (size_t)ntg * 4;
+            part_off += verify_partial_bytes(q.plan, q.M);
+        }
+    }
+    // Row groups of 16 run one after another: they share the workspace and
+    // are independent otherwise.
+    const int groups = (l.N + 15) / 16;
+    for (int g0 = 0; g0 < groups; ++g0) {
+        grp.N = std::min(16, l.N - g0 * 16);
+        for (int i = 0; i < l.count; ++i) {
+            const VerifyProblem &q = l.probs[i];
+            grp.p[i].act = static_cast<const uint16_t *>(q.act) + (size_t)g0 * 16 * q.K;
+            grp.p[i].out = static_cast<char *>(q.out) + (size_t)g0 * 16 * q.M * out_elem_bytes(l.out_dtype);
+        }
+        hipLaunchKernelGGL(kern, dim3(items), dim3(64 * W), shm, l.stream, grp);
     }
     return hipGetLastError();
 }
 
-template <int ACT, bool FP8, int FG>
-hipError_t dispatch_kw(const VerifyArgs &p) {
-    switch (p.waves_k) {
-    case 1: return launch_one<ACT, FP8, FG, 1>(p);
-    case 2: return launch_one<ACT, FP8, FG, 2>(p);
-    case 4: return launch_one<ACT, FP8, FG, 4>(p);
-    case 8:
-        if constexpr (FG <= 2)
-            return launch_one<ACT, FP8, FG, 8>(p);
-        return hipErrorInvalidValue;
-    case 16:
-        if constexpr (FG == 1)
-            return launch_one<ACT, FP8, FG, 16>(p);
-        return hipErrorInvalidValue;
+template <int ACT, bool FP8, int T>
+hipError_t dispatch_w(const VerifyLaunch &l) {
+    switch (l.waves) {
+    case 2: return launch_tw<ACT, FP8, T, 2>(l);
+    case 4: return launch_tw<ACT, FP8, T, 4>(l);
+    case 8: return launch_tw<ACT, FP8, T, 8>(l);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int ACT, bool FP8>
-hipError_t dispatch_fg(const VerifyArgs &p) {
-    switch (p.tiles_per_wg) {
-    case 1: return dispatch_kw<ACT, FP8, 1>(p);
-    case 2: return dispatch_kw<ACT, FP8, 2>(p);
-    case 4: return dispatch_kw<ACT, FP8, 4>(p);
+hipError_t dispatch_t(const VerifyLaunch &l) {
+    switch (l.tiles) {
+    case 1: return dispatch_w<ACT, FP8, 1>(l);
+    case 2: return dispatch_w<ACT, FP8, 2>(l);
+    case 4: return dispatch_w<ACT, FP8, 4>(l);
     default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-size_t verify_lds_bytes(bool fp8, int fg, int kw, int K) {
-    const size_t nbuf = fg > 1 ? 2 : 1;
-    const size_t act_b = (size_t)kw * nbuf * kActTileBytes;
-    const size_t sc_b = fp8 ? 0 : ((((size_t)fg * 16 * (K / 32) * 2) + 15) & ~(size_t)15);
-    return act_b + sc_b;  // the final reduction (kw * fg KB) fits in act_b
+int verify_steps(bool fp8, int K) { return fp8 ? K / 128 : (K / 32 + 3) / 4; }
+
+int verify_tile_groups(int M, int tiles_per_group) { return verify_tile_groups_dev(M, tiles_per_group); }
+
+int pipeline_depth_of(bool fp8, int tiles) { return pipeline_depth(fp8, tiles); }
+
+int verify_max_chunk(int waves) { return max_chunk_steps(waves); }
+
+size_t verify_counter_bytes() { return (size_t)kMaxSplitTileGroups * 4; }
+
+size_t verify_lds_bytes(bool fp8, int tiles, int waves, int chunk) {
+    const size_t act_b = (size_t)chunk * kActStepBytes;
+    const size_t sc_b = fp8 ? 0 : (size_t)tiles * waves * 16 * 4 * chunk * 2;
+    return act_b + sc_b;
 }
 
-bool verify_shape_ok(bool fp8, int fg, int kw, int K) {
-    if (!(fg == 1 || fg == 2 || fg == 4) || !(kw == 1 || kw == 2 || kw == 4 || kw == 8 || kw == 16))
-        return false;
-    if (fg * kw > 16)
-        return false;
-    return verify_lds_bytes(fp8, fg, kw, K) <= kMaxLdsBytes;
+size_t verify_partial_bytes(const VerifyPlan &pl, int M) {
+    if (pl.slices <= 1)
+        return 0;
+    return (size_t)verify_tile_groups(M, pl.tiles * pl.waves) * pl.slices * pl.tiles * pl.waves * 1024;
 }
 
-hipError_t launch_verify(const VerifyArgs &p, bool fp8) {
-    if (p.act_dtype == VQ_DTYPE_BF16)
-        return fp8 ? dispatch_fg<VQ_DTYPE_BF16, true>(p) : dispatch_fg<VQ_DTYPE_BF16, false>(p);
-    return fp8 ? dispatch_fg<VQ_DTYPE_F16, true>(p) : dispatch_fg<VQ_DTYPE_F16, false>(p);
+size_t verify_workspace_bytes(const VerifyPlan &pl, int M) {
+    const size_t part = verify_partial_bytes(pl, M);
+    return part ? verify_counter_bytes() + part : 0;
+}
+
+// Completes and checks a plan whose tiles, waves and requested slices are
+// set: tiles in {1, 2, 4}, waves in {2, 4, 8}, 1 <= slices <= steps, and a
+// split only with at most kMaxSplitTileGroups tile groups and partial tiles
+// addressable in 32 bits.  The slice count becomes the number of non-empty
+// slices of ceil(steps / slices) steps; the LDS chunk is the slice rounded up
+// to whole pipeline rounds, capped by the staging bound.
+bool verify_plan_finish(bool fp8, int M, int K, VerifyPlan &pl) {
+    if (!(pl.tiles == 1 || pl.tiles == 2 || pl.tiles == 4) || !(pl.waves == 2 || pl.waves == 4 || pl.waves == 8))
+        return false;
+    const int steps = verify_steps(fp8, K);
+    if (pl.slices < 1 || pl.slices > steps)
+        return false;
+    pl.sl = (steps + pl.slices - 1) / pl.slices;
+    pl.slices = (steps + pl.sl - 1) / pl.sl;
+    if (pl.slices > 1 && (verify_tile_groups(M, pl.tiles * pl.waves) > kMaxSplitTileGroups ||
+                          verify_partial_bytes(pl, M) >= ((size_t)1 << 31)))
+        return false;
+    const int pf = pipeline_depth(fp8, pl.tiles);
+    pl.chunk = std::min(max_chunk_steps(pl.waves), (pl.sl + pf - 1) / pf * pf);
+    return verify_lds_bytes(fp8, pl.tiles, pl.waves, pl.chunk) <= kMaxLdsBytes;
+}
+
+hipError_t launch_verify(const VerifyLaunch &l) {
+    if (l.count < 1 || l.count > kGroupPerLaunch)
+        return hipErrorInvalidValue;
+    if (l.act_dtype == VQ_DTYPE_BF16)
+        return l.fp8 ? dispatch_t<VQ_DTYPE_BF16, true>(l) : dispatch_t<VQ_DTYPE_BF16, false>(l);
+    return l.fp8 ? dispatch_t<VQ_DTYPE_F16, true>(l) : dispatch_t<VQ_DTYPE_F16, false>(l);
 }
 
 }  // namespace vq

@@ -1,15 +1,17 @@
 // vq_api.cpp -- the C ABI: argument validation, launch-shape choice, dispatch.
 //
 // Every argument is checked before the first HIP call; on any error nothing is
-// enqueued.  The launch shape of a verify GEMM is a function of (M, K) only,
-// never of N, so an output row is computed by the same instruction sequence
-// whatever the draft-block width ("Qwen3.8-27B on the AMD R9700: up to 227
+// enqueued.  The launch shape of a verify GEMM is a function of (M, K) and the
+// workspace capacity only, never of N, so an output row is computed by the
+// same instruction sequence whatever the draft-block width ("Qwen3.8-27B on the AMD R9700: up to 227
 // tok/s", section "What 'lossless' means here, precisely": outputs compared
 // byte for byte across widths 8, 12 and 16).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "vq.h"
 #include "vq_internal.h"
@@ -44,56 +46,155 @@ bool float_act(int d) { return d == VQ_DTYPE_F16 || d == VQ_DTYPE_BF16; }
 bool out_ok(int d) { return d == VQ_DTYPE_F16 || d == VQ_DTYPE_BF16 || d == VQ_DTYPE_F32; }
 bool dim_ok(int64_t v) { return v >= 1 && v <= VQ_MAX_DIM; }
 
-// Default launch shape for an (M, K) verify GEMM: FG feature tiles per
-// workgroup share each staged activation tile (activation traffic per weight
-// byte falls by FG) while keeping about one workgroup per CU or more on the
-// 256-CU part; then KW K-groups per workgroup for ~2-2.5k waves in flight,
-// keeping at least 4 steps of 128 k per K-group.  A function of (M, K) only.
-constexpr int64_t kMinWorkgroups = 240;
-constexpr int64_t kTargetWaves = 2600;
-
-void default_shape(bool fp8, int64_t m, int64_t k, int *fg_out, int *kw_out) {
-    const int64_t tiles = (m + 15) / 16;
-    const int64_t steps = fp8 ? k / 128 : (k / 32 + 3) / 4;
-    int fg = 1;
-    if ((tiles + 3) / 4 >= kMinWorkgroups)
-        fg = 4;
-    else if ((tiles + 1) / 2 >= kMinWorkgroups)
-        fg = 2;
-    const int64_t wgs = (tiles + fg - 1) / fg;
-    int kw = 1;
-    while (fg * kw * 2 <= 16 && wgs * fg * kw * 2 <= kTargetWaves && (steps + kw * 2 - 1) / (kw * 2) >= 4 &&
-           vq::verify_shape_ok(fp8, fg, kw * 2, (int)k))
-        kw *= 2;
-    *fg_out = fg;
-    *kw_out = kw;
+// Default launch shape for an (M, K) verify GEMM: workgroups of four waves,
+// each wave with two 16-feature tiles, so a workgroup stages each activation
+// element once for 8 tiles; K cut into slices of at most one LDS chunk (8
+// steps of 128).  Every workgroup then streams the same number of weight bytes
+// (8 tiles x up to 8 steps), whatever the matrix, which is what lets a launch
+// over several matrices balance.  Small M uses fewer tiles per group.  Without
+// room for the workspace, K is not split and workgroups cover 4 tiles.  A
+// function of (M, K, workspace capacity) only, never of N.
+vq::VerifyPlan default_plan(bool fp8, int64_t m, int64_t k, size_t ws_bytes) {
+    vq::VerifyPlan pl;
+    const int tiles = (int)((m + 15) / 16);
+    pl.tiles = tiles >= 8 ? 2 : 1;
+    pl.waves = tiles >= 4 ? 4 : 2;
+    const int steps = vq::verify_steps(fp8, (int)k);
+    const int chunk = vq::verify_max_chunk(pl.waves);
+    pl.slices = (steps + chunk - 1) / chunk;
+    if (vq::verify_plan_finish(fp8, (int)m, (int)k, pl) && vq::verify_workspace_bytes(pl, (int)m) <= ws_bytes)
+        return pl;
+    vq::VerifyPlan fb;
+    fb.tiles = 1;
+    fb.waves = 4;
+    fb.slices = 1;
+    vq::verify_plan_finish(fp8, (int)m, (int)k, fb);
+    return fb;
 }
 
-int run_verify(bool fp8, const void *w, const void *scales, const void *act, int act_dtype,
-               void *out, int out_dtype, int64_t n, int64_t m, int64_t k, float alpha, int tpw,
-               int kw, void *stream) {
+int check_problem(bool fp8, const void *w, const void *scales, const void *act, void *out, int64_t m,
+                  int64_t k) {
     if (!w || !scales || !act || !out)
         return VQ_ERR_NULL_POINTER;
-    if (!float_act(act_dtype) || !out_ok(out_dtype))
-        return VQ_ERR_BAD_DTYPE;
-    if (!dim_ok(n) || !dim_ok(m) || !dim_ok(k) || k % (fp8 ? 128 : 32) != 0)
+    if (!dim_ok(m) || !dim_ok(k) || k % (fp8 ? 128 : 32) != 0)
         return VQ_ERR_BAD_SHAPE;
     if (!aligned16(w) || !aligned16(scales) || !aligned16(act) || !aligned16(out))
         return VQ_ERR_MISALIGNED;
-    int dt = 0, dk = 0;
-    default_shape(fp8, m, k, &dt, &dk);
-    if (tpw == 0)
-        tpw = dt;
-    if (kw == 0)
-        kw = dk;
-    if (!vq::verify_shape_ok(fp8, tpw, kw, (int)k))
-        return VQ_ERR_BAD_CONFIG;
+    return VQ_OK;
+}
+
+// Launches problems[0 .. count) whose plans are finished: consecutive runs
+// with the same tiles and waves share a launch (up to kGroupPerLaunch
+// problems and kMaxSplitTileGroups counters each).  Launches run one after
+// another on the stream, each using the workspace from its start.
+int launch_problems(bool fp8, const vq::VerifyProblem *probs, int count, int act_dtype, int out_dtype,
+                    int n, float alpha, void *workspace, hipStream_t stream, size_t *ws_need) {
+    size_t need = 0;
+    int i = 0;
+    while (i < count) {
+        int e = i;
+        int counters = 0;
+        size_t part = 0;
+        while (e < count && e - i < vq::kGroupPerLaunch && probs[e].plan.tiles == probs[i].plan.tiles &&
+               probs[e].plan.waves == probs[i].plan.waves) {
+            const int c = probs[e].plan.slices > 1
+                              ? vq::verify_tile_groups(probs[e].M, probs[e].plan.tiles * probs[e].plan.waves)
+                              : 0;
+            if (counters + c > vq::kMaxSplitTileGroups)
+                break;
+            counters += c;
+            part += vq::verify_partial_bytes(probs[e].plan, probs[e].M);
+            ++e;
+        }
+        if (part)
+            need = std::max(need, vq::verify_counter_bytes() + part);
+        if (!ws_need) {
+            vq::VerifyLaunch l{fp8, act_dtype, out_dtype, n, alpha, probs[i].plan.tiles, probs[i].plan.waves,
+                               probs + i, e - i, workspace, stream};
+            if (vq::launch_verify(l) != hipSuccess)
+                return VQ_ERR_LAUNCH;
+        }
+        i = e;
+    }
+    if (ws_need)
+        *ws_need = need;
+    return VQ_OK;
+}
+
+int run_verify(bool fp8, const void *w, const void *scales, const void *act, int act_dtype,
+               void *out, int out_dtype, int64_t n, int64_t m, int64_t k, float alpha, int tiles,
+               int waves, int slices, void *workspace, size_t ws_bytes, void *stream) {
+    const int st = check_problem(fp8, w, scales, act, out, m, k);
+    if (st != VQ_OK)
+        return st;
+    if (!float_act(act_dtype) || !out_ok(out_dtype))
+        return VQ_ERR_BAD_DTYPE;
+    if (!dim_ok(n))
+        return VQ_ERR_BAD_SHAPE;
+    if (workspace && !aligned16(workspace))
+        return VQ_ERR_MISALIGNED;
+    if (!workspace)
+        ws_bytes = 0;
+    vq::VerifyPlan pl;
+    if (tiles == 0 && waves == 0 && slices == 0) {
+        pl = default_plan(fp8, m, k, ws_bytes);
+    } else {
+        const vq::VerifyPlan d = default_plan(fp8, m, k, SIZE_MAX);
+        pl.tiles = tiles ? tiles : d.tiles;
+        pl.waves = waves ? waves : d.waves;
+        pl.slices = slices ? slices : d.slices;
+        if (!vq::verify_plan_finish(fp8, (int)m, (int)k, pl))
+            return VQ_ERR_BAD_CONFIG;
+        if (vq::verify_workspace_bytes(pl, (int)m) > ws_bytes)
+            return VQ_ERR_WORKSPACE;
+    }
     const int dev = check_device();
     if (dev != VQ_OK)
         return dev;
-    vq::VerifyArgs p{w, scales, act, out, act_dtype, out_dtype, (int)n, (int)m, (int)k,
-                     alpha, tpw, kw, static_cast<hipStream_t>(stream)};
-    return vq::launch_verify(p, fp8) == hipSuccess ? VQ_OK : VQ_ERR_LAUNCH;
+    const vq::VerifyProblem prob{w, scales, act, out, (int)m, (int)k, pl};
+    return launch_problems(fp8, &prob, 1, act_dtype, out_dtype, (int)n, alpha, workspace,
+                           static_cast<hipStream_t>(stream), nullptr);
+}
+
+// Plans of a grouped call: the default shape of every problem, split when a
+// workspace is given (the call then needs what vq_workspace_bytes_grouped
+// reports), unsplit without one -- the same shapes single calls pick with
+// enough workspace, or with none, so each output matches its single call.
+int plan_group(bool fp8, const vq_verify_problem *problems, int count, bool split, vq::VerifyProblem *out) {
+    for (int i = 0; i < count; ++i) {
+        const vq_verify_problem &p = problems[i];
+        const int st = check_problem(fp8, p.w, p.scales, p.act, p.out, p.m, p.k);
+        if (st != VQ_OK)
+            return st;
+        out[i] = vq::VerifyProblem{p.w, p.scales, p.act, p.out, (int)p.m, (int)p.k,
+                                   default_plan(fp8, p.m, p.k, split ? SIZE_MAX : 0)};
+    }
+    return VQ_OK;
+}
+
+int run_group(bool fp8, const vq_verify_problem *problems, int count, int act_dtype, int out_dtype,
+              int64_t n, float alpha, void *workspace, size_t ws_bytes, void *stream) {
+    if (!problems)
+        return VQ_ERR_NULL_POINTER;
+    if (count < 1 || count > VQ_MAX_GROUP || !dim_ok(n))
+        return VQ_ERR_BAD_SHAPE;
+    if (!float_act(act_dtype) || !out_ok(out_dtype))
+        return VQ_ERR_BAD_DTYPE;
+    if (workspace && !aligned16(workspace))
+        return VQ_ERR_MISALIGNED;
+    std::vector<vq::VerifyProblem> probs(count);
+    int st = plan_group(fp8, problems, count, workspace != nullptr, probs.data());
+    if (st != VQ_OK)
+        return st;
+    size_t need = 0;
+    launch_problems(fp8, probs.data(), count, act_dtype, out_dtype, (int)n, alpha, workspace, nullptr, &need);
+    if (need > (workspace ? ws_bytes : 0))
+        return VQ_ERR_WORKSPACE;
+    st = check_device();
+    if (st != VQ_OK)
+        return st;
+    return launch_problems(fp8, probs.data(), count, act_dtype, out_dtype, (int)n, alpha, workspace,
+                           static_cast<hipStream_t>(stream), nullptr);
 }
 
 }  // namespace
@@ -102,12 +203,12 @@ extern "C" {
 
 int vq_gemm_q4_0(const void *w_codes, const void *w_scales, const void *act, int act_dtype,
                  const void *act_scales, void *out, int out_dtype, int64_t n_rows, int64_t m,
-                 int64_t k, float alpha, void *stream) {
+                 int64_t k, float alpha, void *workspace, size_t workspace_bytes, void *stream) {
     if (act_dtype != VQ_DTYPE_I8) {
         if (act_scales != nullptr)
             return VQ_ERR_BAD_DTYPE;  // float activations carry no scales
         return run_verify(false, w_codes, w_scales, act, act_dtype, out, out_dtype, n_rows, m, k,
-                          alpha, 0, 0, stream);
+                          alpha, 0, 0, 0, workspace, workspace_bytes, stream);
     }
     if (!w_codes || !w_scales || !act || !act_scales || !out)
         return VQ_ERR_NULL_POINTER;
@@ -128,23 +229,30 @@ int vq_gemm_q4_0(const void *w_codes, const void *w_scales, const void *act, int
 
 int vq_gemm_q4_0_ex(const void *w_codes, const void *w_scales, const void *act, int act_dtype,
                     void *out, int out_dtype, int64_t n_rows, int64_t m, int64_t k, float alpha,
-                    int tiles_per_wave, int waves_k, void *stream) {
+                    int tiles_per_wave, int waves_per_group, int k_slices, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    if (tiles_per_wave < 0 || waves_per_group < 0 || k_slices < 0)
+        return VQ_ERR_BAD_CONFIG;
     return run_verify(false, w_codes, w_scales, act, act_dtype, out, out_dtype, n_rows, m, k, alpha,
-                      tiles_per_wave, waves_k, stream);
+                      tiles_per_wave, waves_per_group, k_slices, workspace, workspace_bytes, stream);
 }
 
 int vq_gemm_fp8_blk128(const void *w_e4m3, const float *w_tile_scales, const void *act,
                        int act_dtype, void *out, int out_dtype, int64_t n_rows, int64_t m,
-                       int64_t k, void *stream) {
+                       int64_t k, void *workspace, size_t workspace_bytes, void *stream) {
     return run_verify(true, w_e4m3, w_tile_scales, act, act_dtype, out, out_dtype, n_rows, m, k,
-                      1.0f, 0, 0, stream);
+                      1.0f, 0, 0, 0, workspace, workspace_bytes, stream);
 }
 
 int vq_gemm_fp8_blk128_ex(const void *w_e4m3, const float *w_tile_scales, const void *act,
                           int act_dtype, void *out, int out_dtype, int64_t n_rows, int64_t m,
-                          int64_t k, int tiles_per_wave, int waves_k, void *stream) {
+                          int64_t k, int tiles_per_wave, int waves_per_group, int k_slices,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    if (tiles_per_wave < 0 || waves_per_group < 0 || k_slices < 0)
+        return VQ_ERR_BAD_CONFIG;
     return run_verify(true, w_e4m3, w_tile_scales, act, act_dtype, out, out_dtype, n_rows, m, k,
-                      1.0f, tiles_per_wave, waves_k, stream);
+                      1.0f, tiles_per_wave, waves_per_group, k_slices, workspace, workspace_bytes,
+                      stream);
 }
 
 int vq_hadamard32_quant_int8(const void *x, int x_dtype, int8_t *q_out, void *scales_out,
@@ -166,13 +274,55 @@ int vq_hadamard32_quant_int8(const void *x, int x_dtype, int8_t *q_out, void *sc
                : VQ_ERR_LAUNCH;
 }
 
-int vq_default_launch_shape(int kind, int64_t m, int64_t k, int *tiles_per_wave, int *waves_k) {
-    if (!tiles_per_wave || !waves_k)
+static bool query_ok(int kind, int64_t m, int64_t k) {
+    return (kind == VQ_KIND_Q4_0 || kind == VQ_KIND_FP8_BLK128) && dim_ok(m) && dim_ok(k) &&
+           k % (kind == VQ_KIND_FP8_BLK128 ? 128 : 32) == 0;
+}
+
+size_t vq_workspace_bytes(int kind, int64_t m, int64_t k) {
+    if (!query_ok(kind, m, k))
+        return 0;
+    const bool fp8 = kind == VQ_KIND_FP8_BLK128;
+    return vq::verify_workspace_bytes(default_plan(fp8, m, k, SIZE_MAX), (int)m);
+}
+
+int vq_default_launch_shape(int kind, int64_t m, int64_t k, size_t workspace_bytes, int *tiles_per_wave,
+                            int *waves_per_group, int *k_slices, size_t *workspace_used) {
+    if (!tiles_per_wave || !waves_per_group || !k_slices || !workspace_used)
         return VQ_ERR_NULL_POINTER;
-    if ((kind != 0 && kind != 1) || !dim_ok(m) || !dim_ok(k))
+    if (!query_ok(kind, m, k))
         return VQ_ERR_BAD_SHAPE;
-    default_shape(kind == 1, m, k, tiles_per_wave, waves_k);
+    const bool fp8 = kind == VQ_KIND_FP8_BLK128;
+    const vq::VerifyPlan pl = default_plan(fp8, m, k, workspace_bytes);
+    *tiles_per_wave = pl.tiles;
+    *waves_per_group = pl.waves;
+    *k_slices = pl.slices;
+    *workspace_used = vq::verify_workspace_bytes(pl, (int)m);
     return VQ_OK;
+}
+
+int vq_gemm_q4_0_grouped(const vq_verify_problem *problems, int count, int act_dtype, int out_dtype,
+                         int64_t n_rows, float alpha, void *workspace, size_t workspace_bytes, void *stream) {
+    return run_group(false, problems, count, act_dtype, out_dtype, n_rows, alpha, workspace, workspace_bytes,
+                     stream);
+}
+
+int vq_gemm_fp8_blk128_grouped(const vq_verify_problem *problems, int count, int act_dtype, int out_dtype,
+                               int64_t n_rows, void *workspace, size_t workspace_bytes, void *stream) {
+    return run_group(true, problems, count, act_dtype, out_dtype, n_rows, 1.0f, workspace, workspace_bytes,
+                     stream);
+}
+
+size_t vq_workspace_bytes_grouped(int kind, const vq_verify_problem *problems, int count) {
+    if ((kind != VQ_KIND_Q4_0 && kind != VQ_KIND_FP8_BLK128) || !problems || count < 1 || count > VQ_MAX_GROUP)
+        return 0;
+    const bool fp8 = kind == VQ_KIND_FP8_BLK128;
+    std::vector<vq::VerifyProblem> probs(count);
+    if (plan_group(fp8, problems, count, true, probs.data()) != VQ_OK)
+        return 0;
+    size_t need = 0;
+    launch_problems(fp8, probs.data(), count, VQ_DTYPE_BF16, VQ_DTYPE_BF16, 1, 1.0f, nullptr, nullptr, &need);
+    return need;
 }
 
 const char *vq_status_string(int status) {
@@ -185,10 +335,11 @@ const char *vq_status_string(int status) {
     case VQ_ERR_DEVICE: return "current HIP device is not gfx950 (or no device)";
     case VQ_ERR_LAUNCH: return "HIP kernel launch failed";
     case VQ_ERR_BAD_CONFIG: return "unsupported explicit launch shape";
+    case VQ_ERR_WORKSPACE: return "workspace too small for the explicit launch shape";
     default: return "unknown status";
     }
 }
 
-int vq_version(void) { return 100; }
+int vq_version(void) { return 200; }
 
 }  // extern "C"

@@ -111,9 +111,18 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kAuxStream = 2;  // nt
 constexpr int kAuxCached = 0;
 
+// The base and size must be wave-uniform: they are moved to scalar registers
+// here, because a descriptor the compiler cannot prove uniform (say, a size
+// computed with a vector min/max) would otherwise turn every load through it
+// into a loop over the distinct descriptors of the wave.
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
     // word 3 = 0x00020000: raw (untyped) dword data format for the gfx9 family
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, 0x00020000);
 }
 template <int AUX>
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, int voff, int soff) {

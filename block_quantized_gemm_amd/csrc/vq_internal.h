@@ -10,17 +10,36 @@
 
 namespace vq {
 
-// Arguments of one verify GEMM launch, already validated.
-struct VerifyArgs {
+// Launch shape of a verify GEMM: `tiles` 16-feature tiles per wave, `waves`
+// waves per workgroup, K cut into `slices` slices of `sl` steps of 128, staged
+// through LDS `chunk` steps at a time.
+struct VerifyPlan {
+    int tiles = 0, waves = 0, slices = 0;
+    int sl = 0, chunk = 0;
+};
+
+// One verify GEMM of a launch, already validated.
+struct VerifyProblem {
     const void *w;       // Q4_0 codes or E4M3 bytes
     const void *scales;  // Q4_0 fp16 block scales or FP8 fp32 tile scales
     const void *act;     // [N][K] 16-bit activations
     void *out;           // [N][M]
+    int M, K;
+    VerifyPlan plan;     // finished; every problem of a launch has the same tiles and waves
+};
+
+// Problems per kernel launch (they travel in the kernel arguments).
+constexpr int kGroupPerLaunch = 32;
+
+struct VerifyLaunch {
+    bool fp8;
     int act_dtype, out_dtype;
-    int N, M, K;
+    int N;
     float alpha;
-    int tiles_per_wg;  // FG: 16-feature tiles per workgroup sharing each activation tile
-    int waves_k;       // KW: K-groups per workgroup
+    int tiles, waves;
+    const VerifyProblem *probs;
+    int count;        // 1 .. kGroupPerLaunch
+    void *workspace;  // counters + partial tiles of every split problem
     hipStream_t stream;
 };
 
@@ -39,9 +58,21 @@ struct W4A8Args {
 
 inline size_t out_elem_bytes(int dtype) { return dtype == VQ_DTYPE_F32 ? 4 : 2; }
 
-hipError_t launch_verify(const VerifyArgs &p, bool fp8);
-size_t verify_lds_bytes(bool fp8, int fg, int kw, int K);
-bool verify_shape_ok(bool fp8, int fg, int kw, int K);
+int verify_steps(bool fp8, int K);
+int verify_tile_groups(int M, int tiles_per_group);
+int pipeline_depth_of(bool fp8, int tiles);
+int verify_max_chunk(int waves);
+// Workspace layout of a split-K call: a fixed region of arrival counters (one
+// per tile group, at most kMaxSplitTileGroups; always zero between calls, so
+// shapes of any size can share one workspace), then the fp32 partial tiles.
+constexpr int kMaxSplitTileGroups = 16384;
+size_t verify_counter_bytes();
+size_t verify_lds_bytes(bool fp8, int tiles, int waves, int chunk);
+size_t verify_partial_bytes(const VerifyPlan &plan, int M);
+size_t verify_workspace_bytes(const VerifyPlan &plan, int M);
+bool verify_plan_finish(bool fp8, int M, int K, VerifyPlan &plan);
+hipError_t launch_verify(const VerifyLaunch &launch);
+
 hipError_t launch_w4a8(const W4A8Args &p);
 hipError_t launch_h32_quant(const void *x, int x_dtype, int8_t *q, void *d, int N, int K,
                             hipStream_t stream);

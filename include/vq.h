@@ -25,17 +25,19 @@
  * Conventions shared by every entry point
  *  - All pointers are DEVICE pointers on the current HIP device, owned by the
  *    caller, 16-byte aligned, to contiguous row-major arrays.  The library
- *    never allocates, frees or synchronises, and keeps no per-call state, so
- *    calls from several host threads are safe.  Outputs must not alias inputs.
+ *    never allocates, frees or synchronises and keeps no state between calls
+ *    beyond what a caller's workspace holds, so calls from several host
+ *    threads are safe (each with its own workspace).  Outputs must not alias
+ *    inputs.
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *    enqueued on it and the call returns at once.
  *  - Every argument is checked before anything is enqueued.  On any non-zero
  *    return nothing was enqueued.  Faults during execution surface at the
  *    caller's next synchronisation, like any asynchronous HIP call.
  *  - Numerics: fp32 accumulation; outputs rounded to nearest-even.  For a given
- *    (M, K) the arithmetic of one output row depends only on that activation
- *    row and the weights: it is bit-identical whatever N is, whatever the other
- *    rows hold, and from run to run.
+ *    (M, K) and launch shape the arithmetic of one output row depends only on
+ *    that activation row and the weights: it is bit-identical whatever N is,
+ *    whatever the other rows hold, and from run to run.
  */
 #ifndef VQ_H
 #define VQ_H
@@ -56,6 +58,7 @@ extern "C" {
 #define VQ_ERR_DEVICE (-5)         /* current device is not gfx950, or no device */
 #define VQ_ERR_LAUNCH (-6)         /* the HIP launch itself reported an error */
 #define VQ_ERR_BAD_CONFIG (-7)     /* explicit launch shape not supported */
+#define VQ_ERR_WORKSPACE (-8)      /* explicit launch shape needs a larger workspace */
 
 /* Element type codes. */
 #define VQ_DTYPE_F16 1             /* IEEE binary16 */
@@ -63,8 +66,26 @@ extern "C" {
 #define VQ_DTYPE_F32 3             /* IEEE binary32 */
 #define VQ_DTYPE_I8 4              /* int8 */
 
+/* Weight formats, for the query functions. */
+#define VQ_KIND_Q4_0 0
+#define VQ_KIND_FP8_BLK128 1
+
 /* Largest M, K or N accepted by any entry point (indices stay in 32 bits). */
 #define VQ_MAX_DIM (1 << 24)
+
+/*
+ * Workspace of the verify GEMMs.  The kernels cut K into slices processed by
+ * different workgroups and combine the slices' fp32 partial sums through a
+ * caller-owned device buffer (per call: a few MB, see vq_workspace_bytes).
+ *  - 16-byte aligned device memory, zero-filled by the caller before its first
+ *    use.  Every call leaves it ready for the next one (its counters back at
+ *    zero), so it is zeroed once, not per call.
+ *  - Calls that share one workspace must not overlap in time: use it from one
+ *    stream, or order the streams.
+ *  - workspace may be NULL (or smaller than needed): the library then does not
+ *    split K, which is correct but slower.  For a fixed (M, K, workspace
+ *    capacity) the launch shape, and hence every output bit, is the same.
+ */
 
 /*
  * vq_gemm_q4_0 -- out[n][m] = alpha * sum_k x[n][k] * w[m][k], Q4_0 weights.
@@ -86,7 +107,8 @@ extern "C" {
  *            q_x[n][k].  Each 32-block dot sum (q - 8) * q_x is formed exactly
  *            in int32 before the fp32 scale products.  For weights and
  *            activations both rotated by the unnormalised H32, pass
- *            alpha = 1/32 to restore the unrotated product.
+ *            alpha = 1/32 to restore the unrotated product.  The workspace is
+ *            not used on this path.
  * Output: out [N][M], out_dtype F16, BF16 or F32.
  * Sizes: 1 <= N, M <= VQ_MAX_DIM; 32 <= K <= VQ_MAX_DIM, K % 32 == 0.
  * Returns VQ_OK or a VQ_ERR_* code.
@@ -95,7 +117,8 @@ int vq_gemm_q4_0(const void *w_codes, const void *w_scales,
                  const void *act, int act_dtype, const void *act_scales,
                  void *out, int out_dtype,
                  int64_t n_rows, int64_t m, int64_t k,
-                 float alpha, void *stream);
+                 float alpha, void *workspace, size_t workspace_bytes,
+                 void *stream);
 
 /*
  * vq_gemm_fp8_blk128 -- out[n][m] = sum_k x[n][k] * w[m][k], FP8 weights with
@@ -113,7 +136,8 @@ int vq_gemm_q4_0(const void *w_codes, const void *w_scales,
 int vq_gemm_fp8_blk128(const void *w_e4m3, const float *w_tile_scales,
                        const void *act, int act_dtype,
                        void *out, int out_dtype,
-                       int64_t n_rows, int64_t m, int64_t k, void *stream);
+                       int64_t n_rows, int64_t m, int64_t k,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * vq_hadamard32_quant_int8 -- per (row n, 32-block b) of x [N][K] [P4]:
@@ -134,31 +158,80 @@ int vq_hadamard32_quant_int8(const void *x, int x_dtype,
                              int64_t n_rows, int64_t k, void *stream);
 
 /*
+ * Grouped verify GEMMs -- several independent problems in as few kernel
+ * launches as possible ([P1]: a block is verified by one batched pass over
+ * all the weights; [P3]: the decode step is replayed as one HIP graph).  A
+ * decode step's projections that read the same activations (or a benchmark's
+ * unchained matrices) are independent; one launch over them pays the kernel
+ * start and drain once instead of per matrix, and its workgroups -- equal
+ * amounts of weight streaming each, by construction of the default shapes --
+ * keep every CU busy across matrix boundaries.
+ *   problems  host array of `count` descriptors, read during the call only.
+ *             Each problem's outputs are bit-identical to the corresponding
+ *             single call (vq_gemm_q4_0 / vq_gemm_fp8_blk128) with a large
+ *             enough workspace (or, with workspace NULL, with none).
+ *   act_dtype, out_dtype, n_rows (and alpha): shared by all problems.
+ *   workspace needs vq_workspace_bytes_grouped() bytes (VQ_ERR_WORKSPACE if
+ *             smaller); NULL runs every problem without splitting K.
+ * 1 <= count <= VQ_MAX_GROUP.  Float activations only.
+ */
+#define VQ_MAX_GROUP 4096
+
+typedef struct vq_verify_problem {
+    const void *w;       /* Q4_0 codes u8 [M][K/2], or E4M3 bytes u8 [M][K] */
+    const void *scales;  /* Q4_0 f16 [M][K/32], or FP8 f32 [ceil(M/128)][K/128] */
+    const void *act;     /* [n_rows][K] */
+    void *out;           /* [n_rows][M] */
+    int64_t m, k;
+} vq_verify_problem;
+
+int vq_gemm_q4_0_grouped(const vq_verify_problem *problems, int count,
+                         int act_dtype, int out_dtype, int64_t n_rows, float alpha,
+                         void *workspace, size_t workspace_bytes, void *stream);
+int vq_gemm_fp8_blk128_grouped(const vq_verify_problem *problems, int count,
+                               int act_dtype, int out_dtype, int64_t n_rows,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace a grouped call with these problems needs (0 if invalid). */
+size_t vq_workspace_bytes_grouped(int kind, const vq_verify_problem *problems, int count);
+
+/* Workspace bytes the default launch shape of an (M, K) verify GEMM uses
+ * (kind VQ_KIND_Q4_0 or VQ_KIND_FP8_BLK128; independent of N).  0 for invalid
+ * arguments or when the default shape does not split K. */
+size_t vq_workspace_bytes(int kind, int64_t m, int64_t k);
+
+/*
  * vq_gemm_q4_0_ex / vq_gemm_fp8_blk128_ex -- the same operations with an
- * explicit launch shape, for tuning: `tiles_per_wave` is the number of
- * 16-feature tiles per workgroup that share each staged activation tile
- * (1, 2 or 4; one wave per tile and K-group) and `waves_k` the number of
- * K-groups per workgroup (1, 2, 4, 8 or 16), with tiles_per_wave * waves_k <=
- * 16 and the workgroup's LDS within 160 KiB (VQ_ERR_BAD_CONFIG otherwise);
- * 0 for either picks the default for (M, K).  Results are bit-identical across
- * N for a fixed launch shape; a different launch shape may round differently.
+ * explicit launch shape, for tuning: `tiles_per_wave` 16-feature tiles per
+ * wave (1, 2 or 4), `waves_per_group` waves per workgroup (2, 4 or 8) and
+ * `k_slices` slices of K (1 .. K/128 rounded up; 1 = no split; the count is
+ * rounded to the number of non-empty equal slices).  0 for any of them picks
+ * the default for (M, K, workspace_bytes).  VQ_ERR_BAD_CONFIG for a shape
+ * outside these sets or beyond 160 KiB of LDS, VQ_ERR_WORKSPACE if
+ * k_slices > 1 needs more workspace than given.  Results are bit-identical
+ * across N for a fixed launch shape; another shape may round differently.
  * Float activations only.
  */
 int vq_gemm_q4_0_ex(const void *w_codes, const void *w_scales,
                     const void *act, int act_dtype,
                     void *out, int out_dtype,
                     int64_t n_rows, int64_t m, int64_t k, float alpha,
-                    int tiles_per_wave, int waves_k, void *stream);
+                    int tiles_per_wave, int waves_per_group, int k_slices,
+                    void *workspace, size_t workspace_bytes, void *stream);
 int vq_gemm_fp8_blk128_ex(const void *w_e4m3, const float *w_tile_scales,
                           const void *act, int act_dtype,
                           void *out, int out_dtype,
                           int64_t n_rows, int64_t m, int64_t k,
-                          int tiles_per_wave, int waves_k, void *stream);
+                          int tiles_per_wave, int waves_per_group, int k_slices,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
-/* The launch shape the library picks by default for an (M, K) verify GEMM:
- * kind 0 = Q4_0, 1 = FP8.  Writes tiles_per_wave and waves_k; returns VQ_OK. */
-int vq_default_launch_shape(int kind, int64_t m, int64_t k,
-                            int *tiles_per_wave, int *waves_k);
+/* The launch shape the library picks for an (M, K) verify GEMM given a
+ * workspace of workspace_bytes (SIZE_MAX = unlimited), and the workspace that
+ * shape uses.  Writes all four outputs; returns VQ_OK or VQ_ERR_BAD_SHAPE /
+ * VQ_ERR_NULL_POINTER. */
+int vq_default_launch_shape(int kind, int64_t m, int64_t k, size_t workspace_bytes,
+                            int *tiles_per_wave, int *waves_per_group, int *k_slices,
+                            size_t *workspace_used);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *vq_status_string(int status);

@@ -28,8 +28,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert vq.lib().vq_version() == 100
-    for st in (0, -1, -2, -3, -4, -5, -6, -7):
+    assert vq.lib().vq_version() == 200
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert vq.status_string(st) and vq.status_string(st) != "unknown status"
     assert vq.status_string(-99) == "unknown status"
 
@@ -41,8 +41,12 @@ D = 0x40000
 E = 0x50000
 
 
-def _q4(w=A, s=B, x=C, xd=vq.DTYPE_BF16, xs=None, o=D, od=vq.DTYPE_BF16, n=16, m=256, k=512, alpha=1.0):
-    return vq.lib().vq_gemm_q4_0(w, s, x, xd, xs, o, od, n, m, k, alpha, None)
+F = 0x60000   # fake workspace
+
+
+def _q4(w=A, s=B, x=C, xd=vq.DTYPE_BF16, xs=None, o=D, od=vq.DTYPE_BF16, n=16, m=256, k=512, alpha=1.0,
+        ws=None, wsb=0):
+    return vq.lib().vq_gemm_q4_0(w, s, x, xd, xs, o, od, n, m, k, alpha, ws, wsb, None)
 
 
 def test_q4_0_argument_errors():
@@ -59,14 +63,15 @@ def test_q4_0_argument_errors():
     assert _q4(m=(1 << 24) + 1) == vq.VQ_ERR_BAD_SHAPE
     assert _q4(x=C + 8) == vq.VQ_ERR_MISALIGNED
     assert _q4(w=A + 1) == vq.VQ_ERR_MISALIGNED
+    assert _q4(ws=F + 4, wsb=1 << 20) == vq.VQ_ERR_MISALIGNED
 
 
 def test_fp8_argument_errors():
     f = vq.lib().vq_gemm_fp8_blk128
-    assert f(None, B, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 4, 256, 512, None) == vq.VQ_ERR_NULL_POINTER
-    assert f(A, B, C, vq.DTYPE_I8, D, vq.DTYPE_BF16, 4, 256, 512, None) == vq.VQ_ERR_BAD_DTYPE
-    assert f(A, B, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 4, 256, 480, None) == vq.VQ_ERR_BAD_SHAPE
-    assert f(A, B + 4, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 4, 256, 512, None) == vq.VQ_ERR_MISALIGNED
+    assert f(None, B, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 4, 256, 512, None, 0, None) == vq.VQ_ERR_NULL_POINTER
+    assert f(A, B, C, vq.DTYPE_I8, D, vq.DTYPE_BF16, 4, 256, 512, None, 0, None) == vq.VQ_ERR_BAD_DTYPE
+    assert f(A, B, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 4, 256, 480, None, 0, None) == vq.VQ_ERR_BAD_SHAPE
+    assert f(A, B + 4, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 4, 256, 512, None, 0, None) == vq.VQ_ERR_MISALIGNED
 
 
 def test_quant_argument_errors():
@@ -77,21 +82,86 @@ def test_quant_argument_errors():
     assert f(A, vq.DTYPE_BF16, B + 2, C, 4, 64, None) == vq.VQ_ERR_MISALIGNED
 
 
+def _ex(t, w, s, ws=None, wsb=0, k=512):
+    return vq.lib().vq_gemm_q4_0_ex(A, B, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 16, 256, k, 1.0, t, w, s,
+                                    ws, wsb, None)
+
+
 def test_explicit_launch_shape_errors():
-    f = vq.lib().vq_gemm_q4_0_ex
-    assert f(A, B, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 16, 256, 512, 1.0, 3, 4, None) == vq.VQ_ERR_BAD_CONFIG
-    assert f(A, B, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 16, 256, 512, 1.0, 1, 32, None) == vq.VQ_ERR_BAD_CONFIG
+    assert _ex(3, 4, 1) == vq.VQ_ERR_BAD_CONFIG       # tiles per wave not in {1, 2, 4}
+    assert _ex(1, 16, 1) == vq.VQ_ERR_BAD_CONFIG      # waves per group not in {2, 4, 8}
+    assert _ex(1, 1, 1) == vq.VQ_ERR_BAD_CONFIG
+    assert _ex(1, 4, 5) == vq.VQ_ERR_BAD_CONFIG       # K = 512 has 4 steps: at most 4 slices
+    assert _ex(-1, 4, 1) == vq.VQ_ERR_BAD_CONFIG
+    assert _ex(1, 4, 2) == vq.VQ_ERR_WORKSPACE        # a split needs a workspace
+    assert _ex(1, 4, 2, ws=F, wsb=64) == vq.VQ_ERR_WORKSPACE
+
+
+def test_workspace_query():
+    f = vq.lib().vq_workspace_bytes
+    assert f(0, 17408, 5120) > 0 and f(1, 17408, 5120) > 0
+    assert f(0, 17408, 5000) == 0 and f(1, 17408, 5120 + 32) == 0 and f(7, 256, 512) == 0
+    for m, k in ((256, 512), (17408, 5120), (5120, 17408), (8192, 5120), (5120, 8192)):
+        t, w, s, used = vq.default_launch_shape("q4_0", m, k)
+        assert used == vq.workspace_bytes("q4_0", m, k)
+        assert used <= 16 << 20
+        # without a workspace the default does not split K
+        t0, w0, s0, used0 = vq.default_launch_shape("q4_0", m, k, workspace_bytes=0)
+        assert s0 == 1 and used0 == 0
 
 
 def test_default_launch_shape_ignores_rows():
-    # the shape is a function of (M, K) only, which is what keeps rows N-invariant
-    for m, k in ((256, 512), (17408, 5120), (5120, 17408), (8192, 5120), (5120, 8192)):
-        t, w = vq.default_launch_shape("q4_0", m, k)
-        assert t in (1, 2, 4) and w in (1, 2, 4, 8, 16)
-        t, w = vq.default_launch_shape("fp8", m, k)
-        assert t in (1, 2, 4) and w in (1, 2, 4, 8, 16)
+    # the shape is a function of (M, K, workspace) only, which keeps rows N-invariant
+    for m, k in ((256, 512), (17408, 5120), (5120, 17408), (8192, 5120), (5120, 8192), (17, 96)):
+        for kind in ("q4_0", "fp8"):
+            if kind == "fp8" and k % 128:
+                continue
+            t, w, s, used = vq.default_launch_shape(kind, m, k)
+            assert t in (1, 2, 4) and w in (2, 4, 8) and 1 <= s <= max(1, (k + 127) // 128)
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
 def test_valid_arguments_without_device_report_device_error():
     assert _q4() == vq.VQ_ERR_DEVICE
+
+
+def _table(rows):
+    t = (vq.VerifyProblem * len(rows))()
+    for i, r in enumerate(rows):
+        t[i] = vq.VerifyProblem(*r)
+    return t
+
+
+def test_grouped_argument_errors():
+    f = vq.lib().vq_gemm_q4_0_grouped
+    good = (A, B, C, D, 256, 512)
+    t = _table([good, good])
+    assert f(None, 2, vq.DTYPE_BF16, vq.DTYPE_BF16, 16, 1.0, None, 0, None) == vq.VQ_ERR_NULL_POINTER
+    assert f(t, 0, vq.DTYPE_BF16, vq.DTYPE_BF16, 16, 1.0, None, 0, None) == vq.VQ_ERR_BAD_SHAPE
+    assert f(t, 4097, vq.DTYPE_BF16, vq.DTYPE_BF16, 16, 1.0, None, 0, None) == vq.VQ_ERR_BAD_SHAPE
+    assert f(t, 2, vq.DTYPE_BF16, vq.DTYPE_BF16, 0, 1.0, None, 0, None) == vq.VQ_ERR_BAD_SHAPE
+    assert f(t, 2, vq.DTYPE_I8, vq.DTYPE_BF16, 16, 1.0, None, 0, None) == vq.VQ_ERR_BAD_DTYPE
+    assert f(_table([good, (A, None, C, D, 256, 512)]), 2, vq.DTYPE_BF16, vq.DTYPE_BF16, 16, 1.0, None, 0,
+             None) == vq.VQ_ERR_NULL_POINTER
+    assert f(_table([good, (A, B, C, D, 256, 500)]), 2, vq.DTYPE_BF16, vq.DTYPE_BF16, 16, 1.0, None, 0,
+             None) == vq.VQ_ERR_BAD_SHAPE
+    assert f(_table([(A, B, C + 2, D, 256, 512)]), 1, vq.DTYPE_BF16, vq.DTYPE_BF16, 16, 1.0, None, 0,
+             None) == vq.VQ_ERR_MISALIGNED
+    # a workspace smaller than the group needs (K = 5120 splits into 5 slices)
+    big = _table([(A, B, C, D, 256, 5120)] * 2)
+    assert f(big, 2, vq.DTYPE_BF16, vq.DTYPE_BF16, 16, 1.0, F, 64, None) == vq.VQ_ERR_WORKSPACE
+    g = vq.lib().vq_gemm_fp8_blk128_grouped
+    assert g(_table([(A, B, C, D, 256, 500)]), 1, vq.DTYPE_BF16, vq.DTYPE_BF16, 4, None, 0,
+             None) == vq.VQ_ERR_BAD_SHAPE
+
+
+def test_grouped_workspace_query():
+    f = vq.lib().vq_workspace_bytes_grouped
+    layer = [(A, B, C, D, m, k) for m, k in ((8192, 5120), (5120, 8192), (17408, 5120), (17408, 5120),
+                                             (5120, 17408))]
+    need = f(vq.KIND_Q4_0, _table(layer), 5)
+    single = [vq.workspace_bytes("q4_0", m, k) for *_, m, k in layer]
+    counters = 64 * 1024
+    assert need == counters + sum(s - counters for s in single)
+    assert f(vq.KIND_Q4_0, _table(layer + [(A, B, C, D, 17, 100)]), 6) == 0   # K % 32 != 0
+    assert f(9, _table(layer), 5) == 0

@@ -95,13 +95,31 @@ def test_fp8_ragged_parity(M, K, N, out_dtype):
     parity(out_to_f64(q.run(f["act"], "bf16", out_dtype)), q.oracle(f["act"]), out_dtype)
 
 
+_WS = {}
+
+
+def big_workspace():
+    if "ws" not in _WS:
+        _WS["ws"] = vq.Workspace(32 << 20)
+    return _WS["ws"]
+
+
 @pytest.mark.parametrize("tpw", [1, 2, 4])
-@pytest.mark.parametrize("kw", [1, 4, 8, 16])
-def test_fp8_launch_shapes(tpw, kw):
+@pytest.mark.parametrize("wpg", [2, 4, 8])
+@pytest.mark.parametrize("ks", [1, 3, 10])
+def test_fp8_launch_shapes(tpw, wpg, ks):
+    """17 tiles (three 128-row scale tiles, the last partial), 10 steps of K:
+    partial tile groups, slices of 1..10 steps, multi-chunk slices (ks = 1)."""
     f = W.fp8(M=272, K=1280, N=16)
     q = FP8(f["w"], f["tscales"])
-    if tpw * kw > 16:
-        with pytest.raises(vq.VqError):
-            q.run(f["act"], tiles_per_wave=tpw, waves_k=kw)
-        return
-    parity(out_to_f64(q.run(f["act"], tiles_per_wave=tpw, waves_k=kw)), q.oracle(f["act"]), "bf16")
+    kw = dict(tiles_per_wave=tpw, waves_per_group=wpg, k_slices=ks, workspace=big_workspace())
+    parity(out_to_f64(q.run(f["act"], **kw)), q.oracle(f["act"]), "bf16")
+
+
+def test_fp8_without_workspace():
+    f = W.fp8(M=1000, K=2560, N=16)
+    q = FP8(f["w"], f["tscales"])
+    y = q.run(f["act"], workspace=None)
+    parity(out_to_f64(y), q.oracle(f["act"]), "bf16")
+    one = bits_u16(q.run(np.ascontiguousarray(f["act"][9:10]), workspace=None))
+    assert np.array_equal(one[0], bits_u16(y)[9])

@@ -180,38 +180,98 @@ def test_ragged_shapes_parity(M, K, N):
     parity(out_to_f64(q.run(a)), q.oracle(a), "bf16")
 
 
+_WS = {}
+
+
+def big_workspace():
+    """One zeroed 32 MiB workspace shared by the explicit-shape tests (calls are
+    ordered on one stream, so sharing it is allowed)."""
+    if "ws" not in _WS:
+        _WS["ws"] = vq.Workspace(32 << 20)
+    return _WS["ws"]
+
+
 @pytest.mark.parametrize("tpw", [1, 2, 4])
-@pytest.mark.parametrize("kw", [1, 2, 4, 8, 16])
-def test_every_launch_shape_parity_and_exact_integers(tpw, kw):
+@pytest.mark.parametrize("wpg", [2, 4, 8])
+@pytest.mark.parametrize("ks", [1, 2, 3, 9])
+def test_every_launch_shape_parity_and_exact_integers(tpw, wpg, ks):
+    """17 tiles and 33 blocks (a partial last step of 128): partial tile groups,
+    slices of 1..9 steps, multi-chunk slices (ks = 1), every tile/wave shape."""
     g = np.random.Generator(np.random.PCG64(105))
-    M, K, N = 272, 1056, 16          # 17 tiles, 33 blocks: partial workgroups and a partial last K step
+    M, K, N = 272, 1056, 16
     codes = W.q4_0_codes(M, K, g)
     q = Q4(codes, W.fp16_scales_uniform(M, K, g))
     a = W.f32_to_bf16_bits(g.standard_normal((N, K)))
-    if tpw * kw > 16:
-        with pytest.raises(vq.VqError) as e:
-            q.run(a, tiles_per_wave=tpw, waves_k=kw)
-        assert e.value.status == vq.VQ_ERR_BAD_CONFIG
-        return
-    parity(out_to_f64(q.run(a, tiles_per_wave=tpw, waves_k=kw)), q.oracle(a), "bf16")
+    kw = dict(tiles_per_wave=tpw, waves_per_group=wpg, k_slices=ks, workspace=big_workspace())
+    parity(out_to_f64(q.run(a, **kw)), q.oracle(a), "bf16")
     qi = Q4(codes, np.full((M, K // 32), 0x3C00, dtype=np.uint16))
     ai = W.f32_to_bf16_bits(g.integers(-4, 5, size=(N, K)))
-    assert np.array_equal(out_to_f64(qi.run(ai, "bf16", "f32", tiles_per_wave=tpw, waves_k=kw)), qi.oracle(ai))
+    assert np.array_equal(out_to_f64(qi.run(ai, "bf16", "f32", **kw)), qi.oracle(ai))
 
 
-@pytest.mark.parametrize("tpw,kw", [(1, 16), (2, 8), (4, 4), (4, 2), (2, 1)])
-def test_launch_shapes_rows_bit_identical_across_widths(tpw, kw):
+@pytest.mark.parametrize("tpw,wpg", [(3, 4), (1, 1), (1, 16), (4, 3)])
+def test_unsupported_launch_shapes_rejected(tpw, wpg):
+    g = np.random.Generator(np.random.PCG64(108))
+    M, K = 64, 256
+    q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_uniform(M, K, g))
+    with pytest.raises(vq.VqError) as e:
+        q.run(W.f32_to_bf16_bits(g.standard_normal((4, K))), tiles_per_wave=tpw, waves_per_group=wpg,
+              k_slices=1, workspace=big_workspace())
+    assert e.value.status == vq.VQ_ERR_BAD_CONFIG
+
+
+def test_split_without_workspace_rejected():
+    g = np.random.Generator(np.random.PCG64(109))
+    M, K = 64, 1024
+    q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_uniform(M, K, g))
+    with pytest.raises(vq.VqError) as e:
+        q.run(W.f32_to_bf16_bits(g.standard_normal((4, K))), tiles_per_wave=1, waves_per_group=4, k_slices=4,
+              workspace=None)
+    assert e.value.status == vq.VQ_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("tpw,wpg,ks", [(4, 4, 9), (2, 8, 4), (1, 2, 1), (4, 2, 3), (2, 4, 0)])
+def test_launch_shapes_rows_bit_identical_across_widths(tpw, wpg, ks):
     """Width invariance holds in every launch shape, not only the default one."""
     g = np.random.Generator(np.random.PCG64(107))
     M, K = 400, 2080
     q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_lognormal(M, K, g))
     x = W.f32_to_bf16_bits(0.5 * g.standard_t(3, size=(16, K)))
-    full = bits_u16(q.run(x, tiles_per_wave=tpw, waves_k=kw))
+    kw = dict(tiles_per_wave=tpw, waves_per_group=wpg, k_slices=ks, workspace=big_workspace())
+    full = bits_u16(q.run(x, **kw))
     for n in (0, 7, 15):
-        one = bits_u16(q.run(np.ascontiguousarray(x[n:n + 1]), tiles_per_wave=tpw, waves_k=kw))
+        one = bits_u16(q.run(np.ascontiguousarray(x[n:n + 1]), **kw))
         assert np.array_equal(one[0], full[n])
-    assert np.array_equal(bits_u16(q.run(np.ascontiguousarray(x[3:11]), tiles_per_wave=tpw, waves_k=kw)),
-                          full[3:11])
+    assert np.array_equal(bits_u16(q.run(np.ascontiguousarray(x[3:11]), **kw)), full[3:11])
+
+
+def test_without_workspace_parity_and_width_invariance():
+    """No workspace: K is not split (every workgroup walks all of K chunk by chunk)."""
+    g = np.random.Generator(np.random.PCG64(110))
+    M, K = 1000, 5120
+    q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_lognormal(M, K, g))
+    x = W.f32_to_bf16_bits(0.5 * g.standard_t(3, size=(16, K)))
+    full = q.run(x, workspace=None)
+    parity(out_to_f64(full), q.oracle(x), "bf16")
+    one = bits_u16(q.run(np.ascontiguousarray(x[5:6]), workspace=None))
+    assert np.array_equal(one[0], bits_u16(full)[5])
+
+
+def test_workspace_reused_across_shapes_and_calls():
+    """A workspace left by one call is ready for the next: the arrival counters
+    return to zero, so alternating shapes and repeats stay exact."""
+    g = np.random.Generator(np.random.PCG64(111))
+    ws = vq.Workspace(32 << 20)
+    mats = []
+    for M, K in ((1088, 5120), (320, 8192), (17, 96)):
+        q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_uniform(M, K, g))
+        x = W.f32_to_bf16_bits(g.standard_normal((16, K)))
+        mats.append((q, x, bits_u16(q.run(x, workspace=ws))))
+    for rep in range(3):
+        for q, x, ref in mats:
+            assert np.array_equal(bits_u16(q.run(x, workspace=ws)), ref)
+    cnt = ws.tensor[:65536].cpu().numpy()
+    assert not cnt.any()  # the arrival-counter region is back to zero
 
 
 def test_many_row_groups():
