@@ -68,11 +68,11 @@ struct KProblem {
 };
 
 // A launch: up to kGroupPerLaunch problems sharing the launch shape, the row
-// count (<= 16), the output dtype and alpha.  Workgroup b works on item
-// b - item0 of the last problem whose item0 <= b.
+// count (<= 16), the output dtype and alpha; `items` workgroups in all.  Item
+// i belongs to the last problem whose item0 <= i.
 struct KGroup {
     KProblem p[kGroupPerLaunch];
-    int count, N, out_dtype;
+    int count, items, N, out_dtype;
     float alpha;
 };
 
@@ -118,10 +118,19 @@ __global__ __launch_bounds__(64 * W) void verify_kernel(const KGroup grp) {
     constexpr int kOut = 0x7FFFFFF0;            // an offset past every buffer: the load returns zeros
     static_assert(CH % PF == 0, "chunks hold whole pipeline rounds");
 
-    // ---- this workgroup's problem and item (wave-uniform scalar work)
+    // ---- this workgroup's item and problem (wave-uniform scalar work).
+    // Workgroups are handed to the 8 XCDs in turn (b % 8); each XCD is given
+    // one contiguous range of items, so the slices and tile groups that share
+    // an activation slice run on one XCD close together in time and find it
+    // in that XCD's L2.  (A bijection on [0, items): the result does not
+    // depend on where an item runs, only the cache behaviour does.)
+    const int b = (int)blockIdx.x;
+    const int nq = grp.items >> 3, nr = grp.items & 7;
+    const int xcd = b & 7, loc = b >> 3;
+    const int it_all = xcd < nr ? xcd * (nq + 1) + loc : nr * (nq + 1) + (xcd - nr) * nq + loc;
     int pi = 0;
     for (int q = 1; q < grp.count; ++q)
-        if ((int)blockIdx.x >= grp.p[q].item0)
+        if (it_all >= grp.p[q].item0)
             pi = q;
     const KProblem &a = grp.p[pi];
     const int lane = threadIdx.x & 63;
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(64 * W) void verify_kernel(const KGroup grp) {
     const int M = a.M, K = a.K, S = a.S;
     const int NB = K >> 5;
     const int steps = FP8 ? (K >> 7) : ((NB + 3) >> 2);  // the last Q4_0 step may be partial
-    const int item = (int)blockIdx.x - a.item0;
+    const int item = it_all - a.item0;
     const int tg = item / S;
     const int sidx = item - tg * S;
     const int s0 = sidx * a.sl;
@@ -462,6 +471,7 @@ hipError_t launch_tw(const VerifyLaunch &l) {
             grp.p[i].act = static_cast<const uint16_t *>(q.act) + (size_t)g0 * 16 * q.K;
             grp.p[i].out = static_cast<char *>(q.out) + (size_t)g0 * 16 * q.M * out_elem_bytes(l.out_dtype);
         }
+        grp.items = items;
         hipLaunchKernelGGL(kern, dim3(items), dim3(64 * W), shm, l.stream, grp);
     }
     return hipGetLastError();
