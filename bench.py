@@ -4,17 +4,30 @@
 One step is one pass over a synthetic 27B-class weight stack: 64 layers, each
 with Q4_0 matrices 8192x5120, 5120x8192, 17408x5120 (twice) and 5120x17408
 (12.65 GB of codes and scales), each multiplied by that layer's 16-row bf16
-draft block -- 320 verify-GEMM calls.  Inputs are drawn on the device with a
-seeded generator and resident in HBM before timing starts.
+draft block -- 320 verify GEMMs.  Inputs are drawn on the device with a seeded
+generator and resident in HBM before timing starts.
+
+Each layer's five independent GEMMs go to the library as one grouped call (one
+kernel launch per layer), and the step's 64 launches are replayed as one HIP
+graph, as an engine replays its decode step.  The same step is also timed with
+one library call per matrix (320 launches, eager and graph-replayed) and as
+whole-stack grouped calls; those figures are reported beside the headline.
 
 Prints one JSON line: the stream's sustained HBM GB/s at 16 rows (the value),
-the same at 1 and 8 rows, rows*weights/s, the verify kernel's roofline
-fraction against 8 TB/s, and the CPU oracle timed on a bounded sample of the
-same workload.  See the --help text for options.
+the same at 1 and 8 rows, rows*weights/s, the verify kernel's roofline fraction
+against 8 TB/s, measured HBM traffic per launch (from rocprofv3 counters, while
+the kernel sources are unchanged since they were taken), and the CPU oracle
+timed on a bounded sample of the same workload.
+
+Counter runs (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE) use
+`--profile-run`; `--traffic-from FETCH_DIR WRITE_DIR` turns their CSV output
+into the stored traffic figure.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -29,7 +42,9 @@ LAYERS = 64
 SHAPES = ((8192, 5120), (5120, 8192), (17408, 5120), (17408, 5120), (5120, 17408))
 METRIC = "verify GEMM HBM GB/s (% of peak) at N_rows=1/8/16; rows·weights/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q4_0_stream.json")
-KERNEL_SOURCES = ("block_quantized_gemm_amd/csrc/verify_gemm.hip", "block_quantized_gemm_amd/csrc/vq_device.h")
+KERNEL_SOURCES = ("block_quantized_gemm_amd/csrc/verify_gemm.hip", "block_quantized_gemm_amd/csrc/vq_device.h",
+                  "block_quantized_gemm_amd/csrc/vq_api.cpp")
+COPY_BYTES = 512 << 20  # calibration copy for the traffic counters
 
 
 def kernel_source_hash() -> str:
@@ -44,10 +59,16 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10, help="timed passes over the stack")
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-oracle budget")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="a short run for rocprofv3 counters: a few grouped passes at 16 rows, then a "
+                         "512 MiB device copy that calibrates the byte counters; prints nothing else")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="read rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output of --profile-run and store "
+                         "the verify kernel's HBM bytes per launch in profiles/")
     return ap.parse_args()
 
 
@@ -75,27 +96,64 @@ def algorithmic_bytes(mats, n_rows):
     return w, w + x + y
 
 
-def time_stream(vq, mats, acts, outs, n_rows, steps, warmup):
+class Stream:
+    """The step in its three launch forms, for a given row count."""
+
+    def __init__(self, vq, mats, acts, outs, n_rows, ws):
+        self.vq, self.mats, self.n = vq, mats, n_rows
+        self.views = {key: a[:n_rows] for key, a in acts.items()}
+        self.oviews = {m: o[:n_rows] for m, o in outs.items()}
+        self.ws = ws
+        layers = sorted({l for l, *_ in mats})
+        self.layer_calls = [
+            vq.GroupedCall("q4_0", [(c, s, self.views[(l, k)], self.oviews[m]) for l2, m, k, c, s in mats if l2 == l],
+                           workspace=ws)
+            for l in layers]
+        self.whole_call = vq.GroupedCall(
+            "q4_0", [(c, s, self.views[(l, k)], self.oviews[m]) for l, m, k, c, s in mats], workspace=ws)
+
+    def per_call(self, stream):
+        for layer, m, k, codes, scales in self.mats:
+            self.vq.gemm_q4_0(codes, scales, self.views[(layer, k)], self.oviews[m], workspace=self.ws, stream=stream)
+
+    def per_layer(self, stream):
+        for call in self.layer_calls:
+            call(stream)
+
+    def whole(self, stream):
+        self.whole_call(stream)
+
+
+def time_ms(fn, stream, steps, warmup, graph):
+    """ms per step: HIP events on the launch stream around `steps` steps (or
+    replays of one captured step) after `warmup` untimed ones."""
     import torch
-    stream = torch.cuda.current_stream()
-    views = {key: a[:n_rows] for key, a in acts.items()}
-    oviews = {m: o[:n_rows] for m, o in outs.items()}
-
-    def one_step():
-        for layer, m, k, codes, scales in mats:
-            vq.gemm_q4_0(codes, scales, views[(layer, k)], oviews[m], stream=stream)
-
-    for _ in range(warmup):
-        one_step()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup)):
+            fn(stream)
     torch.cuda.synchronize()
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn(stream)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                g.replay()
+        torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        one_step()
-    e1.record(stream)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(steps):
+            if g is not None:
+                g.replay()
+            else:
+                fn(stream)
+        e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps  # ms per step
+    return e0.elapsed_time(e1) / steps
 
 
 def cpu_baseline(budget_s):
@@ -124,16 +182,59 @@ def cpu_baseline(budget_s):
         spent += dt
         done_bytes += b
         done_rw += rw
-        sample.append(f)
+        sample.append(feats)
         feats *= 2
     return dict(value=round(done_bytes / spent / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
                 rows_weights_per_s=done_rw / spent,
-                sample="layer 0 of the stack, 16 rows, output features 0..F-1 of each of its 5 matrices "
-                       "for F = %s; %.1f s of fp64 scalar C on %d threads" % (sample, spent, threads))
+                sample="layer 0 of the stack, 16 rows, output features 0..min(F, M)-1 of each of its 5 "
+                       "matrices for F = %s; %.1f s of fp64 scalar C on %d threads" % (sample, spent, threads))
+
+
+def traffic_from(fetch_dir, write_dir):
+    """Per-launch HBM bytes of the verify kernel from two counter runs of
+    --profile-run, each scaled by what the same counter reads for the plain
+    copy of COPY_BYTES in that run."""
+    def per_kernel(d, counter):
+        vals = {"verify": [], "copy": []}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                if "verify_kernel" in name:
+                    vals["verify"].append(float(r["Counter_Value"]))
+                elif "copyBuffer" in name:
+                    vals["copy"].append(float(r["Counter_Value"]))
+        if not vals["verify"] or not vals["copy"]:
+            raise SystemExit("no %s rows for the verify kernel and the copy in %s" % (counter, d))
+        # the calibration copies are the largest device-to-device copies of the run
+        top = max(vals["copy"])
+        cal = [v for v in vals["copy"] if v >= 0.9 * top]
+        return sum(vals["verify"]) / len(vals["verify"]), sum(cal) / len(cal)
+    fv, fc = per_kernel(fetch_dir, "FETCH_SIZE")
+    wv, wc = per_kernel(write_dir, "WRITE_SIZE")
+    fetch_scale, write_scale = COPY_BYTES / (fc * 1024), COPY_BYTES / (wc * 1024)
+    rec = {
+        "kernel_source_hash": kernel_source_hash(),
+        "workload": "grouped per-layer launch, 5 stream matrices, 16 bf16 rows",
+        "hbm_bytes_per_launch": round(fv * 1024 * fetch_scale + wv * 1024 * write_scale),
+        "read_bytes_per_launch": round(fv * 1024 * fetch_scale),
+        "write_bytes_per_launch": round(wv * 1024 * write_scale),
+        "fetch_kib_raw": fv, "write_kib_raw": wv,
+        "copy_fetch_kib": fc, "copy_write_kib": wc,
+        "fetch_scale": fetch_scale, "write_scale": write_scale,
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus %d is not supported" % args.gpus}))
         sys.exit(2)
@@ -141,18 +242,44 @@ def main():
     import block_quantized_gemm_amd as vq
     vq.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
 
-    mats, acts, outs = build_stack(args.layers, dev)
-    n_calls = len(mats)
+    layers = min(args.layers, 8) if args.profile_run else args.layers
+    mats, acts, outs = build_stack(layers, dev)
+    layer_mats = mats[:len(SHAPES)]
+    ws = vq.Workspace(vq.GroupedCall("q4_0", [(c, s, acts[(0, k)], outs[m]) for _, m, k, c, s in mats[:32]],
+                                     workspace=None).workspace_bytes + (1 << 20), dev)
+    streams = {n: Stream(vq, mats, acts, outs, n, ws) for n in (16, 8, 1)}
+
+    if args.profile_run:
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                streams[16].per_layer(stream)
+        torch.cuda.synchronize()
+        a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print("profile run done: %d layers" % layers, flush=True)
+        return
+
+    n_launch = len(streams[16].layer_calls)
     ms = {}
     for n in (16, 8, 1):
-        ms[n] = time_stream(vq, mats, acts, outs, n, args.steps if n == 16 else max(2, args.steps // 2),
-                            args.warmup)
+        ms[n] = time_ms(streams[n].per_layer, stream, args.steps if n == 16 else max(2, args.steps // 2),
+                        args.warmup, graph=True)
+    extra = {
+        "grouped_per_layer_graph": ms[16],
+        "grouped_whole_stack_graph": time_ms(streams[16].whole, stream, max(2, args.steps // 2), args.warmup, True),
+        "per_call_graph": time_ms(streams[16].per_call, stream, max(2, args.steps // 2), args.warmup, True),
+        "per_call_eager": time_ms(streams[16].per_call, stream, max(2, args.steps // 2), args.warmup, False),
+    }
     w_bytes, alg16 = algorithmic_bytes(mats, 16)
     gbs = {n: algorithmic_bytes(mats, n)[1] / (ms[n] * 1e-3) / 1e9 for n in ms}
     n_weights = sum(m * k for _, m, k, _, _ in mats)
-    per_launch_us = ms[16] * 1e3 / n_calls
-    achieved = alg16 / n_calls / (per_launch_us * 1e-6) / 1e9
+    per_launch_us = ms[16] * 1e3 / n_launch
+    achieved = alg16 / n_launch / (per_launch_us * 1e-6) / 1e9
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -176,8 +303,8 @@ def main():
         "data": "synthetic (seeded on-device draws: Q4_0 codes uniform, fp16 scales U[0.001,0.02], bf16 rows N(0,1))",
         "config": {
             "workload": "Q4_0 per-token weight stream: %d layers x (8192x5120, 5120x8192, 17408x5120 x2, "
-                        "5120x17408), %d verify-GEMM calls per step, bf16 draft block of 16 rows per layer"
-                        % (args.layers, n_calls),
+                        "5120x17408), 16-row bf16 draft block per layer; each layer's 5 GEMMs one grouped "
+                        "call, the step's %d launches replayed as one HIP graph" % (args.layers, n_launch),
             "weight_bytes": w_bytes,
             "n_rows": 16,
         },
@@ -186,16 +313,18 @@ def main():
         "ms_by_rows": {str(n): round(ms[n], 4) for n in (1, 8, 16)},
         "t16_over_t1": round(ms[16] / ms[1], 4),
         "rows_weights_per_s": 16 * n_weights / (ms[16] * 1e-3),
+        "launch_forms_gbs_16_rows": {k: round(alg16 / (v * 1e-3) / 1e9, 2) for k, v in extra.items()},
         "roofline": {
             "bound": "hbm",
-            "kernel": "vq::verify_kernel (Q4_0, bf16 activations)",
+            "kernel": "vq::verify_kernel (Q4_0, bf16 activations, grouped per layer)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "avg_launch_us": round(per_launch_us, 3),
-            "launches_per_step": n_calls,
+            "launches_per_step": n_launch,
+            "algorithmic_bytes_per_launch": alg16 // n_launch,
         },
     }
     if not args.no_cpu_baseline:
