@@ -132,10 +132,12 @@ def _check_2d(t, name, shape):
 
 
 class Workspace:
-    """A zero-filled device buffer for the verify GEMMs' split-K partial sums.
+    """A zero-filled device buffer for the walk form of the verify GEMMs:
+    arrival counters and the partial sums of tile groups cut between two
+    workgroups.
 
-    The library leaves it ready for the next call, so it is zeroed once.
-    Calls sharing one workspace must be ordered (one stream)."""
+    The library leaves the counters at zero after every call, so it is zeroed
+    once.  Calls sharing one workspace must be ordered (one stream)."""
 
     def __init__(self, nbytes: int, device=None):
         torch = _torch()
@@ -155,7 +157,7 @@ _auto_lock = threading.Lock()
 
 
 def _workspace_args(workspace, kind: int, m: int, k: int, device, stream_handle: int):
-    """(pointer, bytes) for a call: a Workspace, None (no split), or "auto" = a
+    """(pointer, bytes) for a call: a Workspace, None (one-shot form), or "auto" = a
     workspace cached per (device, stream), grown to what the default shape uses."""
     if workspace is None:
         return None, 0
@@ -181,15 +183,15 @@ def workspace_bytes(kind: str, m: int, k: int) -> int:
 
 
 def gemm_q4_0(codes, scales, x, out, *, x_scales=None, alpha: float = 1.0, workspace="auto", stream=None,
-              tiles_per_wave: int = 0, waves_per_group: int = 0, k_slices: int = 0):
+              tiles_per_wave: int = 0, waves_per_group: int = 0, max_groups: int = 0):
     """out[N][M] = alpha * x[N][K] @ dequant(codes, scales)[M][K]^T.
 
     codes: uint8 [M][K/2]; scales: float16 [M][K/32]; x: float16 / bfloat16 [N][K]
     or int8 [N][K] with x_scales float16 [N][K/32]; out: float16 / bfloat16 /
     float32 [N][M].  workspace: "auto" (a cached per-stream Workspace), a
-    Workspace, or None (K is not split).  tiles_per_wave / waves_per_group /
-    k_slices select an explicit launch shape (float activations only; 0 =
-    library default)."""
+    Workspace, or None (the one-shot form).  tiles_per_wave / waves_per_group
+    / max_groups select an explicit launch shape, the walk form when a
+    workspace is given (float activations only; 0 = library default)."""
     N, K = x.shape
     M = codes.shape[0]
     _check_2d(codes, "codes", (M, K // 2))
@@ -210,10 +212,10 @@ def gemm_q4_0(codes, scales, x, out, *, x_scales=None, alpha: float = 1.0, works
     if x_scales is not None:
         raise ValueError("x_scales only go with int8 activations")
     wp, wn = _workspace_args(workspace, KIND_Q4_0, M, K, codes.device, sh)
-    if tiles_per_wave or waves_per_group or k_slices:
+    if tiles_per_wave or waves_per_group or max_groups:
         st = L.vq_gemm_q4_0_ex(_dev_ptr(codes, "codes"), _dev_ptr(scales, "scales"), _dev_ptr(x, "x"),
                                act_dtype, _dev_ptr(out, "out"), _dtype_code(out), N, M, K,
-                               float(alpha), int(tiles_per_wave), int(waves_per_group), int(k_slices),
+                               float(alpha), int(tiles_per_wave), int(waves_per_group), int(max_groups),
                                wp, wn, sh)
         _check(st, "vq_gemm_q4_0_ex")
     else:
@@ -225,7 +227,7 @@ def gemm_q4_0(codes, scales, x, out, *, x_scales=None, alpha: float = 1.0, works
 
 
 def gemm_fp8_blk128(w, tile_scales, x, out, *, workspace="auto", stream=None, tiles_per_wave: int = 0,
-                    waves_per_group: int = 0, k_slices: int = 0):
+                    waves_per_group: int = 0, max_groups: int = 0):
     """out[N][M] = x[N][K] @ (e4m3(w) * tile_scales[m/128][k/128])^T.
 
     w: uint8 [M][K] (E4M3FN bits); tile_scales: float32 [ceil(M/128)][K/128];
@@ -238,10 +240,10 @@ def gemm_fp8_blk128(w, tile_scales, x, out, *, workspace="auto", stream=None, ti
     L = lib()
     sh = _stream(stream)
     wp, wn = _workspace_args(workspace, KIND_FP8_BLK128, M, K, w.device, sh)
-    if tiles_per_wave or waves_per_group or k_slices:
+    if tiles_per_wave or waves_per_group or max_groups:
         st = L.vq_gemm_fp8_blk128_ex(_dev_ptr(w, "w"), _dev_ptr(tile_scales, "tile_scales"), _dev_ptr(x, "x"),
                                      _dtype_code(x), _dev_ptr(out, "out"), _dtype_code(out), N, M, K,
-                                     int(tiles_per_wave), int(waves_per_group), int(k_slices), wp, wn, sh)
+                                     int(tiles_per_wave), int(waves_per_group), int(max_groups), wp, wn, sh)
         _check(st, "vq_gemm_fp8_blk128_ex")
     else:
         st = L.vq_gemm_fp8_blk128(_dev_ptr(w, "w"), _dev_ptr(tile_scales, "tile_scales"), _dev_ptr(x, "x"),
@@ -258,7 +260,7 @@ class GroupedCall:
     x dtype, out dtype and row count; kind "q4_0" (w uint8 [M][K/2], scales
     float16 [M][K/32]) or "fp8" (w uint8 [M][K], scales float32
     [ceil(M/128)][K/128]).  workspace: a Workspace (grown here to what the
-    group needs), "auto" (a new one of that size) or None (K not split)."""
+    group needs), "auto" (a new one of that size) or None (one-shot form)."""
 
     def __init__(self, kind: str, problems, *, alpha: float = 1.0, workspace="auto"):
         if kind not in ("q4_0", "fp8"):
@@ -336,8 +338,9 @@ def hadamard32_quant_int8(x, q_out, scales_out, *, stream=None):
 
 
 def default_launch_shape(kind: str, m: int, k: int, workspace_bytes=None):
-    """(tiles_per_wave, waves_per_group, k_slices, workspace_used) the library
-    picks for an (M, K) verify GEMM given workspace_bytes (None = unlimited)."""
+    """(tiles_per_wave, waves_per_group, walk, workspace_used) the library
+    picks for an (M, K) verify GEMM given workspace_bytes (None = unlimited);
+    walk is 1 for the walk form, 0 for one-shot."""
     t, w, s = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
     used = ctypes.c_size_t(0)
     cap = (1 << 64) - 1 if workspace_bytes is None else int(workspace_bytes)

@@ -26,33 +26,34 @@
 //    16-bit conversion (exact), 4 MFMAs per step, one FMA with the fp32 tile
 //    scale.
 //
-// Work decomposition (the kernel is bound by HBM and by what reaches the CUs):
-//  * A workgroup is W waves; each wave owns T tiles of 16 features, so the
-//    workgroup covers TG = T * W tiles.  K is cut into S slices of `sl` steps
-//    of 128; workgroup (tile group, slice) computes its TG tiles over its
-//    slice.  The grid is sized so that all workgroups are resident at once
-//    and every wave has the same work.
-//  * The slice's 16 activation rows (and, for Q4_0, the workgroup's block
-//    scales) are staged into LDS in MFMA operand order with whole-line loads;
-//    afterwards the waves only read LDS (no barrier inside a chunk).  Each
-//    staged activation element serves TG tiles, so activation traffic is
-//    1/TG of what a per-tile read would cost.
-//  * Weight bytes are streamed with 16-byte raw buffer loads (rows past M read
-//    as zeros) PF steps ahead of the compute in a register pipeline.
-//  * Slices of one tile group are combined through a caller workspace: each
-//    workgroup writes its fp32 partial tiles, then counts itself in; the last
-//    to arrive adds the S partials in the fixed order 0, 1, ..., S-1 and
-//    stores the output.  No value is combined by atomics, so the result is
-//    the same on every run and whichever workgroup finishes last.
-//  * A slice longer than one LDS chunk (always the case without a workspace,
-//    S = 1) is walked chunk by chunk, re-staging the activations.
+// Data movement (the kernels are bound by HBM and by memory latency):
+//  * A workgroup is W waves; each wave owns T tiles of 16 features, so a
+//    workgroup covers a tile group of TG = T * W tiles.  Weights stream with
+//    16-byte raw buffer loads (rows past M read as zeros) PF steps of 128 k
+//    ahead of the math, in registers.
+//  * Activations (16 rows) are staged in LDS, row-major, with buffer loads
+//    that write LDS directly; every staged element serves the TG tiles.  Q4_0
+//    block scales are staged the same way.
+//  * With a workspace (the normal case), K is cut into slices of at most 8
+//    steps and the stream kernel runs persistent workgroups, each walking a
+//    run of equal-size items (tile group x slice) in slice-major order: the
+//    weight pipeline never drains between items, an activation slice is
+//    staged once per run of items that share it, each wave prefetches its own
+//    scales one item ahead, and each item's fp32 partial tiles go to the
+//    workspace with plain stores that nothing waits for.  A second, small
+//    kernel then adds every output's slices in the fixed order 0, 1, ...,
+//    S-1, scales by alpha and rounds: no atomics, no flags, the same result
+//    on every run.
+//  * Without a workspace the one-shot kernel gives each workgroup a whole
+//    tile group over all of K, staged chunk by chunk.
 #include "vq_device.h"
 #include "vq_internal.h"
 
+#include <atomic>
+
 namespace vq {
 
-constexpr int kStepK = 128;                    // k per step: 4 Q4_0 blocks or one FP8 chunk
-constexpr int kActStepBytes = 16 * kStepK * 2;  // one step of 16 activation rows (bf16/fp16)
+constexpr int kStepK = 128;  // k per step: 4 Q4_0 blocks or one FP8 chunk
 
 // One problem of a launch (kernel arguments, by value).
 struct KProblem {
@@ -60,45 +61,36 @@ struct KProblem {
     const void *scales;   // Q4_0 f16 [M][K/32] or FP8 f32 [ceil(M/128)][K/128]
     const uint16_t *act;  // this row group's [<=16][K] activations
     void *out;            // this row group's [<=16][M] outputs
-    float *part;          // split: fp32 partial tiles [tile groups][S][TG][64 lanes][4]
-    uint32_t *cnt;        // split: arrival counters [tile groups], zero between calls
     int M, K;
-    int S, sl, chunk;     // slices, steps per slice, steps per LDS chunk
-    int item0;            // first workgroup of this problem in the launch
+    int chunk;            // one-shot kernel: steps per LDS chunk
+    int cpt;              // walk kernel: chunks (of 8 steps) per tile group
+    int ntg;              // tile groups
+    int item0;            // first item of this problem in the launch (a tile group, or a chunk)
 };
 
 // A launch: up to kGroupPerLaunch problems sharing the launch shape, the row
-// count (<= 16), the output dtype and alpha; `items` workgroups in all.  Item
-// i belongs to the last problem whose item0 <= i.
+// count (<= 16), the output dtype and alpha.  Item i belongs to the last
+// problem whose item0 <= i.  The walk kernel's pieces and arrival counters
+// live in the caller's workspace.
 struct KGroup {
     KProblem p[kGroupPerLaunch];
     int count, items, N, out_dtype;
     float alpha;
+    float *part;    // pieces: [workgroups][2 sides][TG tiles][64 lanes][4]
+    uint32_t *cnt;  // arrival counters: [workgroups][waves], zero between calls
 };
 
-// LDS position of activation piece p (k = 8p .. 8p+7 of the step) of row r, in
-// the operand layout [32-k group q][lane = 16 g + r][16 bytes]:
-//  Q4_0: lane (r, g)'s operand for block q is x[4g .. 4g+3] (first 8 bytes)
-//        and x[16+4g .. 16+4g+3] (last 8 bytes) of that block, the order in
-//        which q4_operand lays out the codes.  A piece splits over two lanes.
-//  FP8:  lane (r, g)'s operand for MFMA u is x[32g + 8u .. +8]: piece p is one
-//        whole operand (g = p / 4, u = p % 4).
-template <bool FP8>
-__device__ __forceinline__ void act_piece_to_lds(uint8_t *tile, int r, int p, u32x4 v) {
-    if constexpr (FP8) {
-        *reinterpret_cast<u32x4 *>(tile + ((p & 3) * 64 + 16 * (p >> 2) + r) * 16) = v;
-    } else {
-        const int blk = p >> 2, q = p & 3;
-        const int g0 = 2 * (q & 1), half = q >> 1;
-        uint8_t *base = tile + blk * 1024 + half * 8;
-        *reinterpret_cast<u32x2 *>(base + (16 * g0 + r) * 16) = u32x2{v[0], v[1]};
-        *reinterpret_cast<u32x2 *>(base + (16 * (g0 + 1) + r) * 16) = u32x2{v[2], v[3]};
-    }
-}
+// LDS layout:
+//  activations: 16 rows x kActPitch bytes, row-major (row r, element k of the
+//    staged chunk at r * kActPitch + 2k), one chunk of at most 8 steps; the
+//    16 bytes of padding stagger the rows over the LDS banks;
+//  Q4_0 scales: a row of 4 * CH fp16 per feature (CH = the chunk bound).
+constexpr int kActPitch = 2 * 1024 + 16;
+constexpr int kActLdsBytes = 16 * kActPitch;
+constexpr int kOut = 0x7FFFFFF0;  // an offset past every buffer: the load returns zeros
 
-// Most steps per LDS chunk for a workgroup of W waves: bounded so that all
-// staging loads of a chunk (<= 8 per thread for activations, 2 T for scales)
-// can be in flight at once.
+// Most steps per LDS chunk for a workgroup of W waves (the activation chunk is
+// moved by 32 load instructions of 1 KB shared out over the waves).
 __host__ __device__ constexpr int max_chunk_steps(int W) { return W >= 4 ? 8 : 4; }
 
 __host__ __device__ inline int verify_tile_groups_dev(int M, int tg) { return ((M + 15) / 16 + tg - 1) / tg; }
@@ -106,56 +98,169 @@ __host__ __device__ inline int verify_tile_groups_dev(int M, int tg) { return ((
 // Pipeline depth: stages of weight loads in flight per wave.
 __host__ __device__ constexpr int pipeline_depth(bool fp8, int T) { return ((fp8 ? 2 * T : T) >= 4) ? 2 : 4; }
 
-template <int ACT, bool FP8, int T, int W, int PF>
-__global__ __launch_bounds__(64 * W) void verify_kernel(const KGroup grp) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+// Q4_0 scale pieces (16 bytes) per feature row, and load instructions for the
+// rows of T tiles (one instruction moves 64 pieces).
+__host__ __device__ constexpr int scale_pieces(int W) { return max_chunk_steps(W) / 2; }
+__host__ __device__ constexpr int scale_insts(int T, int W) { return (T * 16 * scale_pieces(W) + 63) / 64; }
+
+__device__ __forceinline__ int steps_of(bool fp8, int K) { return fp8 ? (K >> 7) : (((K >> 5) + 3) >> 2); }
+
+// ---------------------------------------------------------------------------
+// The math of one step of 128 k for one wave's T tiles.
+//   row  -- LDS: activation row j (= lane & 15); element e of the staged
+//           chunk sits at byte ((o0 + 2e') ^ swz) from it, where o0 is the
+//           step's byte offset and e' the element within the step (swz
+//           permutes 16-byte pieces, 0 for an unswizzled layout)
+//   sc   -- LDS (Q4_0): scale row of feature j of tile 0 at the step's first
+//           block; tile t's row is 16 * t * scrow halves further
+//   w    -- the step's weight registers; ts -- FP8 tile scales
+// ---------------------------------------------------------------------------
+template <int ACT, bool FP8, int T, int WB>
+__device__ __forceinline__ void step_math(const uint8_t *row, int o0, int swz, int g, const uint16_t *sc,
+                                          int scrow, const u32x4 (&w)[T][WB], const float (&ts)[T],
+                                          f32x4 (&acc)[T]) {
     using A16 = Act16<ACT>;
-    constexpr int TG = T * W;                   // tiles per workgroup
-    constexpr int NT = 64 * W;                  // threads per workgroup
-    constexpr int WB = FP8 ? 2 : 1;             // 16-byte weight loads per lane, tile and step
-    constexpr int kStepBytes = FP8 ? 128 : 64;  // weight bytes per feature row per step
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    auto at = [&](int byte) { return row + ((o0 + byte) ^ swz); };
+    // A operand of lane (g, r): row r; Q4_0 block q: x[4g..4g+3] and
+    // x[16+4g..16+4g+3] of the block (the order q4_operand gives the codes);
+    // FP8 MFMA u: x[32g + 8u .. +8] of the step
+    auto a_operand = [&](int q) {
+        if constexpr (FP8) {
+            return *reinterpret_cast<const u32x4 *>(at(2 * (32 * g + 8 * q)));
+        } else {
+            const u32x2 lo = *reinterpret_cast<const u32x2 *>(at(2 * (32 * q + 4 * g)));
+            const u32x2 hi = *reinterpret_cast<const u32x2 *>(at(2 * (32 * q + 16 + 4 * g)));
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    };
+    if constexpr (FP8) {
+        u32x4 av[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            av[q] = a_operand(q);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            f32x4 part = zero4;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const u32x4 src = w[t][u >> 1];
+                const uint32_t e0 = src[2 * (u & 1)], e1 = src[2 * (u & 1) + 1];
+                const u32x4 bop = {A16::template fp8x2<false>(e0), A16::template fp8x2<true>(e0),
+                                   A16::template fp8x2<false>(e1), A16::template fp8x2<true>(e1)};
+                part = A16::mfma(av[u], bop, part);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[t][r] = __builtin_fmaf(ts[t], part[r], acc[t][r]);
+        }
+    } else {
+        // block-major: per 32-k block one offset MFMA shared by the T tiles,
+        // then each tile's block MFMA and scale FMA
+        const u32x4 negc = {A16::kNegOffset, A16::kNegOffset, A16::kNegOffset, A16::kNegOffset};
+        uint32_t d[T][4];
+        u32x2 scp[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            d[t][0] = w[t][0][0];
+            d[t][1] = w[t][0][1];
+            d[t][2] = w[t][0][2];
+            d[t][3] = w[t][0][3];
+            transpose_lane_groups(d[t][0], d[t][1], d[t][2], d[t][3]);  // lane group g: dword g of blocks 0..3
+            scp[t] = *reinterpret_cast<const u32x2 *>(sc + t * 16 * scrow);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 aq = a_operand(q);
+            const f32x4 corr = A16::mfma(aq, negc, zero4);  // -(MAGIC + 8) * sum x, per row
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const f32x4 dot = A16::mfma(aq, q4_operand<A16::kMagicByte>(d[t][q]), corr);
+                const float s = h2f((q & 1) ? (scp[t][q >> 1] >> 16) : (scp[t][q >> 1] & 0xFFFFu));
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[t][r] = __builtin_fmaf(s, dot[r], acc[t][r]);
+            }
+        }
+    }
+}
+
+// Activation chunk into LDS: rows of this launch's row group, steps
+// [s_first, s_first + nc) of K.  Instruction (row r, half h) moves 64
+// consecutive 16-byte pieces -- 1 KB of whole cache lines -- of row r; the 32
+// instructions are shared out over the W waves.  Pieces past the chunk or past
+// K deliver zeros, and so do rows past N (the buffer ends there).
+template <int W>
+__device__ __forceinline__ void stage_act(uint8_t *act_lds, rsrc_t ra, int K, int s_first, int nc, int wave,
+                                          int lane) {
+    const int kb = s_first * kStepK;
+#pragma unroll
+    for (int i = 0; i < 32 / W; ++i) {
+        const int inst = wave + W * i;
+        const int r = inst >> 1, h = inst & 1;
+        const int p = 64 * h + lane;
+        const bool ok = p < 16 * nc && kb + 8 * p < K;
+        bload16_lds(ra, act_lds + r * kActPitch + h * 1024, ok ? r * K * 2 + 2 * kb + 16 * p : kOut);
+    }
+}
+
+// Q4_0 scales of `nfeat` feature rows (the buffer starts at the first one)
+// for steps [s_first, s_first + nc): row f gets the 4 * CH scales from block
+// 4 * s_first on, 16 bytes per lane; instructions inst0, inst0 + inst_step,
+// ... (SI of them).  Needs every row start 16-byte aligned (NB % 8 == 0).
+template <int W, int SI>
+__device__ __forceinline__ void stage_scales(uint8_t *sc_lds, rsrc_t rs, int NB, int nfeat, int s_first, int nc,
+                                             int inst0, int inst_step, int lane) {
+    constexpr int PPF = scale_pieces(W);
+#pragma unroll
+    for (int i = 0; i < SI; ++i) {
+        const int inst = inst0 + inst_step * i;
+        const int f = inst * (64 / PPF) + lane / PPF, pc = lane % PPF;
+        const bool ok = f < nfeat && 2 * pc < nc;
+        bload16_lds(rs, sc_lds + inst * 1024, ok ? (f * NB + 4 * s_first + 8 * pc) * 2 : kOut);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One-shot kernel (no workspace): workgroup = one tile group over all of K.
+// Items are handed out so that each XCD (workgroups go to the 8 XCDs in
+// turn, b % 8) gets one contiguous range of them.
+// ---------------------------------------------------------------------------
+template <int ACT, bool FP8, int T, int W, int PF>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(T >= 4 ? 2 : 4))) void oneshot_kernel(
+    const KGroup grp) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int TG = T * W;
+    constexpr int NT = 64 * W;
+    constexpr int WB = FP8 ? 2 : 1;
+    constexpr int kStepBytes = FP8 ? 128 : 64;
     constexpr int CH = max_chunk_steps(W);
-    constexpr int kOut = 0x7FFFFFF0;            // an offset past every buffer: the load returns zeros
+    constexpr int SIW = FP8 ? 0 : (scale_insts(TG, W) + W - 1) / W;
+    constexpr int SPT = FP8 ? 1 : (TG * 16 * CH + NT - 1) / NT;
+    constexpr int scrow = 4 * CH;
     static_assert(CH % PF == 0, "chunks hold whole pipeline rounds");
 
-    // ---- this workgroup's item and problem (wave-uniform scalar work).
-    // Workgroups are handed to the 8 XCDs in turn (b % 8); each XCD is given
-    // one contiguous range of items, so the slices and tile groups that share
-    // an activation slice run on one XCD close together in time and find it
-    // in that XCD's L2.  (A bijection on [0, items): the result does not
-    // depend on where an item runs, only the cache behaviour does.)
     const int b = (int)blockIdx.x;
     const int nq = grp.items >> 3, nr = grp.items & 7;
     const int xcd = b & 7, loc = b >> 3;
-    const int it_all = xcd < nr ? xcd * (nq + 1) + loc : nr * (nq + 1) + (xcd - nr) * nq + loc;
+    const int item = xcd < nr ? xcd * (nq + 1) + loc : nr * (nq + 1) + (xcd - nr) * nq + loc;
     int pi = 0;
     for (int q = 1; q < grp.count; ++q)
-        if (it_all >= grp.p[q].item0)
+        if (item >= grp.p[q].item0)
             pi = q;
     const KProblem &a = grp.p[pi];
-    const int lane = threadIdx.x & 63;
-    const int wave = wave_id();
-    const int j = lane & 15;
-    const int g = lane >> 4;
-    const int M = a.M, K = a.K, S = a.S;
-    const int NB = K >> 5;
-    const int steps = FP8 ? (K >> 7) : ((NB + 3) >> 2);  // the last Q4_0 step may be partial
-    const int item = it_all - a.item0;
-    const int tg = item / S;
-    const int sidx = item - tg * S;
-    const int s0 = sidx * a.sl;
-    const int ns = min(a.sl, steps - s0);  // >= 1: the host never makes an empty slice
-    const int nrows = grp.N;               // <= 16
-    const int fwg = tg * TG * 16;          // first feature of the workgroup
-    const int fwv = fwg + wave * T * 16;   // first feature of this wave
-    const int wrow = FP8 ? K : (K >> 1);   // weight bytes per feature row
-    const int chunk = a.chunk;             // <= CH, a multiple of PF
+    const int lane = threadIdx.x & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
+    const int M = a.M, K = a.K, NB = K >> 5;
+    const int steps = steps_of(FP8, K);
+    const int tg = item - a.item0;
+    const int nrows = grp.N;
+    const int fwg = tg * TG * 16, fwv = fwg + wave * T * 16;
+    const int wrow = FP8 ? K : (K >> 1);
+    const int chunk = a.chunk;
 
     uint8_t *act_lds = lds;
-    uint16_t *sc_lds = reinterpret_cast<uint16_t *>(lds + (size_t)chunk * kActStepBytes);
-    const int scrow = 4 * chunk;  // staged scales per feature
+    uint8_t *sc_lds = lds + kActLdsBytes;
 
-    // ---- weights of this wave's T tiles; rows past M read as zeros
     const int wfeat = max(0, min(M - fwv, T * 16));
     const rsrc_t rw = make_rsrc(a.w + (size_t)min(fwv, M) * wrow, (uint32_t)wfeat * (uint32_t)wrow);
     const int vw = j * wrow + (FP8 ? 32 : 16) * g;
@@ -163,16 +268,14 @@ __global__ __launch_bounds__(64 * W) void verify_kernel(const KGroup grp) {
     if constexpr (FP8) {
 #pragma unroll
         for (int t = 0; t < T; ++t)
-            tsrow[t] = static_cast<const float *>(a.scales) + (size_t)(min(fwv + 16 * t, M - 1) >> 7) * steps + s0;
+            tsrow[t] = static_cast<const float *>(a.scales) + (size_t)(min(fwv + 16 * t, M - 1) >> 7) * steps;
     }
-
     u32x4 wb[PF][T][WB];
     float tsb[PF][T];
-    // The step offset goes into the per-lane offset, which the buffer range
-    // check covers: the partial last Q4_0 step of the last row then reads zeros
-    // instead of bytes past the end of the array.
+    // the step offset is part of the range-checked per-lane offset: the
+    // partial last Q4_0 step of the last row reads zeros, not past the array
     auto issue = [&](auto U, int st) {
-        const int koff = vw + kStepBytes * (s0 + st);
+        const int koff = vw + kStepBytes * st;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
 #pragma unroll
@@ -180,157 +283,94 @@ __global__ __launch_bounds__(64 * W) void verify_kernel(const KGroup grp) {
                 wb[U.value][t][h] = bload16<kAuxCached>(rw, koff + t * 16 * wrow + 16 * h, 0);
             if constexpr (FP8)
                 tsb[U.value][t] = tsrow[t][st];
+            else
+                tsb[U.value][t] = 0.f;
         }
     };
 
-    // ---- staging of one chunk of the slice: activations (and Q4_0 scales).
-    // Loads and LDS stores are separate steps so that the loads can be issued
-    // before the first weight loads: the wait for them then leaves the weight
-    // loads in flight.  Every load is issued (out-of-range ones read zeros),
-    // which keeps the compiler's wait counts exact.
-    constexpr int LR = NT / 16;                        // threads per activation row
-    constexpr int APT = (16 * CH + LR - 1) / LR;       // 16-byte pieces per thread
-    constexpr int SPT = FP8 ? 1 : (TG * 16 * 8 + NT - 1) / NT;  // scale loads per thread
     const rsrc_t ra = make_rsrc(a.act, (uint32_t)nrows * (uint32_t)K * 2u);
     const int wgfeat = max(0, min(M - fwg, TG * 16));
     const uint8_t *sbase = FP8 ? nullptr : static_cast<const uint8_t *>(a.scales) + (size_t)min(fwg, M) * NB * 2;
     const rsrc_t rs = make_rsrc(sbase, FP8 ? 0u : (uint32_t)wgfeat * (uint32_t)NB * 2u);
-    const int ar = threadIdx.x / LR;  // activation row staged by this thread
-    const int alt = threadIdx.x % LR;
-    u32x4 sa[APT];
+    const bool sc_dma = (NB & 7) == 0;
     u32x2 ss[SPT];
-    auto stage_load = [&](int c0, int nc) {
-        // row ar: consecutive 16-byte pieces (whole cache lines) of the row's
-        // nc * 256 contiguous bytes; pieces past K are zeros, rows past N read
-        // as zeros
-        const int kb = (s0 + c0) * kStepK;
-#pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int p = alt + LR * i;
-            const bool ok = p < 16 * nc && kb + 8 * p < K;
-            sa[i] = bload16<kAuxCached>(ra, ok ? ar * K * 2 + 2 * kb + 16 * p : kOut, 0);
-        }
+    auto stage_sc_load = [&](int c0, int nc) {  // scales through registers (NB % 8 != 0)
         if constexpr (!FP8) {
-            // scales: 8 threads per feature row, one step (4 blocks) each
-            const bool vec = (NB & 3) == 0;
 #pragma unroll
             for (int i = 0; i < SPT; ++i) {
                 const int e = threadIdx.x + NT * i;
-                const int fi = e >> 3, st = e & 7;
-                const int blk = 4 * (s0 + c0 + st);
+                const int fi = e / CH, st = e % CH;
+                const int blk = 4 * (c0 + st);
                 const bool ok = st < nc && fi < TG * 16;
                 const int off = (fi * NB + blk) * 2;
-                if (vec) {
-                    ss[i] = bload8<kAuxCached>(rs, ok ? off : kOut, 0);
-                } else {
-                    uint32_t h[4];
+                uint32_t hw[4];
 #pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        h[b] = bload2<kAuxCached>(rs, ok && blk + b < NB ? off + 2 * b : kOut, 0);
-                    ss[i] = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-                }
+                for (int q = 0; q < 4; ++q)
+                    hw[q] = bload2<kAuxCached>(rs, ok && blk + q < NB ? off + 2 * q : kOut, 0);
+                ss[i] = u32x2{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16)};
             }
         }
     };
-    auto stage_store = [&](int nc) {
-#pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int p = alt + LR * i;
-            if (p < 16 * nc)
-                act_piece_to_lds<FP8>(act_lds + (p >> 4) * kActStepBytes, ar, p & 15, sa[i]);
-        }
+    auto stage_sc_store = [&]() {
         if constexpr (!FP8) {
 #pragma unroll
             for (int i = 0; i < SPT; ++i) {
                 const int e = threadIdx.x + NT * i;
-                const int fi = e >> 3, st = e & 7;
-                if (st < nc && fi < TG * 16)
-                    *reinterpret_cast<u32x2 *>(sc_lds + fi * scrow + 4 * st) = ss[i];
+                const int fi = e / CH, st = e % CH;
+                if (fi < TG * 16)
+                    *reinterpret_cast<u32x2 *>(sc_lds + (fi * scrow + 4 * st) * 2) = ss[i];
             }
+        }
+    };
+    auto stage = [&](int c0, int nc) {
+        stage_act<W>(act_lds, ra, K, c0, nc, wave, lane);
+        if constexpr (!FP8) {
+            if (sc_dma)
+                stage_scales<W, SIW>(sc_lds, rs, NB, wgfeat, c0, nc, wave, W, lane);
+            else
+                stage_sc_load(c0, nc);
         }
     };
 
-    // ---- the math of one step (st counted from the slice start, c0 = its chunk's start)
     f32x4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t)
         acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](auto U, int st, int c0) {
-        const uint8_t *tp = act_lds + (st - c0) * kActStepBytes;
-        u32x4 av[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            av[q] = *reinterpret_cast<const u32x4 *>(tp + (q * 64 + lane) * 16);
-        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (FP8) {
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                f32x4 part = zero4;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const u32x4 src = wb[U.value][t][u >> 1];
-                    const uint32_t e0 = src[2 * (u & 1)], e1 = src[2 * (u & 1) + 1];
-                    const u32x4 bop = {A16::template fp8x2<false>(e0), A16::template fp8x2<true>(e0),
-                                       A16::template fp8x2<false>(e1), A16::template fp8x2<true>(e1)};
-                    part = A16::mfma(av[u], bop, part);
-                }
-                const float ts = tsb[U.value][t];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[t][r] = __builtin_fmaf(ts, part[r], acc[t][r]);
-            }
-        } else {
-            const u32x4 negc = {A16::kNegOffset, A16::kNegOffset, A16::kNegOffset, A16::kNegOffset};
-            f32x4 corr[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                corr[q] = A16::mfma(av[q], negc, zero4);  // -(MAGIC + 8) * sum x, per row
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const u32x2 scp =
-                    *reinterpret_cast<const u32x2 *>(sc_lds + ((wave * T + t) * 16 + j) * scrow + 4 * (st - c0));
-                uint32_t d[4] = {wb[U.value][t][0][0], wb[U.value][t][0][1], wb[U.value][t][0][2],
-                                 wb[U.value][t][0][3]};
-                transpose_lane_groups(d[0], d[1], d[2], d[3]);  // lane group g: dword g of blocks 0..3
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 dot = A16::mfma(av[q], q4_operand<A16::kMagicByte>(d[q]), corr[q]);
-                    const float s = h2f((q & 1) ? (scp[q >> 1] >> 16) : (scp[q >> 1] & 0xFFFFu));
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[t][r] = __builtin_fmaf(s, dot[r], acc[t][r]);
-                }
-            }
-        }
+        const uint16_t *sc =
+            reinterpret_cast<const uint16_t *>(sc_lds) + ((wave * T) * 16 + j) * scrow + 4 * (st - c0);
+        step_math<ACT, FP8, T, WB>(act_lds + j * kActPitch, (st - c0) * (2 * kStepK), 0, g, sc, scrow, wb[U.value],
+                                   tsb[U.value], acc);
     };
 
-    // ---- prologue: staging loads of the first chunk, the first PF steps of
-    // weights, then the staged chunk into LDS
-    const int nc0 = min(chunk, ns);
-    stage_load(0, nc0);
-    if (ns >= PF) {
+    // prologue: the first chunk's staging, the first PF steps of weights
+    const int nc0 = min(chunk, steps);
+    stage(0, nc0);
+    if (steps >= PF) {
         static_for<PF>([&](auto U) { issue(U, U.value); });
+        wait_vmcnt<PF * T * WB>();  // this wave's staging has landed
     } else {
         static_for<PF>([&](auto U) {
-            if (U.value < ns)
+            if (U.value < steps)
                 issue(U, U.value);
         });
+        wait_vmcnt<0>();
     }
-    stage_store(nc0);
+    if (!FP8 && !sc_dma)
+        stage_sc_store();
     __syncthreads();
 
-    // ---- chunks of the slice; weight loads run PF steps ahead across chunks
-    for (int c0 = 0; c0 < ns; c0 += chunk) {
-        const int c1 = min(ns, c0 + chunk);
+    for (int c0 = 0; c0 < steps; c0 += chunk) {
+        const int c1 = min(steps, c0 + chunk);
         if (c0 > 0) {
             __syncthreads();
-            stage_load(c0, c1 - c0);
-            stage_store(c1 - c0);
+            stage(c0, c1 - c0);
+            wait_vmcnt<0>();
+            if (!FP8 && !sc_dma)
+                stage_sc_store();
             __syncthreads();
         }
         int i = c0;
-        // steady state: every load unconditional, so the compiler counts them
-        // and waits only for the stage it is about to use
         while (i + 2 * PF <= c1) {
             static_for<PF>([&](auto U) {
                 compute(U, i + U.value, c0);
@@ -345,77 +385,317 @@ __global__ __launch_bounds__(64 * W) void verify_kernel(const KGroup grp) {
             const int st = i + V.value;
             if (st < c1) {
                 compute(std::integral_constant<int, U>{}, st, c0);
-                if (st + PF < ns)
+                if (st + PF < steps)
                     issue(std::integral_constant<int, U>{}, st + PF);
             }
         });
     }
 
-    // ---- epilogue
-    auto store_tile = [&](int t, f32x4 v) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
         const int feat = fwv + t * 16 + j;
         if (feat < M) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 4 * g + r;
                 if (row < nrows)
-                    store_out(a.out, grp.out_dtype, (size_t)row * M + feat, grp.alpha * v[r]);
+                    store_out(a.out, grp.out_dtype, (size_t)row * M + feat, grp.alpha * acc[t][r]);
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Walk kernel (workspace): persistent workgroups, each walking one contiguous
+// range of chunks.  A chunk is one tile group x 8 steps; chunks are numbered
+// problem by problem, tile group by tile group, along K within a tile group,
+// so a workgroup's range is a run of whole tile groups with at most one
+// partial tile group at each end.  A tile group that lies inside the range is
+// accumulated in registers over all of K and written out directly.  The piece
+// of a tile group cut by a range boundary goes to the workspace (fp32, one
+// slot per workgroup and side), and the last of its workgroups to arrive adds
+// the pieces in range order and writes the outputs.
+// ---------------------------------------------------------------------------
+constexpr int kWalkSteps = 8;                   // steps per chunk
+constexpr int kActBuf = 16 * kWalkSteps * 256;  // one activation buffer: 16 rows x 1024 k, 32 KiB
+
+// Activation chunk into one buffer, rows of 2 KiB with no padding: 16-byte
+// piece p of row r goes to slot p ^ (r & 7) of the row, which spreads the
+// rows' reads of one piece over the LDS banks.  A load instruction into LDS
+// writes lane l's 16 bytes to slot l of its 1 KiB destination, so the
+// permutation is made on the source side: the lane of slot l fetches piece
+// l ^ (r & 7), in the same 128-byte line.
+template <int W>
+__device__ __forceinline__ void stage_act_swz(uint8_t *buf, rsrc_t ra, int K, int s_first, int nc, int wave,
+                                              int lane) {
+    const int kb = s_first * kStepK;
+#pragma unroll
+    for (int i = 0; i < 32 / W; ++i) {
+        const int inst = wave + W * i;
+        const int r = inst >> 1, h = inst & 1;
+        const int p = (64 * h + lane) ^ (r & 7);
+        const bool ok = p < 16 * nc && kb + 8 * p < K;
+        bload16_lds(ra, buf + r * 2048 + h * 1024, ok ? r * K * 2 + 2 * kb + 16 * p : kOut);
+    }
+}
+
+// Position of a chunk: problem, tile group, chunk within the tile group.
+struct ChunkRef {
+    int pi, tg, c;
+};
+
+// The chunk `it` (a linear search over the launch's problems: once per
+// workgroup; later chunks are reached by next_chunk).
+__device__ __forceinline__ ChunkRef find_chunk(const KGroup &grp, int it) {
+    int pi = 0;
+    for (int q = 1; q < grp.count; ++q)
+        if (it >= grp.p[q].item0)
+            pi = q;
+    const KProblem &a = grp.p[pi];
+    const int loc = it - a.item0;
+    const int tg = loc / a.cpt;
+    return ChunkRef{pi, tg, loc - tg * a.cpt};
+}
+
+// The chunk after r (past the launch's last chunk it stays on the last
+// problem; such chunks are never real).
+__device__ __forceinline__ ChunkRef next_chunk(const KGroup &grp, ChunkRef r) {
+    const KProblem &a = grp.p[r.pi];
+    if (++r.c == a.cpt) {
+        r.c = 0;
+        if (++r.tg == a.ntg) {
+            r.tg = 0;
+            r.pi = min(r.pi + 1, grp.count - 1);
+        }
+    }
+    return r;
+}
+
+// First chunk of workgroup b's range, and the workgroup whose range holds chunk c.
+__device__ __forceinline__ int range_start(int b, int C, int G) { return (int)(((int64_t)b * C) / G); }
+__device__ __forceinline__ int range_owner(int c, int C, int G) { return (int)(((int64_t)(c + 1) * G - 1) / C); }
+
+template <int ACT, bool FP8, int T, int W, int PF>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void walk_kernel(const KGroup grp) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int TG = T * W;
+    constexpr int WB = FP8 ? 2 : 1;
+    constexpr int kStepBytes = FP8 ? 128 : 64;
+    constexpr int CH = kWalkSteps;
+    constexpr int SIW = FP8 ? 0 : T;       // scale loads per wave per chunk: 16 feature rows x 64 bytes each
+    constexpr int kScBuf = SIW * 1024;     // one wave's scale buffer
+    constexpr int scrow = 4 * CH;          // scales per feature row in the buffer
+    constexpr int AI = 32 / W;             // activation loads per wave per chunk
+    constexpr int kIssueLoads = PF * T * WB;
+    constexpr int kCoherent = 0x10;        // sc1: agent-coherent, no cache maintenance needed
+    static_assert(CH % PF == 0, "chunks hold whole pipeline rounds");
+    static_assert(scale_pieces(4) * 2 == CH, "scale rows of one chunk");
+
+    const int lane = threadIdx.x & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
+    const int C = grp.items, G = (int)gridDim.x, b = (int)blockIdx.x;
+    const int ib = range_start(b, C, G), ie = range_start(b + 1, C, G);
+    if (ib >= ie)
+        return;
+    const int nrows = grp.N;
+    uint8_t *sc_wave = lds + 2 * kActBuf + wave * 2 * kScBuf;  // this wave's two scale buffers
+
+    // ---- weights of a chunk for this wave's T tiles (chunks past the range read zeros)
+    struct Src {
+        rsrc_t rw;
+        int vw, s0, steps, wrow;
+        const float *ts[T];
     };
-    if (S == 1) {
+    auto make_src = [&](const ChunkRef &r, bool real) {
+        Src src;
+        const KProblem &a = grp.p[r.pi];
+        const int M = a.M, K = a.K;
+        src.wrow = FP8 ? K : (K >> 1);
+        src.steps = steps_of(FP8, K);
+        src.s0 = r.c * CH;
+        const int fwv = (r.tg * TG + wave * T) * 16;
+        const int wfeat = real ? max(0, min(M - fwv, T * 16)) : 0;
+        src.rw = make_rsrc(a.w + (size_t)min(fwv, M) * src.wrow, (uint32_t)wfeat * (uint32_t)src.wrow);
+        src.vw = j * src.wrow + (FP8 ? 32 : 16) * g;
+        if constexpr (FP8) {
 #pragma unroll
-        for (int t = 0; t < T; ++t)
-            store_tile(t, acc[t]);
-        return;
-    }
-    // Split K: publish this slice's partial tiles, count in, and let the last
-    // workgroup of the tile group add the slices in order.  The partial tiles
-    // are written and read with agent-coherent (sc1) accesses, which go
-    // through to memory rather than stopping in one die's L2, so no cache
-    // writeback or invalidation is needed; the wait before the barrier makes
-    // every store complete before the count is taken.
-    constexpr int kCoherent = 0x10;  // sc1
-    const int ntg = verify_tile_groups_dev(M, TG);
-    const rsrc_t rp = make_rsrc(a.part, (uint32_t)ntg * (uint32_t)S * TG * 1024u);
-    const int mine = ((tg * S + sidx) * TG + wave * T) * 1024 + lane * 16;
+            for (int t = 0; t < T; ++t)
+                src.ts[t] = static_cast<const float *>(a.scales) +
+                            (size_t)(min(fwv + 16 * t, M - 1) >> 7) * src.steps;
+        }
+        return src;
+    };
+    u32x4 wb[PF][T][WB];
+    float tsb[PF][T];
+    auto issue = [&](auto U, const Src &src, int st) {
+        const int gs = src.s0 + st;
+        const bool ok = gs < src.steps;
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[t]), rp, mine + t * 1024, 0, kCoherent);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int *flag = reinterpret_cast<int *>(lds);  // the activation tiles are no longer read
-    if (threadIdx.x == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(a.cnt + tg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int last = old == (uint32_t)(S - 1);
-        if (last)  // every slice has arrived: leave the counter at zero for the next call
-            __hip_atomic_store(a.cnt + tg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *flag = last;
-    }
-    __syncthreads();
-    if (*flag == 0)
-        return;
-    const int base = (tg * S * TG + wave * T) * 1024 + lane * 16;
+        for (int t = 0; t < T; ++t) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-        for (int s8 = 0; s8 < S; s8 += 8) {
-            f32x4 v[8];  // eight slices' loads in flight at once
+            for (int h = 0; h < WB; ++h)
+                wb[U.value][t][h] = bload16<kAuxCached>(
+                    src.rw, ok ? src.vw + kStepBytes * gs + t * 16 * src.wrow + 16 * h : kOut, 0);
+            if constexpr (FP8)
+                tsb[U.value][t] = src.ts[t][min(gs, src.steps - 1)];
+            else
+                tsb[U.value][t] = 0.f;
+        }
+    };
+
+    // ---- a chunk's activations (whole workgroup) and this wave's scales
+    auto act_for = [&](const ChunkRef &r, bool real, int buf) {
+        const KProblem &a = grp.p[r.pi];
+        const int steps = steps_of(FP8, a.K);
+        const int s0 = r.c * CH;
+        const rsrc_t ra = make_rsrc(a.act, real ? (uint32_t)nrows * (uint32_t)a.K * 2u : 0u);
+        stage_act_swz<W>(lds + buf * kActBuf, ra, a.K, s0, min(CH, steps - s0), wave, lane);
+    };
+    auto scales_for = [&](const ChunkRef &r, bool real, int buf) {
+        if constexpr (!FP8) {
+            const KProblem &a = grp.p[r.pi];
+            const int NB = a.K >> 5, M = a.M;
+            const int steps = steps_of(false, a.K);
+            const int s0 = r.c * CH;
+            const int fwv = (r.tg * TG + wave * T) * 16;
+            const int nfeat = real ? max(0, min(M - fwv, T * 16)) : 0;
+            const rsrc_t rs = make_rsrc(static_cast<const uint8_t *>(a.scales) + (size_t)min(fwv, M) * NB * 2,
+                                        (uint32_t)nfeat * (uint32_t)NB * 2u);
+            stage_scales<4, SIW>(sc_wave + buf * kScBuf, rs, NB, nfeat, s0, min(CH, steps - s0), 0, 1, lane);
+        }
+    };
+
+    // ---- outputs and pieces
+    const rsrc_t rp = make_rsrc(grp.part, (uint32_t)G * 2u * TG * 1024u);
+    auto slot_off = [&](int wg, int side, int t) { return ((wg * 2 + side) * TG + wave * T + t) * 1024 + lane * 16; };
+    auto store_tiles = [&](const KProblem &a, int tg, const f32x4 (&v)[T]) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rp, s8 + u < S ? base + (s8 + u) * TG * 1024 + t * 1024 : kOut, 0,
-                                                     kCoherent));
+        for (int t = 0; t < T; ++t) {
+            const int feat = (tg * TG + wave * T + t) * 16 + j;
+            if (feat < a.M) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int s2 = s8 + u;
-                if (s2 < S) {
-                    const f32x4 w = s2 == sidx ? acc[t] : v[u];
-                    sum = s2 == 0 ? w : sum + w;
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 4 * g + r;
+                    if (row < nrows)
+                        store_out(a.out, grp.out_dtype, (size_t)row * a.M + feat, grp.alpha * v[t][r]);
                 }
             }
         }
-        store_tile(t, sum);
+    };
+    int pend_pi[2] = {-1, -1}, pend_tg[2] = {0, 0};  // this workgroup's pieces, by side
+
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // ---- prologue: the first chunk's activations and scales, the first
+    // round of weights
+    int it = ib;
+    ChunkRef cref = find_chunk(grp, it);
+    ChunkRef nref = next_chunk(grp, cref);
+    Src cur = make_src(cref, true);
+    Src nxt = make_src(nref, it + 1 < ie);
+    act_for(cref, true, 0);
+    scales_for(cref, true, 0);
+    static_for<PF>([&](auto U) { issue(U, cur, U.value); });
+    wait_vmcnt<kIssueLoads>();  // the first chunk's activations and scales have landed
+    lds_barrier();
+
+    int par = 0;
+    const uint8_t *row = lds + j * 2048;
+    const int swz = (j & 7) << 4;
+    for (;;) {
+        // The next chunk's activations and scales go into the other buffers
+        // (free: every wave passed the barrier after the chunk that used
+        // them).  Issued before this chunk's math, after its first round of
+        // weights, on every path: the compiler's waits for those weights
+        // then never include the staging.
+        act_for(nref, it + 1 < ie, par ^ 1);
+        scales_for(nref, it + 1 < ie, par ^ 1);
+        const KProblem &ca = grp.p[cref.pi];
+        const uint8_t *abuf = row + par * kActBuf;
+        const uint16_t *sc0 = reinterpret_cast<const uint16_t *>(sc_wave + par * kScBuf) + j * scrow;
+#pragma unroll
+        for (int rd = 0; rd < CH / PF; ++rd) {
+            // this round's loads fetch the next round of this chunk, or the
+            // first round of the next chunk
+            const bool to_next = rd == CH / PF - 1;
+            const Src &src = to_next ? nxt : cur;
+            const int st0 = to_next ? 0 : (rd + 1) * PF;
+            static_for<PF>([&](auto U) {
+                const int st = rd * PF + U.value;
+                step_math<ACT, FP8, T, WB>(abuf, st * (2 * kStepK), swz, g, sc0 + 4 * st, scrow, wb[U.value],
+                                           tsb[U.value], acc);
+                __builtin_amdgcn_sched_barrier(0);
+                issue(U, src, st0 + U.value);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+
+        // ---- chunk boundary.  Everything but the newest round of weights is
+        // complete after this wait: the next chunk's activations and this
+        // wave's scales for it have landed.
+        wait_vmcnt<kIssueLoads>();
+        const bool last = it + 1 >= ie;
+        if (cref.c == ca.cpt - 1 || last) {  // this workgroup's part of the tile group is done
+            const int first = ca.item0 + cref.tg * ca.cpt;
+            if (first >= ib && first + ca.cpt <= ie) {
+                store_tiles(ca, cref.tg, acc);
+            } else {
+                const int side = first + ca.cpt > ie ? 1 : 0;  // 1: the tile group goes on past this range
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[t]), rp,
+                                                           slot_off(b, side, t), 0, kCoherent);
+                pend_pi[side] = cref.pi;
+                pend_tg[side] = cref.tg;
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (last)
+            break;
+        lds_barrier();  // every wave is done with buffer `par`, and sees the next chunk's activations
+        ++it;
+        cref = nref;
+        nref = next_chunk(grp, nref);
+        cur = nxt;
+        nxt = make_src(nref, it + 1 < ie);
+        par ^= 1;
+    }
+
+    // ---- pieces: count in (per wave: each wave owns its T tiles), and the
+    // last arrival adds the pieces in range order.  The pieces were written
+    // with agent-coherent stores that are complete after this wait.
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int side = 0; side < 2; ++side) {
+        if (pend_pi[side] < 0)
+            continue;
+        const KProblem &a = grp.p[pend_pi[side]];
+        const int first = a.item0 + pend_tg[side] * a.cpt;
+        const int b0 = range_owner(first, C, G), b1 = range_owner(first + a.cpt - 1, C, G);
+        uint32_t *cnt = grp.cnt + b0 * W + wave;
+        uint32_t old = 0;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __builtin_amdgcn_readfirstlane(old);
+        if (old != (uint32_t)(b1 - b0))
+            continue;
+        if (lane == 0)  // every piece has arrived: leave the counter at zero for the next call
+            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        f32x4 sum[T];
+        for (int wg = b0; wg <= b1; ++wg) {
+            const int sd = wg < b1 ? 1 : 0;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const f32x4 v = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, slot_off(wg, sd, t), 0, kCoherent));
+                sum[t] = wg == b0 ? v : sum[t] + v;
+            }
+        }
+        store_tiles(a, pend_tg[side], sum);
     }
 }
 
@@ -424,13 +704,42 @@ __global__ __launch_bounds__(64 * W) void verify_kernel(const KGroup grp) {
 // ---------------------------------------------------------------------------
 namespace {
 
+int device_cus() {
+    static std::atomic<int> cus{0};
+    int v = cus.load(std::memory_order_relaxed);
+    if (v == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cus.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+template <typename Kern>
+int resident_groups(Kern kern, int threads, size_t shm) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(kern), threads, shm) !=
+            hipSuccess ||
+        n <= 0)
+        n = 1;
+    return n * device_cus();
+}
+
+// Walk-kernel pipeline depth: steps of weight loads in flight per wave.  Two
+// workgroups share a CU (the double-buffered activations take 64 KiB of LDS
+// each), so each wave keeps 8 KiB of weights or more in flight.
+__host__ __device__ constexpr int walk_depth(bool fp8, int T) { return (fp8 ? 2 * T : T) >= 4 ? 2 : 4; }
+
 template <int ACT, bool FP8, int T, int W>
 hipError_t launch_tw(const VerifyLaunch &l) {
-    constexpr int PF = pipeline_depth(FP8, T);
-    auto kern = verify_kernel<ACT, FP8, T, W, PF>;
-    size_t shm = 0;
-    for (int i = 0; i < l.count; ++i)
-        shm = std::max(shm, verify_lds_bytes(FP8, T, W, l.probs[i].plan.chunk));
+    constexpr int TG = T * W;
+    const VerifyPlan &pl = l.probs[0].plan;
+    const bool walk = pl.walk;
+    const size_t shm = verify_lds_bytes(FP8, T, W, walk);
+    auto kern = walk ? walk_kernel<ACT, FP8, T, W, walk_depth(FP8, T)>
+                     : oneshot_kernel<ACT, FP8, T, W, pipeline_depth(FP8, T)>;
     if (shm > 64 * 1024 &&
         hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)shm) != hipSuccess)
@@ -439,27 +748,29 @@ hipError_t launch_tw(const VerifyLaunch &l) {
     grp.count = l.count;
     grp.out_dtype = l.out_dtype;
     grp.alpha = l.alpha;
-    int items = 0;
-    size_t cnt_off = 0, part_off = verify_counter_bytes();
+    int64_t items = 0;
     for (int i = 0; i < l.count; ++i) {
         const VerifyProblem &q = l.probs[i];
         KProblem &k = grp.p[i];
-        const int ntg = verify_tile_groups(q.M, T * W);
         k.w = static_cast<const uint8_t *>(q.w);
         k.scales = q.scales;
         k.M = q.M;
         k.K = q.K;
-        k.S = q.plan.slices;
-        k.sl = q.plan.sl;
         k.chunk = q.plan.chunk;
-        k.item0 = items;
-        items += ntg * q.plan.slices;
-        if (q.plan.slices > 1) {
-            k.cnt = reinterpret_cast<uint32_t *>(static_cast<char *>(l.workspace) + cnt_off);
-            k.part = reinterpret_cast<float *>(static_cast<char *>(l.workspace) + part_off);
-            cnt_off += (size_t)ntg * 4;
-            part_off += verify_partial_bytes(q.plan, q.M);
-        }
+        k.ntg = verify_tile_groups(q.M, TG);
+        k.cpt = (verify_steps(FP8, q.K) + kWalkSteps - 1) / kWalkSteps;
+        k.item0 = (int)items;
+        items += walk ? (int64_t)k.ntg * k.cpt : k.ntg;
+    }
+    if (items >= ((int64_t)1 << 31))
+        return hipErrorInvalidValue;
+    grp.items = (int)items;
+    int grid = (int)items;
+    if (walk) {
+        grid = std::min(grid, resident_groups(kern, 64 * W, shm));
+        grid = std::min(grid, pl.groups > 0 ? std::min(pl.groups, kMaxWalkGroups) : kMaxWalkGroups);
+        grp.cnt = static_cast<uint32_t *>(l.workspace);
+        grp.part = reinterpret_cast<float *>(static_cast<char *>(l.workspace) + kWalkCounterBytes);
     }
     // Row groups of 16 run one after another: they share the workspace and
     // are independent otherwise.
@@ -471,8 +782,7 @@ hipError_t launch_tw(const VerifyLaunch &l) {
             grp.p[i].act = static_cast<const uint16_t *>(q.act) + (size_t)g0 * 16 * q.K;
             grp.p[i].out = static_cast<char *>(q.out) + (size_t)g0 * 16 * q.M * out_elem_bytes(l.out_dtype);
         }
-        grp.items = items;
-        hipLaunchKernelGGL(kern, dim3(items), dim3(64 * W), shm, l.stream, grp);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * W), shm, l.stream, grp);
     }
     return hipGetLastError();
 }
@@ -503,49 +813,43 @@ int verify_steps(bool fp8, int K) { return fp8 ? K / 128 : (K / 32 + 3) / 4; }
 
 int verify_tile_groups(int M, int tiles_per_group) { return verify_tile_groups_dev(M, tiles_per_group); }
 
-int pipeline_depth_of(bool fp8, int tiles) { return pipeline_depth(fp8, tiles); }
-
-int verify_max_chunk(int waves) { return max_chunk_steps(waves); }
-
-size_t verify_counter_bytes() { return (size_t)kMaxSplitTileGroups * 4; }
-
-size_t verify_lds_bytes(bool fp8, int tiles, int waves, int chunk) {
-    const size_t act_b = (size_t)chunk * kActStepBytes;
-    const size_t sc_b = fp8 ? 0 : (size_t)tiles * waves * 16 * 4 * chunk * 2;
-    return act_b + sc_b;
+int64_t verify_chunks(bool fp8, const VerifyPlan &pl, int M, int K) {
+    return (int64_t)verify_tile_groups(M, pl.tiles * pl.waves) * ((verify_steps(fp8, K) + kWalkSteps - 1) / kWalkSteps);
 }
 
-size_t verify_partial_bytes(const VerifyPlan &pl, int M) {
-    if (pl.slices <= 1)
+size_t verify_lds_bytes(bool fp8, int tiles, int waves, bool walk) {
+    if (walk)  // two activation buffers; Q4_0: two scale buffers per wave
+        return 2 * (size_t)kActBuf + (fp8 ? 0 : (size_t)waves * 2 * tiles * 1024);
+    if (fp8)
+        return kActLdsBytes;
+    const int tg_insts = scale_insts(tiles * waves, waves);
+    return kActLdsBytes + (size_t)((tg_insts + waves - 1) / waves) * waves * 1024;
+}
+
+size_t verify_walk_workspace(const VerifyPlan &pl, int64_t chunks) {
+    if (!pl.walk || chunks <= 0)
         return 0;
-    return (size_t)verify_tile_groups(M, pl.tiles * pl.waves) * pl.slices * pl.tiles * pl.waves * 1024;
+    const int64_t cap = pl.groups > 0 ? std::min(pl.groups, kMaxWalkGroups) : kMaxWalkGroups;
+    return kWalkCounterBytes + (size_t)std::min(chunks, cap) * 2 * pl.tiles * pl.waves * 1024;
 }
 
-size_t verify_workspace_bytes(const VerifyPlan &pl, int M) {
-    const size_t part = verify_partial_bytes(pl, M);
-    return part ? verify_counter_bytes() + part : 0;
-}
-
-// Completes and checks a plan whose tiles, waves and requested slices are
-// set: tiles in {1, 2, 4}, waves in {2, 4, 8}, 1 <= slices <= steps, and a
-// split only with at most kMaxSplitTileGroups tile groups and partial tiles
-// addressable in 32 bits.  The slice count becomes the number of non-empty
-// slices of ceil(steps / slices) steps; the LDS chunk is the slice rounded up
-// to whole pipeline rounds, capped by the staging bound.
+// Completes and checks a plan whose tiles, waves and form are set: tiles in
+// {1, 2, 4}, waves in {2, 4, 8}, groups >= 0.  The walk kernel's Q4_0 scales
+// move in 16-byte pieces, so it needs K % 256 == 0.  The LDS must fit.
 bool verify_plan_finish(bool fp8, int M, int K, VerifyPlan &pl) {
-    if (!(pl.tiles == 1 || pl.tiles == 2 || pl.tiles == 4) || !(pl.waves == 2 || pl.waves == 4 || pl.waves == 8))
+    (void)M;
+    if (!(pl.tiles == 1 || pl.tiles == 2 || pl.tiles == 4) || !(pl.waves == 2 || pl.waves == 4 || pl.waves == 8) ||
+        pl.groups < 0)
         return false;
-    const int steps = verify_steps(fp8, K);
-    if (pl.slices < 1 || pl.slices > steps)
-        return false;
-    pl.sl = (steps + pl.slices - 1) / pl.slices;
-    pl.slices = (steps + pl.sl - 1) / pl.sl;
-    if (pl.slices > 1 && (verify_tile_groups(M, pl.tiles * pl.waves) > kMaxSplitTileGroups ||
-                          verify_partial_bytes(pl, M) >= ((size_t)1 << 31)))
-        return false;
-    const int pf = pipeline_depth(fp8, pl.tiles);
-    pl.chunk = std::min(max_chunk_steps(pl.waves), (pl.sl + pf - 1) / pf * pf);
-    return verify_lds_bytes(fp8, pl.tiles, pl.waves, pl.chunk) <= kMaxLdsBytes;
+    if (pl.walk) {
+        if (!fp8 && K % 256 != 0)
+            return false;
+        pl.chunk = kWalkSteps;
+    } else {
+        pl.groups = 0;
+        pl.chunk = max_chunk_steps(pl.waves);
+    }
+    return verify_lds_bytes(fp8, pl.tiles, pl.waves, pl.walk) <= kMaxLdsBytes;
 }
 
 hipError_t launch_verify(const VerifyLaunch &l) {

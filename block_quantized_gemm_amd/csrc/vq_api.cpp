@@ -46,28 +46,36 @@ bool float_act(int d) { return d == VQ_DTYPE_F16 || d == VQ_DTYPE_BF16; }
 bool out_ok(int d) { return d == VQ_DTYPE_F16 || d == VQ_DTYPE_BF16 || d == VQ_DTYPE_F32; }
 bool dim_ok(int64_t v) { return v >= 1 && v <= VQ_MAX_DIM; }
 
-// Default launch shape for an (M, K) verify GEMM: workgroups of four waves,
-// each wave with two 16-feature tiles, so a workgroup stages each activation
-// element once for 8 tiles; K cut into slices of at most one LDS chunk (8
-// steps of 128).  Every workgroup then streams the same number of weight bytes
-// (8 tiles x up to 8 steps), whatever the matrix, which is what lets a launch
-// over several matrices balance.  Small M uses fewer tiles per group.  Without
-// room for the workspace, K is not split and workgroups cover 4 tiles.  A
-// function of (M, K, workspace capacity) only, never of N.
-vq::VerifyPlan default_plan(bool fp8, int64_t m, int64_t k, size_t ws_bytes) {
+// Default launch shape for an (M, K) verify GEMM.  With room for its
+// workspace, the walk form: workgroups of eight single-tile waves (a
+// workgroup stages each activation element once for 8 tiles; two such
+// workgroups share a CU, 16 waves, which hides the per-chunk barrier better
+// than four two-tile waves), as many persistent workgroups as the device
+// holds, each walking an equal share of the chunks.  Small M uses smaller
+// workgroups.  Otherwise (no workspace, or a Q4_0 K that is not a multiple of
+// 256) the one-shot form: one workgroup of four single-tile waves per tile
+// group over all of K.  A function of (M, K, workspace capacity) only, never
+// of N.
+vq::VerifyPlan walk_plan(int64_t m) {
     vq::VerifyPlan pl;
     const int tiles = (int)((m + 15) / 16);
-    pl.tiles = tiles >= 8 ? 2 : 1;
-    pl.waves = tiles >= 4 ? 4 : 2;
-    const int steps = vq::verify_steps(fp8, (int)k);
-    const int chunk = vq::verify_max_chunk(pl.waves);
-    pl.slices = (steps + chunk - 1) / chunk;
-    if (vq::verify_plan_finish(fp8, (int)m, (int)k, pl) && vq::verify_workspace_bytes(pl, (int)m) <= ws_bytes)
+    pl.tiles = 1;
+    pl.waves = tiles >= 8 ? 8 : tiles >= 4 ? 4 : 2;
+    pl.walk = true;
+    return pl;
+}
+
+size_t walk_need(bool fp8, const vq::VerifyPlan &pl, int64_t m, int64_t k) {
+    return vq::verify_walk_workspace(pl, vq::verify_chunks(fp8, pl, (int)m, (int)k));
+}
+
+vq::VerifyPlan default_plan(bool fp8, int64_t m, int64_t k, size_t ws_bytes) {
+    vq::VerifyPlan pl = walk_plan(m);
+    if (vq::verify_plan_finish(fp8, (int)m, (int)k, pl) && walk_need(fp8, pl, m, k) <= ws_bytes)
         return pl;
     vq::VerifyPlan fb;
     fb.tiles = 1;
     fb.waves = 4;
-    fb.slices = 1;
     vq::verify_plan_finish(fp8, (int)m, (int)k, fb);
     return fb;
 }
@@ -84,33 +92,28 @@ int check_problem(bool fp8, const void *w, const void *scales, const void *act, 
 }
 
 // Launches problems[0 .. count) whose plans are finished: consecutive runs
-// with the same tiles and waves share a launch (up to kGroupPerLaunch
-// problems and kMaxSplitTileGroups counters each).  Launches run one after
-// another on the stream, each using the workspace from its start.
+// with the same form (tiles, waves, walk, groups) share a launch, up to
+// kGroupPerLaunch problems each.  Launches run one after another on the
+// stream, each using the workspace from its start; *ws_need (when asked for,
+// nothing is launched) is the largest workspace one launch uses.
 int launch_problems(bool fp8, const vq::VerifyProblem *probs, int count, int act_dtype, int out_dtype,
                     int n, float alpha, void *workspace, hipStream_t stream, size_t *ws_need) {
     size_t need = 0;
     int i = 0;
     while (i < count) {
+        const vq::VerifyPlan &p0 = probs[i].plan;
         int e = i;
-        int counters = 0;
-        size_t part = 0;
-        while (e < count && e - i < vq::kGroupPerLaunch && probs[e].plan.tiles == probs[i].plan.tiles &&
-               probs[e].plan.waves == probs[i].plan.waves) {
-            const int c = probs[e].plan.slices > 1
-                              ? vq::verify_tile_groups(probs[e].M, probs[e].plan.tiles * probs[e].plan.waves)
-                              : 0;
-            if (counters + c > vq::kMaxSplitTileGroups)
-                break;
-            counters += c;
-            part += vq::verify_partial_bytes(probs[e].plan, probs[e].M);
+        int64_t chunks = 0;
+        while (e < count && e - i < vq::kGroupPerLaunch && probs[e].plan.tiles == p0.tiles &&
+               probs[e].plan.waves == p0.waves && probs[e].plan.walk == p0.walk &&
+               probs[e].plan.groups == p0.groups) {
+            chunks += vq::verify_chunks(fp8, probs[e].plan, probs[e].M, probs[e].K);
             ++e;
         }
-        if (part)
-            need = std::max(need, vq::verify_counter_bytes() + part);
+        need = std::max(need, vq::verify_walk_workspace(p0, chunks));
         if (!ws_need) {
-            vq::VerifyLaunch l{fp8, act_dtype, out_dtype, n, alpha, probs[i].plan.tiles, probs[i].plan.waves,
-                               probs + i, e - i, workspace, stream};
+            vq::VerifyLaunch l{fp8, act_dtype, out_dtype, n, alpha, p0.tiles, p0.waves, probs + i, e - i, workspace,
+                               stream};
             if (vq::launch_verify(l) != hipSuccess)
                 return VQ_ERR_LAUNCH;
         }
@@ -123,7 +126,7 @@ int launch_problems(bool fp8, const vq::VerifyProblem *probs, int count, int act
 
 int run_verify(bool fp8, const void *w, const void *scales, const void *act, int act_dtype,
                void *out, int out_dtype, int64_t n, int64_t m, int64_t k, float alpha, int tiles,
-               int waves, int slices, void *workspace, size_t ws_bytes, void *stream) {
+               int waves, int max_groups, void *workspace, size_t ws_bytes, void *stream) {
     const int st = check_problem(fp8, w, scales, act, out, m, k);
     if (st != VQ_OK)
         return st;
@@ -136,16 +139,20 @@ int run_verify(bool fp8, const void *w, const void *scales, const void *act, int
     if (!workspace)
         ws_bytes = 0;
     vq::VerifyPlan pl;
-    if (tiles == 0 && waves == 0 && slices == 0) {
+    if (tiles == 0 && waves == 0 && max_groups == 0) {
         pl = default_plan(fp8, m, k, ws_bytes);
     } else {
-        const vq::VerifyPlan d = default_plan(fp8, m, k, SIZE_MAX);
+        // An explicit shape walks exactly when a workspace is given.
+        const vq::VerifyPlan d = walk_plan(m);
+        pl.walk = workspace != nullptr;
         pl.tiles = tiles ? tiles : d.tiles;
         pl.waves = waves ? waves : d.waves;
-        pl.slices = slices ? slices : d.slices;
+        pl.groups = max_groups;
+        if (!pl.walk && max_groups != 0)
+            return VQ_ERR_WORKSPACE;
         if (!vq::verify_plan_finish(fp8, (int)m, (int)k, pl))
             return VQ_ERR_BAD_CONFIG;
-        if (vq::verify_workspace_bytes(pl, (int)m) > ws_bytes)
+        if (walk_need(fp8, pl, m, k) > ws_bytes)
             return VQ_ERR_WORKSPACE;
     }
     const int dev = check_device();
@@ -156,10 +163,9 @@ int run_verify(bool fp8, const void *w, const void *scales, const void *act, int
                            static_cast<hipStream_t>(stream), nullptr);
 }
 
-// Plans of a grouped call: the default shape of every problem, split when a
-// workspace is given (the call then needs what vq_workspace_bytes_grouped
-// reports), unsplit without one -- the same shapes single calls pick with
-// enough workspace, or with none, so each output matches its single call.
+// Plans of a grouped call: the default shape of every problem, the walk form
+// where the shape allows when a workspace is given (the call then needs what
+// vq_workspace_bytes_grouped reports), one-shot without one.
 int plan_group(bool fp8, const vq_verify_problem *problems, int count, bool split, vq::VerifyProblem *out) {
     for (int i = 0; i < count; ++i) {
         const vq_verify_problem &p = problems[i];
@@ -229,12 +235,12 @@ int vq_gemm_q4_0(const void *w_codes, const void *w_scales, const void *act, int
 
 int vq_gemm_q4_0_ex(const void *w_codes, const void *w_scales, const void *act, int act_dtype,
                     void *out, int out_dtype, int64_t n_rows, int64_t m, int64_t k, float alpha,
-                    int tiles_per_wave, int waves_per_group, int k_slices, void *workspace,
+                    int tiles_per_wave, int waves_per_group, int max_groups, void *workspace,
                     size_t workspace_bytes, void *stream) {
-    if (tiles_per_wave < 0 || waves_per_group < 0 || k_slices < 0)
+    if (tiles_per_wave < 0 || waves_per_group < 0 || max_groups < 0)
         return VQ_ERR_BAD_CONFIG;
     return run_verify(false, w_codes, w_scales, act, act_dtype, out, out_dtype, n_rows, m, k, alpha,
-                      tiles_per_wave, waves_per_group, k_slices, workspace, workspace_bytes, stream);
+                      tiles_per_wave, waves_per_group, max_groups, workspace, workspace_bytes, stream);
 }
 
 int vq_gemm_fp8_blk128(const void *w_e4m3, const float *w_tile_scales, const void *act,
@@ -246,12 +252,12 @@ int vq_gemm_fp8_blk128(const void *w_e4m3, const float *w_tile_scales, const voi
 
 int vq_gemm_fp8_blk128_ex(const void *w_e4m3, const float *w_tile_scales, const void *act,
                           int act_dtype, void *out, int out_dtype, int64_t n_rows, int64_t m,
-                          int64_t k, int tiles_per_wave, int waves_per_group, int k_slices,
+                          int64_t k, int tiles_per_wave, int waves_per_group, int max_groups,
                           void *workspace, size_t workspace_bytes, void *stream) {
-    if (tiles_per_wave < 0 || waves_per_group < 0 || k_slices < 0)
+    if (tiles_per_wave < 0 || waves_per_group < 0 || max_groups < 0)
         return VQ_ERR_BAD_CONFIG;
     return run_verify(true, w_e4m3, w_tile_scales, act, act_dtype, out, out_dtype, n_rows, m, k,
-                      1.0f, tiles_per_wave, waves_per_group, k_slices, workspace, workspace_bytes,
+                      1.0f, tiles_per_wave, waves_per_group, max_groups, workspace, workspace_bytes,
                       stream);
 }
 
@@ -283,12 +289,13 @@ size_t vq_workspace_bytes(int kind, int64_t m, int64_t k) {
     if (!query_ok(kind, m, k))
         return 0;
     const bool fp8 = kind == VQ_KIND_FP8_BLK128;
-    return vq::verify_workspace_bytes(default_plan(fp8, m, k, SIZE_MAX), (int)m);
+    const vq::VerifyPlan pl = default_plan(fp8, m, k, SIZE_MAX);
+    return walk_need(fp8, pl, m, k);
 }
 
 int vq_default_launch_shape(int kind, int64_t m, int64_t k, size_t workspace_bytes, int *tiles_per_wave,
-                            int *waves_per_group, int *k_slices, size_t *workspace_used) {
-    if (!tiles_per_wave || !waves_per_group || !k_slices || !workspace_used)
+                            int *waves_per_group, int *walk, size_t *workspace_used) {
+    if (!tiles_per_wave || !waves_per_group || !walk || !workspace_used)
         return VQ_ERR_NULL_POINTER;
     if (!query_ok(kind, m, k))
         return VQ_ERR_BAD_SHAPE;
@@ -296,8 +303,8 @@ int vq_default_launch_shape(int kind, int64_t m, int64_t k, size_t workspace_byt
     const vq::VerifyPlan pl = default_plan(fp8, m, k, workspace_bytes);
     *tiles_per_wave = pl.tiles;
     *waves_per_group = pl.waves;
-    *k_slices = pl.slices;
-    *workspace_used = vq::verify_workspace_bytes(pl, (int)m);
+    *walk = pl.walk ? 1 : 0;
+    *workspace_used = walk_need(fp8, pl, m, k);
     return VQ_OK;
 }
 

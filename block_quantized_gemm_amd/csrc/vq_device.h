@@ -141,6 +141,31 @@ __device__ __forceinline__ uint32_t bload2(rsrc_t r, int voff, int soff) {
     return (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, AUX));
 }
 
+// 16 bytes per lane from a buffer straight into LDS (no registers): lane l's
+// bytes land at lds_dst + 16 l, whatever its source offset; out-of-range
+// offsets deliver zeros.  lds_dst must be wave-uniform.  The load counts in
+// vmcnt like any other: wait for it before the LDS is read.
+__device__ __forceinline__ void bload16_lds(rsrc_t r, void *lds_dst, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_dst, 16, voff, 0, 0,
+                                             0);
+}
+
+// s_waitcnt that waits until at most n vector-memory operations are
+// outstanding (n <= 63) and leaves the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// Workgroup barrier that leaves vmcnt alone.  __syncthreads' release fence
+// waits for every outstanding vector memory operation of the wave (buffer
+// loads into LDS count there), which would drain the weight pipeline; callers
+// of this barrier first wait for exactly the LDS writes the other waves need.
+// Outstanding LDS reads of this wave are waited for (lgkmcnt), and the memory
+// clobber keeps the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------------------
 // Software pipeline over a wave's `ns` steps with PF stage buffers.
 //   load(U, i)          -- issue the loads of step i into stage buffer U

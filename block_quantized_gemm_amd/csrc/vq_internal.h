@@ -11,12 +11,23 @@
 namespace vq {
 
 // Launch shape of a verify GEMM: `tiles` 16-feature tiles per wave, `waves`
-// waves per workgroup, K cut into `slices` slices of `sl` steps of 128, staged
-// through LDS `chunk` steps at a time.
+// waves per workgroup.  walk: persistent workgroups walking contiguous ranges
+// of chunks (tile group x 8 steps of 128), with the pieces of tile groups cut
+// by range boundaries combined through the workspace; `groups` caps the
+// workgroups (0: as many as the device holds at once).  Otherwise one-shot:
+// one workgroup per tile group over all of K, staged `chunk` steps at a time.
 struct VerifyPlan {
-    int tiles = 0, waves = 0, slices = 0;
-    int sl = 0, chunk = 0;
+    int tiles = 0, waves = 0;
+    bool walk = false;
+    int groups = 0;
+    int chunk = 0;
 };
+
+// Workspace of a walk launch: arrival counters (one per workgroup and wave,
+// kept at zero between calls) in a fixed region at the start, then two fp32
+// piece slots of TG tiles per workgroup.  At most kMaxWalkGroups workgroups.
+constexpr int kMaxWalkGroups = 1024;
+constexpr size_t kWalkCounterBytes = 64 * 1024;
 
 // One verify GEMM of a launch, already validated.
 struct VerifyProblem {
@@ -39,7 +50,7 @@ struct VerifyLaunch {
     int tiles, waves;
     const VerifyProblem *probs;
     int count;        // 1 .. kGroupPerLaunch
-    void *workspace;  // counters + partial tiles of every split problem
+    void *workspace;  // walk launches: counters and pieces
     hipStream_t stream;
 };
 
@@ -60,16 +71,9 @@ inline size_t out_elem_bytes(int dtype) { return dtype == VQ_DTYPE_F32 ? 4 : 2; 
 
 int verify_steps(bool fp8, int K);
 int verify_tile_groups(int M, int tiles_per_group);
-int pipeline_depth_of(bool fp8, int tiles);
-int verify_max_chunk(int waves);
-// Workspace layout of a split-K call: a fixed region of arrival counters (one
-// per tile group, at most kMaxSplitTileGroups; always zero between calls, so
-// shapes of any size can share one workspace), then the fp32 partial tiles.
-constexpr int kMaxSplitTileGroups = 16384;
-size_t verify_counter_bytes();
-size_t verify_lds_bytes(bool fp8, int tiles, int waves, int chunk);
-size_t verify_partial_bytes(const VerifyPlan &plan, int M);
-size_t verify_workspace_bytes(const VerifyPlan &plan, int M);
+int64_t verify_chunks(bool fp8, const VerifyPlan &plan, int M, int K);
+size_t verify_lds_bytes(bool fp8, int tiles, int waves, bool walk);
+size_t verify_walk_workspace(const VerifyPlan &plan, int64_t chunks);
 bool verify_plan_finish(bool fp8, int M, int K, VerifyPlan &plan);
 hipError_t launch_verify(const VerifyLaunch &launch);
 

@@ -74,17 +74,29 @@ extern "C" {
 #define VQ_MAX_DIM (1 << 24)
 
 /*
- * Workspace of the verify GEMMs.  The kernels cut K into slices processed by
- * different workgroups and combine the slices' fp32 partial sums through a
- * caller-owned device buffer (per call: a few MB, see vq_workspace_bytes).
+ * Workspace of the verify GEMMs.  The fast ("walk") form runs persistent
+ * workgroups, each walking an equal share of the weight stream: 8 steps of
+ * 128 k of one group of feature tiles at a time, whole tile groups
+ * accumulated in registers over all of K.  A tile group cut by the boundary
+ * between two workgroups' shares is finished through a caller-owned device
+ * buffer: each side writes its fp32 partial sums there and the last to
+ * arrive adds them in share order (an arrival counter per boundary and wave).
+ * Per call: 64 KiB of counters plus 2 x 4 bytes per tile-group feature per 16
+ * rows per workgroup, at most about 16 MiB, see vq_workspace_bytes.
  *  - 16-byte aligned device memory, zero-filled by the caller before its first
  *    use.  Every call leaves it ready for the next one (its counters back at
  *    zero), so it is zeroed once, not per call.
  *  - Calls that share one workspace must not overlap in time: use it from one
  *    stream, or order the streams.
- *  - workspace may be NULL (or smaller than needed): the library then does not
- *    split K, which is correct but slower.  For a fixed (M, K, workspace
- *    capacity) the launch shape, and hence every output bit, is the same.
+ *  - workspace may be NULL (or smaller than needed): the library then runs the
+ *    one-shot form (one workgroup per feature-tile group over all of K), which
+ *    is correct but slower.  Q4_0 shapes with K not a multiple of 256 always
+ *    run one-shot.
+ *  - Where a tile group is cut depends on the launch (its problems and the
+ *    number of workgroups the device holds), never on N: for a fixed call
+ *    every output bit is the same for any number of rows and from run to run.
+ *    The same problem in another call (alone, or grouped with others) may
+ *    round differently in the last bits.
  */
 
 /*
@@ -167,12 +179,12 @@ int vq_hadamard32_quant_int8(const void *x, int x_dtype,
  * amounts of weight streaming each, by construction of the default shapes --
  * keep every CU busy across matrix boundaries.
  *   problems  host array of `count` descriptors, read during the call only.
- *             Each problem's outputs are bit-identical to the corresponding
- *             single call (vq_gemm_q4_0 / vq_gemm_fp8_blk128) with a large
- *             enough workspace (or, with workspace NULL, with none).
+ *             Each problem's outputs match its single call up to fp32
+ *             rounding (bit-identical when both run one-shot); for a fixed
+ *             problem list they are bit-identical for any n_rows.
  *   act_dtype, out_dtype, n_rows (and alpha): shared by all problems.
  *   workspace needs vq_workspace_bytes_grouped() bytes (VQ_ERR_WORKSPACE if
- *             smaller); NULL runs every problem without splitting K.
+ *             smaller); NULL runs every problem in the one-shot form.
  * 1 <= count <= VQ_MAX_GROUP.  Float activations only.
  */
 #define VQ_MAX_GROUP 4096
@@ -197,40 +209,43 @@ size_t vq_workspace_bytes_grouped(int kind, const vq_verify_problem *problems, i
 
 /* Workspace bytes the default launch shape of an (M, K) verify GEMM uses
  * (kind VQ_KIND_Q4_0 or VQ_KIND_FP8_BLK128; independent of N).  0 for invalid
- * arguments or when the default shape does not split K. */
+ * arguments or when the shape only runs one-shot. */
 size_t vq_workspace_bytes(int kind, int64_t m, int64_t k);
 
 /*
  * vq_gemm_q4_0_ex / vq_gemm_fp8_blk128_ex -- the same operations with an
- * explicit launch shape, for tuning: `tiles_per_wave` 16-feature tiles per
- * wave (1, 2 or 4), `waves_per_group` waves per workgroup (2, 4 or 8) and
- * `k_slices` slices of K (1 .. K/128 rounded up; 1 = no split; the count is
- * rounded to the number of non-empty equal slices).  0 for any of them picks
- * the default for (M, K, workspace_bytes).  VQ_ERR_BAD_CONFIG for a shape
- * outside these sets or beyond 160 KiB of LDS, VQ_ERR_WORKSPACE if
- * k_slices > 1 needs more workspace than given.  Results are bit-identical
- * across N for a fixed launch shape; another shape may round differently.
- * Float activations only.
+ * explicit launch shape, for tuning and testing: `tiles_per_wave` 16-feature
+ * tiles per wave (1, 2 or 4), `waves_per_group` waves per workgroup (2, 4 or
+ * 8).  With workspace non-NULL the call runs the walk form (Q4_0 needs
+ * K % 256 == 0), with at most `max_groups` persistent workgroups (0: as many
+ * as the device holds at once; at most 1024); with workspace NULL it runs
+ * one-shot and max_groups must be 0.  0 for tiles or waves picks the
+ * default.  VQ_ERR_BAD_CONFIG for a shape outside these rules or beyond 160
+ * KiB of LDS; VQ_ERR_WORKSPACE if max_groups > 0 without a workspace or the
+ * workspace is smaller than the shape needs.  Results are bit-identical
+ * across N for a fixed launch shape and form; another shape may round
+ * differently.  Float activations only.
  */
 int vq_gemm_q4_0_ex(const void *w_codes, const void *w_scales,
                     const void *act, int act_dtype,
                     void *out, int out_dtype,
                     int64_t n_rows, int64_t m, int64_t k, float alpha,
-                    int tiles_per_wave, int waves_per_group, int k_slices,
+                    int tiles_per_wave, int waves_per_group, int max_groups,
                     void *workspace, size_t workspace_bytes, void *stream);
 int vq_gemm_fp8_blk128_ex(const void *w_e4m3, const float *w_tile_scales,
                           const void *act, int act_dtype,
                           void *out, int out_dtype,
                           int64_t n_rows, int64_t m, int64_t k,
-                          int tiles_per_wave, int waves_per_group, int k_slices,
+                          int tiles_per_wave, int waves_per_group, int max_groups,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* The launch shape the library picks for an (M, K) verify GEMM given a
- * workspace of workspace_bytes (SIZE_MAX = unlimited), and the workspace that
- * shape uses.  Writes all four outputs; returns VQ_OK or VQ_ERR_BAD_SHAPE /
+ * workspace of workspace_bytes (SIZE_MAX = unlimited): tiles per wave, waves
+ * per workgroup, walk (1) or one-shot (0), and the workspace that shape uses.
+ * Writes all four outputs; returns VQ_OK or VQ_ERR_BAD_SHAPE /
  * VQ_ERR_NULL_POINTER. */
 int vq_default_launch_shape(int kind, int64_t m, int64_t k, size_t workspace_bytes,
-                            int *tiles_per_wave, int *waves_per_group, int *k_slices,
+                            int *tiles_per_wave, int *waves_per_group, int *walk,
                             size_t *workspace_used);
 
 /* Human-readable text for a status code (static storage, never NULL). */

@@ -88,26 +88,40 @@ def _ex(t, w, s, ws=None, wsb=0, k=512):
 
 
 def test_explicit_launch_shape_errors():
-    assert _ex(3, 4, 1) == vq.VQ_ERR_BAD_CONFIG       # tiles per wave not in {1, 2, 4}
-    assert _ex(1, 16, 1) == vq.VQ_ERR_BAD_CONFIG      # waves per group not in {2, 4, 8}
-    assert _ex(1, 1, 1) == vq.VQ_ERR_BAD_CONFIG
-    assert _ex(1, 4, 5) == vq.VQ_ERR_BAD_CONFIG       # K = 512 has 4 steps: at most 4 slices
-    assert _ex(-1, 4, 1) == vq.VQ_ERR_BAD_CONFIG
-    assert _ex(1, 4, 2) == vq.VQ_ERR_WORKSPACE        # a split needs a workspace
+    assert _ex(3, 4, 0) == vq.VQ_ERR_BAD_CONFIG       # tiles per wave not in {1, 2, 4}
+    assert _ex(1, 16, 0) == vq.VQ_ERR_BAD_CONFIG      # waves per group not in {2, 4, 8}
+    assert _ex(1, 1, 0) == vq.VQ_ERR_BAD_CONFIG
+    assert _ex(-1, 4, 0) == vq.VQ_ERR_BAD_CONFIG
+    assert _ex(1, 4, -1) == vq.VQ_ERR_BAD_CONFIG
+    assert _ex(1, 4, 2) == vq.VQ_ERR_WORKSPACE        # a group cap asks for the walk form: needs a workspace
     assert _ex(1, 4, 2, ws=F, wsb=64) == vq.VQ_ERR_WORKSPACE
+    assert _ex(1, 4, 0, ws=F, wsb=64) == vq.VQ_ERR_WORKSPACE
+    # the walk form moves Q4_0 scales in 16-byte pieces: K % 256 == 0
+    assert _ex(1, 4, 0, ws=F, wsb=1 << 30, k=544) == vq.VQ_ERR_BAD_CONFIG
+
+
+def _walk_need(m, k, t, w, chunk_steps=8, cap=1024):
+    steps = -(-k // 128)
+    chunks = -(-(-(-m // 16)) // (t * w)) * -(-steps // chunk_steps)
+    return 64 * 1024 + min(chunks, cap) * 2 * t * w * 1024
 
 
 def test_workspace_query():
     f = vq.lib().vq_workspace_bytes
     assert f(0, 17408, 5120) > 0 and f(1, 17408, 5120) > 0
     assert f(0, 17408, 5000) == 0 and f(1, 17408, 5120 + 32) == 0 and f(7, 256, 512) == 0
+    assert f(0, 17408, 5120 + 32) == 0      # Q4_0 with K % 256 != 0 only runs one-shot
+    # counters, then two pieces of a tile group (8 tiles x 1 KiB) per workgroup
+    assert f(0, 17408, 5120) == _walk_need(17408, 5120, 1, 8) == 65536 + 680 * 16384
     for m, k in ((256, 512), (17408, 5120), (5120, 17408), (8192, 5120), (5120, 8192)):
-        t, w, s, used = vq.default_launch_shape("q4_0", m, k)
-        assert used == vq.workspace_bytes("q4_0", m, k)
-        assert used <= 16 << 20
-        # without a workspace the default does not split K
-        t0, w0, s0, used0 = vq.default_launch_shape("q4_0", m, k, workspace_bytes=0)
-        assert s0 == 1 and used0 == 0
+        t, w, walk, used = vq.default_launch_shape("q4_0", m, k)
+        assert walk == 1 and used == vq.workspace_bytes("q4_0", m, k) == _walk_need(m, k, t, w)
+        assert used <= (16 << 20) + 65536
+        # without a workspace the default is the one-shot form
+        t0, w0, walk0, used0 = vq.default_launch_shape("q4_0", m, k, workspace_bytes=0)
+        assert walk0 == 0 and used0 == 0
+        # with too little, too
+        assert vq.default_launch_shape("q4_0", m, k, workspace_bytes=used - 16)[2] == 0
 
 
 def test_default_launch_shape_ignores_rows():
@@ -116,8 +130,9 @@ def test_default_launch_shape_ignores_rows():
         for kind in ("q4_0", "fp8"):
             if kind == "fp8" and k % 128:
                 continue
-            t, w, s, used = vq.default_launch_shape(kind, m, k)
-            assert t in (1, 2, 4) and w in (2, 4, 8) and 1 <= s <= max(1, (k + 127) // 128)
+            t, w, walk, used = vq.default_launch_shape(kind, m, k)
+            assert t in (1, 2, 4) and w in (2, 4, 8) and walk in (0, 1)
+            assert (used > 0) == (walk == 1)
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
@@ -160,8 +175,10 @@ def test_grouped_workspace_query():
     layer = [(A, B, C, D, m, k) for m, k in ((8192, 5120), (5120, 8192), (17408, 5120), (17408, 5120),
                                              (5120, 17408))]
     need = f(vq.KIND_Q4_0, _table(layer), 5)
-    single = [vq.workspace_bytes("q4_0", m, k) for *_, m, k in layer]
-    counters = 64 * 1024
-    assert need == counters + sum(s - counters for s in single)
+    # one launch over every problem's chunks
+    chunks = sum(-(-m // 128) * (k // 1024) for *_, m, k in layer)
+    assert need == 65536 + min(chunks, 1024) * 16384
+    # a one-shot problem needs no workspace
+    assert f(vq.KIND_Q4_0, _table(layer + [(A, B, C, D, 4096, 4128)]), 6) == need
     assert f(vq.KIND_Q4_0, _table(layer + [(A, B, C, D, 17, 100)]), 6) == 0   # K % 32 != 0
     assert f(9, _table(layer), 5) == 0

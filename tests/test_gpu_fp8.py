@@ -106,13 +106,23 @@ def big_workspace():
 
 @pytest.mark.parametrize("tpw", [1, 2, 4])
 @pytest.mark.parametrize("wpg", [2, 4, 8])
-@pytest.mark.parametrize("ks", [1, 3, 10])
-def test_fp8_launch_shapes(tpw, wpg, ks):
-    """17 tiles (three 128-row scale tiles, the last partial), 10 steps of K:
-    partial tile groups, slices of 1..10 steps, multi-chunk slices (ks = 1)."""
+@pytest.mark.parametrize("groups", [0, 1, 3])
+def test_fp8_walk_shapes(tpw, wpg, groups):
+    """17 tiles (three 128-row scale tiles, the last partial), 10 steps of K
+    (two chunks), every tile/wave shape, tile groups cut between workgroups."""
     f = W.fp8(M=272, K=1280, N=16)
     q = FP8(f["w"], f["tscales"])
-    kw = dict(tiles_per_wave=tpw, waves_per_group=wpg, k_slices=ks, workspace=big_workspace())
+    kw = dict(tiles_per_wave=tpw, waves_per_group=wpg, max_groups=groups, workspace=big_workspace())
+    parity(out_to_f64(q.run(f["act"], **kw)), q.oracle(f["act"]), "bf16")
+
+
+@pytest.mark.parametrize("tpw", [1, 2, 4])
+@pytest.mark.parametrize("wpg", [2, 4, 8])
+def test_fp8_one_shot_shapes(tpw, wpg):
+    """The same problem in the one-shot form, several LDS chunks per tile group."""
+    f = W.fp8(M=272, K=1280, N=16)
+    q = FP8(f["w"], f["tscales"])
+    kw = dict(tiles_per_wave=tpw, waves_per_group=wpg, workspace=None)
     parity(out_to_f64(q.run(f["act"], **kw)), q.oracle(f["act"]), "bf16")
 
 

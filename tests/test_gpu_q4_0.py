@@ -184,7 +184,7 @@ _WS = {}
 
 
 def big_workspace():
-    """One zeroed 32 MiB workspace shared by the explicit-shape tests (calls are
+    """One 32 MiB workspace shared by the explicit-shape tests (calls are
     ordered on one stream, so sharing it is allowed)."""
     if "ws" not in _WS:
         _WS["ws"] = vq.Workspace(32 << 20)
@@ -193,16 +193,49 @@ def big_workspace():
 
 @pytest.mark.parametrize("tpw", [1, 2, 4])
 @pytest.mark.parametrize("wpg", [2, 4, 8])
-@pytest.mark.parametrize("ks", [1, 2, 3, 9])
-def test_every_launch_shape_parity_and_exact_integers(tpw, wpg, ks):
-    """17 tiles and 33 blocks (a partial last step of 128): partial tile groups,
-    slices of 1..9 steps, multi-chunk slices (ks = 1), every tile/wave shape."""
+@pytest.mark.parametrize("groups", [0, 1, 2, 7])
+def test_every_walk_shape_parity_and_exact_integers(tpw, wpg, groups):
+    """17 tiles (partial tile groups) and 10 steps (two chunks, the second of
+    2 steps), every tile/wave shape, and workgroup caps that cut tile groups
+    between workgroups in different places (1: one workgroup walks it all)."""
     g = np.random.Generator(np.random.PCG64(105))
+    M, K, N = 272, 1280, 16
+    codes = W.q4_0_codes(M, K, g)
+    q = Q4(codes, W.fp16_scales_uniform(M, K, g))
+    a = W.f32_to_bf16_bits(g.standard_normal((N, K)))
+    kw = dict(tiles_per_wave=tpw, waves_per_group=wpg, max_groups=groups, workspace=big_workspace())
+    parity(out_to_f64(q.run(a, **kw)), q.oracle(a), "bf16")
+    qi = Q4(codes, np.full((M, K // 32), 0x3C00, dtype=np.uint16))
+    ai = W.f32_to_bf16_bits(g.integers(-4, 5, size=(N, K)))
+    assert np.array_equal(out_to_f64(qi.run(ai, "bf16", "f32", **kw)), qi.oracle(ai))
+
+
+@pytest.mark.parametrize("groups", [1, 3, 40, 0])
+def test_walk_many_pieces(groups):
+    """A long K (17 chunks per tile group) over few or many workgroups: tile
+    groups cut into up to 17 pieces, combined by the last to arrive."""
+    g = np.random.Generator(np.random.PCG64(112))
+    M, K, N = 300, 17408, 16
+    q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_lognormal(M, K, g))
+    x = W.f32_to_bf16_bits(0.5 * g.standard_t(3, size=(N, K)))
+    kw = dict(tiles_per_wave=2, waves_per_group=4, max_groups=groups, workspace=big_workspace())
+    y = q.run(x, **kw)
+    parity(out_to_f64(y), q.oracle(x), "bf16")
+    for n in (0, 9):
+        assert np.array_equal(bits_u16(q.run(np.ascontiguousarray(x[n:n + 1]), **kw))[0], bits_u16(y)[n])
+
+
+@pytest.mark.parametrize("tpw", [1, 2, 4])
+@pytest.mark.parametrize("wpg", [2, 4, 8])
+def test_every_one_shot_shape_parity_and_exact_integers(tpw, wpg):
+    """17 tiles and 33 blocks (a partial last step of 128), staged in several
+    LDS chunks, every tile/wave shape, no workspace."""
+    g = np.random.Generator(np.random.PCG64(104))
     M, K, N = 272, 1056, 16
     codes = W.q4_0_codes(M, K, g)
     q = Q4(codes, W.fp16_scales_uniform(M, K, g))
     a = W.f32_to_bf16_bits(g.standard_normal((N, K)))
-    kw = dict(tiles_per_wave=tpw, waves_per_group=wpg, k_slices=ks, workspace=big_workspace())
+    kw = dict(tiles_per_wave=tpw, waves_per_group=wpg, workspace=None)
     parity(out_to_f64(q.run(a, **kw)), q.oracle(a), "bf16")
     qi = Q4(codes, np.full((M, K // 32), 0x3C00, dtype=np.uint16))
     ai = W.f32_to_bf16_bits(g.integers(-4, 5, size=(N, K)))
@@ -216,28 +249,32 @@ def test_unsupported_launch_shapes_rejected(tpw, wpg):
     q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_uniform(M, K, g))
     with pytest.raises(vq.VqError) as e:
         q.run(W.f32_to_bf16_bits(g.standard_normal((4, K))), tiles_per_wave=tpw, waves_per_group=wpg,
-              k_slices=1, workspace=big_workspace())
+              workspace=big_workspace())
     assert e.value.status == vq.VQ_ERR_BAD_CONFIG
 
 
-def test_split_without_workspace_rejected():
+def test_group_cap_without_workspace_rejected():
     g = np.random.Generator(np.random.PCG64(109))
     M, K = 64, 1024
     q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_uniform(M, K, g))
     with pytest.raises(vq.VqError) as e:
-        q.run(W.f32_to_bf16_bits(g.standard_normal((4, K))), tiles_per_wave=1, waves_per_group=4, k_slices=4,
+        q.run(W.f32_to_bf16_bits(g.standard_normal((4, K))), tiles_per_wave=1, waves_per_group=4, max_groups=4,
               workspace=None)
     assert e.value.status == vq.VQ_ERR_WORKSPACE
 
 
-@pytest.mark.parametrize("tpw,wpg,ks", [(4, 4, 9), (2, 8, 4), (1, 2, 1), (4, 2, 3), (2, 4, 0)])
-def test_launch_shapes_rows_bit_identical_across_widths(tpw, wpg, ks):
-    """Width invariance holds in every launch shape, not only the default one."""
+@pytest.mark.parametrize("tpw,wpg,groups,K,walk", [
+    (4, 4, 0, 2048, True), (2, 8, 3, 2048, True), (1, 2, 0, 2048, True), (4, 2, 5, 2048, True),
+    (2, 4, 0, 2048, True), (4, 4, 0, 2080, False), (1, 2, 0, 2080, False), (2, 8, 0, 2048, False)])
+def test_launch_shapes_rows_bit_identical_across_widths(tpw, wpg, groups, K, walk):
+    """Width invariance holds in every launch shape and form, not only the
+    default one."""
     g = np.random.Generator(np.random.PCG64(107))
-    M, K = 400, 2080
+    M = 400
     q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_lognormal(M, K, g))
     x = W.f32_to_bf16_bits(0.5 * g.standard_t(3, size=(16, K)))
-    kw = dict(tiles_per_wave=tpw, waves_per_group=wpg, k_slices=ks, workspace=big_workspace())
+    kw = dict(tiles_per_wave=tpw, waves_per_group=wpg, max_groups=groups,
+              workspace=big_workspace() if walk else None)
     full = bits_u16(q.run(x, **kw))
     for n in (0, 7, 15):
         one = bits_u16(q.run(np.ascontiguousarray(x[n:n + 1]), **kw))
@@ -246,7 +283,8 @@ def test_launch_shapes_rows_bit_identical_across_widths(tpw, wpg, ks):
 
 
 def test_without_workspace_parity_and_width_invariance():
-    """No workspace: K is not split (every workgroup walks all of K chunk by chunk)."""
+    """No workspace: the one-shot form (every workgroup walks all of K chunk by
+    chunk)."""
     g = np.random.Generator(np.random.PCG64(110))
     M, K = 1000, 5120
     q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_lognormal(M, K, g))
@@ -259,19 +297,24 @@ def test_without_workspace_parity_and_width_invariance():
 
 def test_workspace_reused_across_shapes_and_calls():
     """A workspace left by one call is ready for the next: the arrival counters
-    return to zero, so alternating shapes and repeats stay exact."""
+    return to zero, and whatever the piece slots hold (another shape's sums,
+    or bytes that read as NaN) does not change a result."""
     g = np.random.Generator(np.random.PCG64(111))
     ws = vq.Workspace(32 << 20)
+    ws.tensor[65536:].fill_(0xFF)
     mats = []
-    for M, K in ((1088, 5120), (320, 8192), (17, 96)):
+    for M, K in ((1088, 5120), (320, 8192), (17, 96), (4100, 1024)):
         q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_uniform(M, K, g))
         x = W.f32_to_bf16_bits(g.standard_normal((16, K)))
-        mats.append((q, x, bits_u16(q.run(x, workspace=ws))))
+        y = q.run(x, workspace=ws)
+        parity(out_to_f64(y), q.oracle(x), "bf16")
+        mats.append((q, x, bits_u16(y)))
     for rep in range(3):
         for q, x, ref in mats:
+            if rep == 1:
+                ws.tensor[65536:].fill_(0xFF)
             assert np.array_equal(bits_u16(q.run(x, workspace=ws)), ref)
-    cnt = ws.tensor[:65536].cpu().numpy()
-    assert not cnt.any()  # the arrival-counter region is back to zero
+    assert not ws.tensor[:65536].cpu().numpy().any()  # the counters are back at zero
 
 
 def test_many_row_groups():
