@@ -492,7 +492,14 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     static_assert(scale_pieces(4) * 2 == CH, "scale rows of one chunk");
 
     const int lane = threadIdx.x & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
-    const int C = grp.items, G = (int)gridDim.x, b = (int)blockIdx.x;
+    const int C = grp.items, G = (int)gridDim.x;
+    // Workgroups go to the 8 XCDs in turn (blockIdx % 8); give each XCD a
+    // contiguous run of ranges, so that the workgroups sharing an L2 walk
+    // neighbouring tile groups and reuse each other's activation chunks.
+    const int b = [&] {
+        const int nq = G >> 3, nr = G & 7, xcd = (int)blockIdx.x & 7, loc = (int)blockIdx.x >> 3;
+        return xcd < nr ? xcd * (nq + 1) + loc : nr * (nq + 1) + (xcd - nr) * nq + loc;
+    }();
     const int ib = range_start(b, C, G), ie = range_start(b + 1, C, G);
     if (ib >= ie)
         return;
