@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", action="store_true",
+                    help="instead of the stream: time the prefill-sized W4A8 path (H32 int8 quantizer over 512 "
+                         "bf16 rows x 5120, then the int8-MFMA GEMM against Q4_0 17408 x 5120) and print its "
+                         "own JSON line against the int8 MFMA roofline")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline form (grouped per layer, 16 rows), so that a kernel trace of "
                          "this run holds the headline's launches alone")
@@ -233,8 +237,65 @@ def traffic_from(fetch_dir, write_dir):
     print(json.dumps(rec))
 
 
+INT8_MFMA_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, published
+
+
+def prefill_bench(args):
+    """The prefill-sized W4A8 path on synthetic inputs shaped as its workload."""
+    import numpy as np
+    import torch
+    import block_quantized_gemm_amd as vq
+    import workloads as W
+    vq.lib()
+    p = W.prefill()
+    N, M, K = p["N"], p["M"], p["K"]
+    dev = torch.device("cuda:0")
+    codes = torch.from_numpy(p["codes"]).to(dev)
+    scales = torch.from_numpy(p["scales"].view(np.int16).copy()).to(dev).view(torch.float16)
+    x = torch.from_numpy(p["act"].view(np.int16).copy()).to(dev).view(torch.bfloat16)
+    q = torch.empty((N, K), dtype=torch.int8, device=dev)
+    d = torch.empty((N, K // 32), dtype=torch.float16, device=dev)
+    out = torch.empty((N, M), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+
+    def quant(s):
+        vq.hadamard32_quant_int8(x, q, d, stream=s)
+
+    def gemm(s):
+        vq.gemm_q4_0(codes, scales, q, out, x_scales=d, alpha=1.0 / 32, stream=s)
+
+    def both(s):
+        quant(s)
+        gemm(s)
+
+    t_q = time_ms(quant, stream, args.steps, args.warmup, graph=True)
+    t_g = time_ms(gemm, stream, args.steps, args.warmup, graph=True)
+    t_b = time_ms(both, stream, args.steps, args.warmup, graph=True)
+    ops = 2.0 * N * M * K
+    tops = ops / (t_g * 1e-3) / 1e12
+    result = {
+        "metric": "W4A8 prefill int8-MFMA TOPS",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "higher_is_better": True,
+        "dtype": "i8",
+        "data": "synthetic (Q4_0 codes uniform, fp16 scales lognormal; bf16 rows Student-t with outlier channels)",
+        "config": {"workload": "W4A8 prefill: %d bf16 rows x K=%d, H32 int8 quantizer, then Q4_0 %d x %d "
+                               "int8-MFMA GEMM, fp32 out" % (N, K, M, K)},
+        "gemm_us": round(t_g * 1e3, 2),
+        "quantizer_us": round(t_q * 1e3, 2),
+        "quantizer_plus_gemm_us": round(t_b * 1e3, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_MFMA_PEAK_TOPS, "unit": "TOPS",
+                     "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "ops_per_launch": ops},
+    }
+    print(json.dumps(result))
+
+
 def main():
     args = parse()
+    if args.prefill:
+        prefill_bench(args)
+        return
     if args.traffic_from:
         traffic_from(*args.traffic_from)
         return

@@ -430,8 +430,10 @@ __device__ __forceinline__ void stage_act_swz(uint8_t *buf, rsrc_t ra, int K, in
                                               int lane) {
     const int kb = s_first * kStepK;
 #pragma unroll
-    for (int i = 0; i < 32 / W; ++i) {
+    for (int i = 0; i < (32 + W - 1) / W; ++i) {
         const int inst = wave + W * i;
+        if (32 % W != 0 && inst >= 32)
+            break;
         const int r = inst >> 1, h = inst & 1;
         const int p = (64 * h + lane) ^ (r & 7);
         const bool ok = p < 16 * nc && kb + 8 * p < K;
@@ -485,7 +487,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int SIW = FP8 ? 0 : T;       // scale loads per wave per chunk: 16 feature rows x 64 bytes each
     constexpr int kScBuf = SIW * 1024;     // one wave's scale buffer
     constexpr int scrow = 4 * CH;          // scales per feature row in the buffer
-    constexpr int AI = 32 / W;             // activation loads per wave per chunk
     constexpr int kIssueLoads = PF * T * WB;
     constexpr int kCoherent = 0x10;        // sc1: agent-coherent, no cache maintenance needed
     static_assert(CH % PF == 0, "chunks hold whole pipeline rounds");
@@ -745,8 +746,13 @@ hipError_t launch_tw(const VerifyLaunch &l) {
     const VerifyPlan &pl = l.probs[0].plan;
     const bool walk = pl.walk;
     const size_t shm = verify_lds_bytes(FP8, T, W, walk);
-    auto kern = walk ? walk_kernel<ACT, FP8, T, W, walk_depth(FP8, T)>
-                     : oneshot_kernel<ACT, FP8, T, W, pipeline_depth(FP8, T)>;
+    void (*kern)(KGroup) = walk_kernel<ACT, FP8, T, W, walk_depth(FP8, T)>;
+    if constexpr (W <= 8) {  // the one-shot kernel takes 2, 4 or 8 waves
+        if (!walk)
+            kern = oneshot_kernel<ACT, FP8, T, W, pipeline_depth(FP8, T)>;
+    } else if (!walk) {
+        return hipErrorInvalidValue;
+    }
     if (shm > 64 * 1024 &&
         hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)shm) != hipSuccess)
@@ -800,6 +806,7 @@ hipError_t dispatch_w(const VerifyLaunch &l) {
     case 2: return launch_tw<ACT, FP8, T, 2>(l);
     case 4: return launch_tw<ACT, FP8, T, 4>(l);
     case 8: return launch_tw<ACT, FP8, T, 8>(l);
+    case 12: return T == 1 ? launch_tw<ACT, FP8, 1, 12>(l) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
@@ -845,7 +852,8 @@ size_t verify_walk_workspace(const VerifyPlan &pl, int64_t chunks) {
 // move in 16-byte pieces, so it needs K % 256 == 0.  The LDS must fit.
 bool verify_plan_finish(bool fp8, int M, int K, VerifyPlan &pl) {
     (void)M;
-    if (!(pl.tiles == 1 || pl.tiles == 2 || pl.tiles == 4) || !(pl.waves == 2 || pl.waves == 4 || pl.waves == 8) ||
+    if (!(pl.tiles == 1 || pl.tiles == 2 || pl.tiles == 4) || !(pl.waves == 2 || pl.waves == 4 || pl.waves == 8 ||
+                                                                 (pl.waves == 12 && pl.tiles == 1 && pl.walk)) ||
         pl.groups < 0)
         return false;
     if (pl.walk) {
