@@ -74,7 +74,9 @@ struct KProblem {
 // live in the caller's workspace.
 struct KGroup {
     KProblem p[kGroupPerLaunch];
+    int item0[kGroupPerLaunch];  // p[i].item0, packed for one batch of scalar loads
     int count, items, N, out_dtype;
+    int share, extra;            // walk kernel: ranges of share + 1 chunks for the first `extra` workgroups, then share
     float alpha;
     float *part;    // pieces: [workgroups][2 sides][TG tiles][64 lanes][4]
     uint32_t *cnt;  // arrival counters: [workgroups][waves], zero between calls
@@ -450,9 +452,9 @@ struct ChunkRef {
 // workgroup; later chunks are reached by next_chunk).
 __device__ __forceinline__ ChunkRef find_chunk(const KGroup &grp, int it) {
     int pi = 0;
-    for (int q = 1; q < grp.count; ++q)
-        if (it >= grp.p[q].item0)
-            pi = q;
+#pragma unroll
+    for (int q = 1; q < kGroupPerLaunch; ++q)  // independent loads: one wait, not a chain
+        pi += (q < grp.count && it >= grp.item0[q]) ? 1 : 0;
     const KProblem &a = grp.p[pi];
     const int loc = it - a.item0;
     const int tg = loc / a.cpt;
@@ -473,9 +475,13 @@ __device__ __forceinline__ ChunkRef next_chunk(const KGroup &grp, ChunkRef r) {
     return r;
 }
 
-// First chunk of workgroup b's range, and the workgroup whose range holds chunk c.
-__device__ __forceinline__ int range_start(int b, int C, int G) { return (int)(((int64_t)b * C) / G); }
-__device__ __forceinline__ int range_owner(int c, int C, int G) { return (int)(((int64_t)(c + 1) * G - 1) / C); }
+// First chunk of workgroup b's range, and the workgroup whose range holds
+// chunk c: the first `extra` ranges hold share + 1 chunks, the others share.
+__device__ __forceinline__ int range_start(const KGroup &grp, int b) { return b * grp.share + min(b, grp.extra); }
+__device__ __forceinline__ int range_owner(const KGroup &grp, int c) {
+    const int big = grp.extra * (grp.share + 1);
+    return c < big ? c / (grp.share + 1) : grp.extra + (c - big) / grp.share;
+}
 
 template <int ACT, bool FP8, int T, int W, int PF>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void walk_kernel(const KGroup grp) {
@@ -493,7 +499,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     static_assert(scale_pieces(4) * 2 == CH, "scale rows of one chunk");
 
     const int lane = threadIdx.x & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
-    const int C = grp.items, G = (int)gridDim.x;
+    const int G = (int)gridDim.x;
     // Workgroups go to the 8 XCDs in turn (blockIdx % 8); give each XCD a
     // contiguous run of ranges, so that the workgroups sharing an L2 walk
     // neighbouring tile groups and reuse each other's activation chunks.
@@ -501,7 +507,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int nq = G >> 3, nr = G & 7, xcd = (int)blockIdx.x & 7, loc = (int)blockIdx.x >> 3;
         return xcd < nr ? xcd * (nq + 1) + loc : nr * (nq + 1) + (xcd - nr) * nq + loc;
     }();
-    const int ib = range_start(b, C, G), ie = range_start(b + 1, C, G);
+    const int ib = range_start(grp, b), ie = range_start(grp, b + 1);
     if (ib >= ie)
         return;
     const int nrows = grp.N;
@@ -683,7 +689,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             continue;
         const KProblem &a = grp.p[pend_pi[side]];
         const int first = a.item0 + pend_tg[side] * a.cpt;
-        const int b0 = range_owner(first, C, G), b1 = range_owner(first + a.cpt - 1, C, G);
+        const int b0 = range_owner(grp, first), b1 = range_owner(grp, first + a.cpt - 1);
         uint32_t *cnt = grp.cnt + b0 * W + wave;
         uint32_t old = 0;
         if (lane == 0)
@@ -784,7 +790,11 @@ hipError_t launch_tw(const VerifyLaunch &l) {
         grid = std::min(grid, pl.groups > 0 ? std::min(pl.groups, kMaxWalkGroups) : kMaxWalkGroups);
         grp.cnt = static_cast<uint32_t *>(l.workspace);
         grp.part = reinterpret_cast<float *>(static_cast<char *>(l.workspace) + kWalkCounterBytes);
+        grp.share = (int)(items / grid);
+        grp.extra = (int)(items % grid);
     }
+    for (int i = 0; i < l.count; ++i)
+        grp.item0[i] = grp.p[i].item0;
     // Row groups of 16 run one after another: they share the workspace and
     // are independent otherwise.
     const int groups = (l.N + 15) / 16;
