@@ -76,7 +76,7 @@ struct KGroup {
     KProblem p[kGroupPerLaunch];
     int item0[kGroupPerLaunch];  // p[i].item0, packed for one batch of scalar loads
     int count, items, N, out_dtype;
-    int share, extra;            // walk kernel: ranges of share + 1 chunks for the first `extra` workgroups, then share
+    int share, extra;            // walk kernel: items = share * gridDim.x + extra (range arithmetic in 32 bits)
     float alpha;
     float *part;    // pieces: [workgroups][2 sides][TG tiles][64 lanes][4]
     uint32_t *cnt;  // arrival counters: [workgroups][waves], zero between calls
@@ -475,12 +475,16 @@ __device__ __forceinline__ ChunkRef next_chunk(const KGroup &grp, ChunkRef r) {
     return r;
 }
 
-// First chunk of workgroup b's range, and the workgroup whose range holds
-// chunk c: the first `extra` ranges hold share + 1 chunks, the others share.
-__device__ __forceinline__ int range_start(const KGroup &grp, int b) { return b * grp.share + min(b, grp.extra); }
-__device__ __forceinline__ int range_owner(const KGroup &grp, int c) {
-    const int big = grp.extra * (grp.share + 1);
-    return c < big ? c / (grp.share + 1) : grp.extra + (c - big) / grp.share;
+// First chunk of workgroup b's range, floor(b * items / G), and the workgroup
+// whose range holds chunk c.  Ranges hold share or share + 1 chunks, and the
+// longer ones are spread evenly over the logical ids (so over the XCDs, which
+// take contiguous runs of ids); items = share * G + extra keeps the start in
+// 32 bits.
+__device__ __forceinline__ int range_start(const KGroup &grp, int b, int G) {
+    return b * grp.share + (b * grp.extra) / G;
+}
+__device__ __forceinline__ int range_owner(const KGroup &grp, int c, int G) {
+    return (int)(((int64_t)(c + 1) * G - 1) / grp.items);
 }
 
 template <int ACT, bool FP8, int T, int W, int PF>
@@ -507,7 +511,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int nq = G >> 3, nr = G & 7, xcd = (int)blockIdx.x & 7, loc = (int)blockIdx.x >> 3;
         return xcd < nr ? xcd * (nq + 1) + loc : nr * (nq + 1) + (xcd - nr) * nq + loc;
     }();
-    const int ib = range_start(grp, b), ie = range_start(grp, b + 1);
+    const int ib = range_start(grp, b, G), ie = range_start(grp, b + 1, G);
     if (ib >= ie)
         return;
     const int nrows = grp.N;
@@ -689,7 +693,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             continue;
         const KProblem &a = grp.p[pend_pi[side]];
         const int first = a.item0 + pend_tg[side] * a.cpt;
-        const int b0 = range_owner(grp, first), b1 = range_owner(grp, first + a.cpt - 1);
+        const int b0 = range_owner(grp, first, G), b1 = range_owner(grp, first + a.cpt - 1, G);
         uint32_t *cnt = grp.cnt + b0 * W + wave;
         uint32_t old = 0;
         if (lane == 0)
@@ -791,7 +795,7 @@ hipError_t launch_tw(const VerifyLaunch &l) {
         grp.cnt = static_cast<uint32_t *>(l.workspace);
         grp.part = reinterpret_cast<float *>(static_cast<char *>(l.workspace) + kWalkCounterBytes);
         grp.share = (int)(items / grid);
-        grp.extra = (int)(items % grid);
+        grp.extra = (int)(items % grid);  // below grid <= 1024: b * extra stays in 32 bits
     }
     for (int i = 0; i < l.count; ++i)
         grp.item0[i] = grp.p[i].item0;
