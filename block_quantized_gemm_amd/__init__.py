@@ -29,6 +29,8 @@ VQ_ERR_WORKSPACE = -8
 
 KIND_Q4_0 = 0
 KIND_FP8_BLK128 = 1
+KIND_Q4_0_PANEL = 2
+_KINDS = {"q4_0": KIND_Q4_0, "fp8": KIND_FP8_BLK128, "q4_0_panel": KIND_Q4_0_PANEL}
 
 DTYPE_F16 = 1
 DTYPE_BF16 = 2
@@ -53,6 +55,11 @@ SIGNATURES = {
     "vq_gemm_q4_0_grouped": (_I, [_P, _I, _I, _I, _I64, _F, _P, _SZ, _P]),
     "vq_gemm_fp8_blk128_grouped": (_I, [_P, _I, _I, _I, _I64, _P, _SZ, _P]),
     "vq_workspace_bytes_grouped": (_SZ, [_I, _P, _I]),
+    "vq_q4_0_panel_bytes": (_SZ, [_I64, _I64]),
+    "vq_q4_0_to_panel": (_I, [_P, _P, _I64, _I64, _P, _SZ, _P]),
+    "vq_gemm_q4_0_panel": (_I, [_P, _P, _I, _P, _I, _I64, _I64, _I64, _F, _P, _SZ, _P]),
+    "vq_gemm_q4_0_panel_ex": (_I, [_P, _P, _I, _P, _I, _I64, _I64, _I64, _F, _I, _P, _SZ, _P]),
+    "vq_gemm_q4_0_panel_grouped": (_I, [_P, _I, _I, _I, _I64, _F, _P, _SZ, _P]),
     "vq_status_string": (ctypes.c_char_p, [_I]),
     "vq_version": (_I, []),
 }
@@ -177,9 +184,16 @@ def _workspace_args(workspace, kind: int, m: int, k: int, device, stream_handle:
     return ws.ptr(), ws.nbytes
 
 
+def _kind(kind: str) -> int:
+    if kind not in _KINDS:
+        raise ValueError("kind must be one of %s" % sorted(_KINDS))
+    return _KINDS[kind]
+
+
 def workspace_bytes(kind: str, m: int, k: int) -> int:
-    """Workspace bytes the default launch shape of an (M, K) verify GEMM uses."""
-    return int(lib().vq_workspace_bytes(KIND_FP8_BLK128 if kind == "fp8" else KIND_Q4_0, m, k))
+    """Workspace bytes the default launch shape of an (M, K) verify GEMM uses
+    (kind "q4_0", "fp8" or "q4_0_panel")."""
+    return int(lib().vq_workspace_bytes(_kind(kind), m, k))
 
 
 def gemm_q4_0(codes, scales, x, out, *, x_scales=None, alpha: float = 1.0, workspace="auto", stream=None,
@@ -252,22 +266,73 @@ def gemm_fp8_blk128(w, tile_scales, x, out, *, workspace="auto", stream=None, ti
     return out
 
 
+def q4_0_panel_bytes(m: int, k: int) -> int:
+    """Bytes of the panel form of an M x K Q4_0 matrix (0 for invalid sizes)."""
+    return int(lib().vq_q4_0_panel_bytes(m, k))
+
+
+def q4_0_to_panel(codes, scales, panel=None, *, stream=None):
+    """The panel form of Q4_0 weights (codes uint8 [M][K/2], scales float16
+    [M][K/32]) as a uint8 device tensor of q4_0_panel_bytes(M, K) bytes
+    (written into `panel` when given)."""
+    torch = _torch()
+    M, K = codes.shape[0], codes.shape[1] * 2
+    _check_2d(scales, "scales", (M, K // 32))
+    nbytes = q4_0_panel_bytes(M, K)
+    if nbytes == 0:
+        raise ValueError("invalid Q4_0 shape %s" % ((M, K),))
+    if panel is None:
+        panel = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    if panel.dtype != torch.uint8 or panel.numel() < nbytes:
+        raise ValueError("panel must be a uint8 tensor of at least %d bytes" % nbytes)
+    st = lib().vq_q4_0_to_panel(_dev_ptr(codes, "codes"), _dev_ptr(scales, "scales"), M, K,
+                                _dev_ptr(panel, "panel"), panel.numel(), _stream(stream))
+    _check(st, "vq_q4_0_to_panel")
+    return panel
+
+
+def gemm_q4_0_panel(panel, m: int, k: int, x, out, *, alpha: float = 1.0, workspace="auto", stream=None,
+                    max_groups: int = 0):
+    """gemm_q4_0 on panel weights (q4_0_to_panel) with float16 / bfloat16 x
+    [N][K]; the walk form always (workspace "auto" or a Workspace)."""
+    N, K = x.shape
+    if K != k:
+        raise ValueError("x has K = %d, the panel %d" % (K, k))
+    _check_2d(out, "out", (N, m))
+    if panel.numel() < q4_0_panel_bytes(m, k):
+        raise ValueError("panel tensor is smaller than the panel form of (%d, %d)" % (m, k))
+    L = lib()
+    sh = _stream(stream)
+    if workspace is None:
+        raise ValueError("panel weights need a workspace")
+    wp, wn = _workspace_args(workspace, KIND_Q4_0_PANEL, m, k, x.device, sh)
+    if max_groups:
+        st = L.vq_gemm_q4_0_panel_ex(_dev_ptr(panel, "panel"), _dev_ptr(x, "x"), _dtype_code(x),
+                                     _dev_ptr(out, "out"), _dtype_code(out), N, m, k, float(alpha),
+                                     int(max_groups), wp, wn, sh)
+        _check(st, "vq_gemm_q4_0_panel_ex")
+    else:
+        st = L.vq_gemm_q4_0_panel(_dev_ptr(panel, "panel"), _dev_ptr(x, "x"), _dtype_code(x),
+                                  _dev_ptr(out, "out"), _dtype_code(out), N, m, k, float(alpha), wp, wn, sh)
+        _check(st, "vq_gemm_q4_0_panel")
+    return out
+
+
 class GroupedCall:
     """A prepared grouped verify GEMM: the problem table is built once, so a
     repeated call (a decode step) costs one C call.
 
     problems: list of (w, scales, x, out) device tensors, all with the same
     x dtype, out dtype and row count; kind "q4_0" (w uint8 [M][K/2], scales
-    float16 [M][K/32]) or "fp8" (w uint8 [M][K], scales float32
-    [ceil(M/128)][K/128]).  workspace: a Workspace (grown here to what the
-    group needs), "auto" (a new one of that size) or None (one-shot form)."""
+    float16 [M][K/32]), "fp8" (w uint8 [M][K], scales float32
+    [ceil(M/128)][K/128]) or "q4_0_panel" (w the panel form, scales the
+    integer M).  workspace: a Workspace (grown here to what the group needs),
+    "auto" (a new one of that size) or None (one-shot form; not for panels)."""
 
     def __init__(self, kind: str, problems, *, alpha: float = 1.0, workspace="auto"):
-        if kind not in ("q4_0", "fp8"):
-            raise ValueError("kind must be 'q4_0' or 'fp8'")
+        self.kind = _kind(kind)
         if not problems:
             raise ValueError("empty group")
-        self.kind = KIND_FP8_BLK128 if kind == "fp8" else KIND_Q4_0
         self.alpha = float(alpha)
         x0, o0 = problems[0][2], problems[0][3]
         self.n_rows = x0.shape[0]
@@ -276,9 +341,17 @@ class GroupedCall:
         self._keep = []
         for i, (w, sc, x, out) in enumerate(problems):
             N, K = x.shape
-            M = w.shape[0]
+            M = int(sc) if self.kind == KIND_Q4_0_PANEL else w.shape[0]
             if N != self.n_rows or _dtype_code(x) != self.act_dtype or _dtype_code(out) != self.out_dtype:
                 raise ValueError("problem %d: row count and dtypes must match the first problem" % i)
+            if self.kind == KIND_Q4_0_PANEL:
+                if w.numel() < q4_0_panel_bytes(M, K):
+                    raise ValueError("problem %d: panel tensor too small" % i)
+                _check_2d(out, "out", (N, M))
+                self.table[i] = VerifyProblem(_dev_ptr(w, "w"), None, _dev_ptr(x, "x"), _dev_ptr(out, "out"),
+                                              M, K)
+                self._keep.append((w, x, out))
+                continue
             if self.kind == KIND_Q4_0:
                 _check_2d(w, "w", (M, K // 2))
                 _check_2d(sc, "scales", (M, K // 32))
@@ -292,6 +365,8 @@ class GroupedCall:
         self.count = len(problems)
         need = int(lib().vq_workspace_bytes_grouped(self.kind, self.table, self.count))
         if workspace is None:
+            if self.kind == KIND_Q4_0_PANEL:
+                raise ValueError("panel weights need a workspace")
             self.ws = None
         elif isinstance(workspace, Workspace):
             self.ws = workspace if workspace.nbytes >= need else Workspace(need, x0.device)
@@ -308,6 +383,10 @@ class GroupedCall:
             st = L.vq_gemm_q4_0_grouped(self.table, self.count, self.act_dtype, self.out_dtype, self.n_rows,
                                         self.alpha, wp, wn, _stream(stream))
             _check(st, "vq_gemm_q4_0_grouped")
+        elif self.kind == KIND_Q4_0_PANEL:
+            st = L.vq_gemm_q4_0_panel_grouped(self.table, self.count, self.act_dtype, self.out_dtype,
+                                              self.n_rows, self.alpha, wp, wn, _stream(stream))
+            _check(st, "vq_gemm_q4_0_panel_grouped")
         else:
             st = L.vq_gemm_fp8_blk128_grouped(self.table, self.count, self.act_dtype, self.out_dtype,
                                               self.n_rows, wp, wn, _stream(stream))
@@ -344,7 +423,7 @@ def default_launch_shape(kind: str, m: int, k: int, workspace_bytes=None):
     t, w, s = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
     used = ctypes.c_size_t(0)
     cap = (1 << 64) - 1 if workspace_bytes is None else int(workspace_bytes)
-    _check(lib().vq_default_launch_shape(KIND_FP8_BLK128 if kind == "fp8" else KIND_Q4_0, m, k, cap,
+    _check(lib().vq_default_launch_shape(_kind(kind), m, k, cap,
                                          ctypes.byref(t), ctypes.byref(w), ctypes.byref(s), ctypes.byref(used)),
            "vq_default_launch_shape")
     return t.value, w.value, s.value, used.value

@@ -116,8 +116,10 @@ __device__ __forceinline__ int steps_of(bool fp8, int K) { return fp8 ? (K >> 7)
 //   sc   -- LDS (Q4_0): scale row of feature j of tile 0 at the step's first
 //           block; tile t's row is 16 * t * scrow halves further
 //   w    -- the step's weight registers; ts -- FP8 tile scales
+//   PRE  -- Q4_0 codes already in lane-group order (dword q of lane group g =
+//           dword g of block q), as the panel layout stores them
 // ---------------------------------------------------------------------------
-template <int ACT, bool FP8, int T, int WB>
+template <int ACT, bool FP8, int T, int WB, bool PRE = false>
 __device__ __forceinline__ void step_math(const uint8_t *row, int o0, int swz, int g, const uint16_t *sc,
                                           int scrow, const u32x4 (&w)[T][WB], const float (&ts)[T],
                                           f32x4 (&acc)[T]) {
@@ -168,7 +170,8 @@ __device__ __forceinline__ void step_math(const uint8_t *row, int o0, int swz, i
             d[t][1] = w[t][0][1];
             d[t][2] = w[t][0][2];
             d[t][3] = w[t][0][3];
-            transpose_lane_groups(d[t][0], d[t][1], d[t][2], d[t][3]);  // lane group g: dword g of blocks 0..3
+            if constexpr (!PRE)  // lane group g: dword g of blocks 0..3 (panel codes arrive that way)
+                transpose_lane_groups(d[t][0], d[t][1], d[t][2], d[t][3]);
             scp[t] = *reinterpret_cast<const u32x2 *>(sc + t * 16 * scrow);
         }
 #pragma unroll
@@ -487,7 +490,7 @@ __device__ __forceinline__ int range_owner(const KGroup &grp, int c, int G) {
     return (int)(((int64_t)(c + 1) * G - 1) / grp.items);
 }
 
-template <int ACT, bool FP8, int T, int W, int PF>
+template <int ACT, bool FP8, int T, int W, int PF, bool PANEL>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void walk_kernel(const KGroup grp) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int TG = T * W;
@@ -501,6 +504,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int kCoherent = 0x10;        // sc1: agent-coherent, no cache maintenance needed
     static_assert(CH % PF == 0, "chunks hold whole pipeline rounds");
     static_assert(scale_pieces(4) * 2 == CH, "scale rows of one chunk");
+    static_assert(!PANEL || (!FP8 && T == 1 && W == kPanelTiles && CH == kPanelSteps), "one panel per tile group");
 
     const int lane = threadIdx.x & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
     const int G = (int)gridDim.x;
@@ -530,6 +534,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         src.wrow = FP8 ? K : (K >> 1);
         src.steps = steps_of(FP8, K);
         src.s0 = r.c * CH;
+        if constexpr (PANEL) {  // the chunk's record; wave w's 1 KiB of step s at 8 KiB * s + 1 KiB * w
+            src.rw = make_rsrc(a.w + ((size_t)r.tg * a.cpt + r.c) * kPanelRecordBytes,
+                               real ? (uint32_t)kPanelRecordBytes : 0u);
+            src.vw = wave * 1024 + 16 * lane;
+            return src;
+        }
         const int fwv = (r.tg * TG + wave * T) * 16;
         const int wfeat = real ? max(0, min(M - fwv, T * 16)) : 0;
         src.rw = make_rsrc(a.w + (size_t)min(fwv, M) * src.wrow, (uint32_t)wfeat * (uint32_t)src.wrow);
@@ -552,7 +562,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
             for (int h = 0; h < WB; ++h)
                 wb[U.value][t][h] = bload16<kAuxCached>(
-                    src.rw, ok ? src.vw + kStepBytes * gs + t * 16 * src.wrow + 16 * h : kOut, 0);
+                    src.rw,
+                    !ok ? kOut
+                        : PANEL ? src.vw + kPanelTiles * 1024 * st
+                                : src.vw + kStepBytes * gs + t * 16 * src.wrow + 16 * h,
+                    0);
             if constexpr (FP8)
                 tsb[U.value][t] = src.ts[t][min(gs, src.steps - 1)];
             else
@@ -569,7 +583,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         stage_act_swz<W>(lds + buf * kActBuf, ra, a.K, s0, min(CH, steps - s0), wave, lane);
     };
     auto scales_for = [&](const ChunkRef &r, bool real, int buf) {
-        if constexpr (!FP8) {
+        if constexpr (PANEL) {  // this wave's 1 KiB of the record's scale rows
+            const KProblem &a = grp.p[r.pi];
+            const rsrc_t rs = make_rsrc(a.w + ((size_t)r.tg * a.cpt + r.c) * kPanelRecordBytes,
+                                        real ? (uint32_t)kPanelRecordBytes : 0u);
+            bload16_lds(rs, sc_wave + buf * kScBuf, kPanelCodeBytes + wave * 1024 + 16 * lane);
+        } else if constexpr (!FP8) {
             const KProblem &a = grp.p[r.pi];
             const int NB = a.K >> 5, M = a.M;
             const int steps = steps_of(false, a.K);
@@ -642,8 +661,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             const int st0 = to_next ? 0 : (rd + 1) * PF;
             static_for<PF>([&](auto U) {
                 const int st = rd * PF + U.value;
-                step_math<ACT, FP8, T, WB>(abuf, st * (2 * kStepK), swz, g, sc0 + 4 * st, scrow, wb[U.value],
-                                           tsb[U.value], acc);
+                step_math<ACT, FP8, T, WB, PANEL>(abuf, st * (2 * kStepK), swz, g, sc0 + 4 * st, scrow,
+                                                  wb[U.value], tsb[U.value], acc);
                 __builtin_amdgcn_sched_barrier(0);
                 issue(U, src, st0 + U.value);
                 __builtin_amdgcn_sched_barrier(0);
@@ -718,6 +737,56 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 }
 
 // ---------------------------------------------------------------------------
+// Q4_0 panel layout.  A panel is 128 consecutive features (8 tiles of 16), a
+// chunk 8 steps of 128 k; record (panel p, chunk c) of a matrix with C chunks
+// per panel starts at byte (p * C + c) * kPanelRecordBytes and holds
+//   codes:  for step s, tile t, lane l = 16 g + j, at 8 KiB * s + 1 KiB * t +
+//           16 l: dword q (q = 0..3) is dword g (bytes 4g..4g+3) of block
+//           4 (8c + s) + q of feature 128p + 16t + j -- what the lane would
+//           hold after loading block 4 (8c + s) + g and the lane-group
+//           transpose;
+//   scales: at 64 KiB + 1 KiB * t: the fp16 scales of the tile's 16 features,
+//           feature-major, 32 blocks (32c .. 32c + 31) each.
+// Features past M and blocks past K/32 are zeros.  A workgroup of 8 waves
+// reads one record per chunk front to back: 8 KiB per step, then the scales.
+// The repack runs once per matrix; every thread writes one 16-byte piece.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void panel_pack_kernel(const uint32_t *codes, const uint16_t *scales, int M,
+                                                         int K, int chunks, int64_t pieces, u32x4 *panel) {
+    constexpr int kPieces = kPanelRecordBytes / 16, kCodePieces = kPanelCodeBytes / 16;
+    const int NB = K >> 5;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < pieces; i += (int64_t)gridDim.x * 256) {
+        const int64_t rec = i / kPieces;
+        const int in = (int)(i - rec * kPieces);
+        const int p = (int)(rec / chunks), c = (int)(rec - (int64_t)p * chunks);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (in < kCodePieces) {
+            const int s = in >> 9, t = (in >> 6) & 7, l = in & 63, g = l >> 4, j = l & 15;
+            const int m = 128 * p + 16 * t + j;
+            if (m < M) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int blk = 4 * (8 * c + s) + q;
+                    if (blk < NB)
+                        v[q] = codes[(size_t)m * (K >> 3) + 4 * blk + g];
+                }
+            }
+        } else {
+            const int t = (in - kCodePieces) >> 6, l = (in - kCodePieces) & 63;
+            const int m = 128 * p + 16 * t + (l >> 2), b0 = 32 * c + 8 * (l & 3);
+            if (m < M) {
+                uint32_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    h[e] = b0 + e < NB ? scales[(size_t)m * NB + b0 + e] : 0u;
+                v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+            }
+        }
+        panel[i] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 namespace {
@@ -750,14 +819,14 @@ int resident_groups(Kern kern, int threads, size_t shm) {
 // each), so each wave keeps 8 KiB of weights or more in flight.
 __host__ __device__ constexpr int walk_depth(bool fp8, int T) { return (fp8 ? 2 * T : T) >= 4 ? 2 : 4; }
 
-template <int ACT, bool FP8, int T, int W>
+template <int ACT, bool FP8, int T, int W, bool PANEL = false>
 hipError_t launch_tw(const VerifyLaunch &l) {
     constexpr int TG = T * W;
     const VerifyPlan &pl = l.probs[0].plan;
     const bool walk = pl.walk;
     const size_t shm = verify_lds_bytes(FP8, T, W, walk);
-    void (*kern)(KGroup) = walk_kernel<ACT, FP8, T, W, walk_depth(FP8, T)>;
-    if constexpr (W <= 8) {  // the one-shot kernel takes 2, 4 or 8 waves
+    void (*kern)(KGroup) = walk_kernel<ACT, FP8, T, W, walk_depth(FP8, T), PANEL>;
+    if constexpr (W <= 8 && !PANEL) {  // the one-shot kernel takes 2, 4 or 8 waves
         if (!walk)
             kern = oneshot_kernel<ACT, FP8, T, W, pipeline_depth(FP8, T)>;
     } else if (!walk) {
@@ -837,6 +906,22 @@ hipError_t dispatch_t(const VerifyLaunch &l) {
 
 }  // namespace
 
+int64_t panel_chunks(int K) { return ((int64_t)verify_steps(false, K) + kPanelSteps - 1) / kPanelSteps; }
+
+size_t panel_bytes(int M, int K) {
+    return (size_t)((M + kPanelFeatures - 1) / kPanelFeatures) * (size_t)panel_chunks(K) * kPanelRecordBytes;
+}
+
+hipError_t launch_panel_pack(const void *codes, const void *scales, int M, int K, void *panel,
+                             hipStream_t stream) {
+    const int64_t pieces = (int64_t)(panel_bytes(M, K) / 16);
+    const int64_t blocks = std::min<int64_t>((pieces + 255) / 256, 65536);
+    hipLaunchKernelGGL(panel_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint32_t *>(codes), static_cast<const uint16_t *>(scales), M, K,
+                       (int)panel_chunks(K), pieces, static_cast<u32x4 *>(panel));
+    return hipGetLastError();
+}
+
 int verify_steps(bool fp8, int K) { return fp8 ? K / 128 : (K / 32 + 3) / 4; }
 
 int verify_tile_groups(int M, int tiles_per_group) { return verify_tile_groups_dev(M, tiles_per_group); }
@@ -863,9 +948,17 @@ size_t verify_walk_workspace(const VerifyPlan &pl, int64_t chunks) {
 
 // Completes and checks a plan whose tiles, waves and form are set: tiles in
 // {1, 2, 4}, waves in {2, 4, 8}, groups >= 0.  The walk kernel's Q4_0 scales
-// move in 16-byte pieces, so it needs K % 256 == 0.  The LDS must fit.
+// move in 16-byte pieces, so it needs K % 256 == 0 for row-major weights.
+// Panel weights walk with one tile per wave and one panel per workgroup, at
+// any K.  The LDS must fit.
 bool verify_plan_finish(bool fp8, int M, int K, VerifyPlan &pl) {
     (void)M;
+    if (pl.panel) {
+        if (fp8 || pl.tiles != 1 || pl.waves != kPanelTiles || !pl.walk || pl.groups < 0)
+            return false;
+        pl.chunk = kWalkSteps;
+        return true;
+    }
     if (!(pl.tiles == 1 || pl.tiles == 2 || pl.tiles == 4) || !(pl.waves == 2 || pl.waves == 4 || pl.waves == 8 ||
                                                                  (pl.waves == 12 && pl.tiles == 1 && pl.walk)) ||
         pl.groups < 0)
@@ -884,6 +977,12 @@ bool verify_plan_finish(bool fp8, int M, int K, VerifyPlan &pl) {
 hipError_t launch_verify(const VerifyLaunch &l) {
     if (l.count < 1 || l.count > kGroupPerLaunch)
         return hipErrorInvalidValue;
+    if (l.probs[0].plan.panel) {
+        if (l.fp8 || l.tiles != 1 || l.waves != kPanelTiles || !l.probs[0].plan.walk)
+            return hipErrorInvalidValue;
+        return l.act_dtype == VQ_DTYPE_BF16 ? launch_tw<VQ_DTYPE_BF16, false, 1, kPanelTiles, true>(l)
+                                            : launch_tw<VQ_DTYPE_F16, false, 1, kPanelTiles, true>(l);
+    }
     if (l.act_dtype == VQ_DTYPE_BF16)
         return l.fp8 ? dispatch_t<VQ_DTYPE_BF16, true>(l) : dispatch_t<VQ_DTYPE_BF16, false>(l);
     return l.fp8 ? dispatch_t<VQ_DTYPE_F16, true>(l) : dispatch_t<VQ_DTYPE_F16, false>(l);

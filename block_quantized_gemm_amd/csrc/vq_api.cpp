@@ -80,6 +80,29 @@ vq::VerifyPlan default_plan(bool fp8, int64_t m, int64_t k, size_t ws_bytes) {
     return fb;
 }
 
+// The plan of a panel-layout Q4_0 problem: always the walk form, one tile per
+// wave and one 128-feature panel per workgroup.
+vq::VerifyPlan panel_plan(int max_groups) {
+    vq::VerifyPlan pl;
+    pl.tiles = 1;
+    pl.waves = vq::kPanelTiles;
+    pl.walk = true;
+    pl.panel = true;
+    pl.groups = max_groups;
+    vq::verify_plan_finish(false, 1, 32, pl);
+    return pl;
+}
+
+int check_panel_problem(const void *w, const void *act, void *out, int64_t m, int64_t k) {
+    if (!w || !act || !out)
+        return VQ_ERR_NULL_POINTER;
+    if (!dim_ok(m) || !dim_ok(k) || k % 32 != 0)
+        return VQ_ERR_BAD_SHAPE;
+    if (!aligned16(w) || !aligned16(act) || !aligned16(out))
+        return VQ_ERR_MISALIGNED;
+    return VQ_OK;
+}
+
 int check_problem(bool fp8, const void *w, const void *scales, const void *act, void *out, int64_t m,
                   int64_t k) {
     if (!w || !scales || !act || !out)
@@ -106,7 +129,7 @@ int launch_problems(bool fp8, const vq::VerifyProblem *probs, int count, int act
         int64_t chunks = 0;
         while (e < count && e - i < vq::kGroupPerLaunch && probs[e].plan.tiles == p0.tiles &&
                probs[e].plan.waves == p0.waves && probs[e].plan.walk == p0.walk &&
-               probs[e].plan.groups == p0.groups) {
+               probs[e].plan.groups == p0.groups && probs[e].plan.panel == p0.panel) {
             chunks += vq::verify_chunks(fp8, probs[e].plan, probs[e].M, probs[e].K);
             ++e;
         }
@@ -163,12 +186,45 @@ int run_verify(bool fp8, const void *w, const void *scales, const void *act, int
                            static_cast<hipStream_t>(stream), nullptr);
 }
 
+int run_panel(const void *w, const void *act, int act_dtype, void *out, int out_dtype, int64_t n, int64_t m,
+              int64_t k, float alpha, int max_groups, void *workspace, size_t ws_bytes, void *stream) {
+    const int st = check_panel_problem(w, act, out, m, k);
+    if (st != VQ_OK)
+        return st;
+    if (!float_act(act_dtype) || !out_ok(out_dtype))
+        return VQ_ERR_BAD_DTYPE;
+    if (!dim_ok(n))
+        return VQ_ERR_BAD_SHAPE;
+    if (max_groups < 0)
+        return VQ_ERR_BAD_CONFIG;
+    if (workspace && !aligned16(workspace))
+        return VQ_ERR_MISALIGNED;
+    const vq::VerifyPlan pl = panel_plan(max_groups);
+    if (!workspace || walk_need(false, pl, m, k) > ws_bytes)
+        return VQ_ERR_WORKSPACE;
+    const int dev = check_device();
+    if (dev != VQ_OK)
+        return dev;
+    const vq::VerifyProblem prob{w, nullptr, act, out, (int)m, (int)k, pl};
+    return launch_problems(false, &prob, 1, act_dtype, out_dtype, (int)n, alpha, workspace,
+                           static_cast<hipStream_t>(stream), nullptr);
+}
+
 // Plans of a grouped call: the default shape of every problem, the walk form
 // where the shape allows when a workspace is given (the call then needs what
-// vq_workspace_bytes_grouped reports), one-shot without one.
-int plan_group(bool fp8, const vq_verify_problem *problems, int count, bool split, vq::VerifyProblem *out) {
+// vq_workspace_bytes_grouped reports), one-shot without one.  Panel problems
+// always walk.
+int plan_group(bool fp8, bool panel, const vq_verify_problem *problems, int count, bool split,
+               vq::VerifyProblem *out) {
     for (int i = 0; i < count; ++i) {
         const vq_verify_problem &p = problems[i];
+        if (panel) {
+            const int st = check_panel_problem(p.w, p.act, p.out, p.m, p.k);
+            if (st != VQ_OK)
+                return st;
+            out[i] = vq::VerifyProblem{p.w, nullptr, p.act, p.out, (int)p.m, (int)p.k, panel_plan(0)};
+            continue;
+        }
         const int st = check_problem(fp8, p.w, p.scales, p.act, p.out, p.m, p.k);
         if (st != VQ_OK)
             return st;
@@ -178,7 +234,7 @@ int plan_group(bool fp8, const vq_verify_problem *problems, int count, bool spli
     return VQ_OK;
 }
 
-int run_group(bool fp8, const vq_verify_problem *problems, int count, int act_dtype, int out_dtype,
+int run_group(bool fp8, bool panel, const vq_verify_problem *problems, int count, int act_dtype, int out_dtype,
               int64_t n, float alpha, void *workspace, size_t ws_bytes, void *stream) {
     if (!problems)
         return VQ_ERR_NULL_POINTER;
@@ -189,12 +245,12 @@ int run_group(bool fp8, const vq_verify_problem *problems, int count, int act_dt
     if (workspace && !aligned16(workspace))
         return VQ_ERR_MISALIGNED;
     std::vector<vq::VerifyProblem> probs(count);
-    int st = plan_group(fp8, problems, count, workspace != nullptr, probs.data());
+    int st = plan_group(fp8, panel, problems, count, workspace != nullptr, probs.data());
     if (st != VQ_OK)
         return st;
     size_t need = 0;
     launch_problems(fp8, probs.data(), count, act_dtype, out_dtype, (int)n, alpha, workspace, nullptr, &need);
-    if (need > (workspace ? ws_bytes : 0))
+    if (need > (workspace ? ws_bytes : 0) || (panel && !workspace))
         return VQ_ERR_WORKSPACE;
     st = check_device();
     if (st != VQ_OK)
@@ -281,16 +337,22 @@ int vq_hadamard32_quant_int8(const void *x, int x_dtype, int8_t *q_out, void *sc
 }
 
 static bool query_ok(int kind, int64_t m, int64_t k) {
-    return (kind == VQ_KIND_Q4_0 || kind == VQ_KIND_FP8_BLK128) && dim_ok(m) && dim_ok(k) &&
-           k % (kind == VQ_KIND_FP8_BLK128 ? 128 : 32) == 0;
+    return (kind == VQ_KIND_Q4_0 || kind == VQ_KIND_FP8_BLK128 || kind == VQ_KIND_Q4_0_PANEL) && dim_ok(m) &&
+           dim_ok(k) && k % (kind == VQ_KIND_FP8_BLK128 ? 128 : 32) == 0;
+}
+
+// The default plan of a query: panel problems have only one.
+static vq::VerifyPlan query_plan(int kind, int64_t m, int64_t k, size_t ws_bytes) {
+    if (kind == VQ_KIND_Q4_0_PANEL)
+        return panel_plan(0);
+    return default_plan(kind == VQ_KIND_FP8_BLK128, m, k, ws_bytes);
 }
 
 size_t vq_workspace_bytes(int kind, int64_t m, int64_t k) {
     if (!query_ok(kind, m, k))
         return 0;
     const bool fp8 = kind == VQ_KIND_FP8_BLK128;
-    const vq::VerifyPlan pl = default_plan(fp8, m, k, SIZE_MAX);
-    return walk_need(fp8, pl, m, k);
+    return walk_need(fp8, query_plan(kind, m, k, SIZE_MAX), m, k);
 }
 
 int vq_default_launch_shape(int kind, int64_t m, int64_t k, size_t workspace_bytes, int *tiles_per_wave,
@@ -300,7 +362,7 @@ int vq_default_launch_shape(int kind, int64_t m, int64_t k, size_t workspace_byt
     if (!query_ok(kind, m, k))
         return VQ_ERR_BAD_SHAPE;
     const bool fp8 = kind == VQ_KIND_FP8_BLK128;
-    const vq::VerifyPlan pl = default_plan(fp8, m, k, workspace_bytes);
+    const vq::VerifyPlan pl = query_plan(kind, m, k, workspace_bytes);
     *tiles_per_wave = pl.tiles;
     *waves_per_group = pl.waves;
     *walk = pl.walk ? 1 : 0;
@@ -310,22 +372,69 @@ int vq_default_launch_shape(int kind, int64_t m, int64_t k, size_t workspace_byt
 
 int vq_gemm_q4_0_grouped(const vq_verify_problem *problems, int count, int act_dtype, int out_dtype,
                          int64_t n_rows, float alpha, void *workspace, size_t workspace_bytes, void *stream) {
-    return run_group(false, problems, count, act_dtype, out_dtype, n_rows, alpha, workspace, workspace_bytes,
-                     stream);
+    return run_group(false, false, problems, count, act_dtype, out_dtype, n_rows, alpha, workspace,
+                     workspace_bytes, stream);
 }
 
 int vq_gemm_fp8_blk128_grouped(const vq_verify_problem *problems, int count, int act_dtype, int out_dtype,
                                int64_t n_rows, void *workspace, size_t workspace_bytes, void *stream) {
-    return run_group(true, problems, count, act_dtype, out_dtype, n_rows, 1.0f, workspace, workspace_bytes,
+    return run_group(true, false, problems, count, act_dtype, out_dtype, n_rows, 1.0f, workspace,
+                     workspace_bytes, stream);
+}
+
+int vq_gemm_q4_0_panel_grouped(const vq_verify_problem *problems, int count, int act_dtype, int out_dtype,
+                               int64_t n_rows, float alpha, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    return run_group(false, true, problems, count, act_dtype, out_dtype, n_rows, alpha, workspace,
+                     workspace_bytes, stream);
+}
+
+size_t vq_q4_0_panel_bytes(int64_t m, int64_t k) {
+    if (!dim_ok(m) || !dim_ok(k) || k % 32 != 0)
+        return 0;
+    return vq::panel_bytes((int)m, (int)k);
+}
+
+int vq_q4_0_to_panel(const void *w_codes, const void *w_scales, int64_t m, int64_t k, void *w_panel,
+                     size_t panel_bytes, void *stream) {
+    if (!w_codes || !w_scales || !w_panel)
+        return VQ_ERR_NULL_POINTER;
+    if (!dim_ok(m) || !dim_ok(k) || k % 32 != 0)
+        return VQ_ERR_BAD_SHAPE;
+    if (!aligned16(w_codes) || !aligned16(w_scales) || !aligned16(w_panel))
+        return VQ_ERR_MISALIGNED;
+    if (panel_bytes < vq::panel_bytes((int)m, (int)k))
+        return VQ_ERR_BAD_SHAPE;
+    const int dev = check_device();
+    if (dev != VQ_OK)
+        return dev;
+    return vq::launch_panel_pack(w_codes, w_scales, (int)m, (int)k, w_panel, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? VQ_OK
+               : VQ_ERR_LAUNCH;
+}
+
+int vq_gemm_q4_0_panel(const void *w_panel, const void *act, int act_dtype, void *out, int out_dtype,
+                       int64_t n_rows, int64_t m, int64_t k, float alpha, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    return run_panel(w_panel, act, act_dtype, out, out_dtype, n_rows, m, k, alpha, 0, workspace, workspace_bytes,
                      stream);
 }
 
+int vq_gemm_q4_0_panel_ex(const void *w_panel, const void *act, int act_dtype, void *out, int out_dtype,
+                          int64_t n_rows, int64_t m, int64_t k, float alpha, int max_groups, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    return run_panel(w_panel, act, act_dtype, out, out_dtype, n_rows, m, k, alpha, max_groups, workspace,
+                     workspace_bytes, stream);
+}
+
 size_t vq_workspace_bytes_grouped(int kind, const vq_verify_problem *problems, int count) {
-    if ((kind != VQ_KIND_Q4_0 && kind != VQ_KIND_FP8_BLK128) || !problems || count < 1 || count > VQ_MAX_GROUP)
+    if ((kind != VQ_KIND_Q4_0 && kind != VQ_KIND_FP8_BLK128 && kind != VQ_KIND_Q4_0_PANEL) || !problems ||
+        count < 1 || count > VQ_MAX_GROUP)
         return 0;
     const bool fp8 = kind == VQ_KIND_FP8_BLK128;
     std::vector<vq::VerifyProblem> probs(count);
-    if (plan_group(fp8, problems, count, true, probs.data()) != VQ_OK)
+    if (plan_group(fp8, kind == VQ_KIND_Q4_0_PANEL, problems, count, true, probs.data()) != VQ_OK)
         return 0;
     size_t need = 0;
     launch_problems(fp8, probs.data(), count, VQ_DTYPE_BF16, VQ_DTYPE_BF16, 1, 1.0f, nullptr, nullptr, &need);
@@ -347,6 +456,6 @@ const char *vq_status_string(int status) {
     }
 }
 
-int vq_version(void) { return 200; }
+int vq_version(void) { return 300; }
 
 }  // extern "C"

@@ -21,7 +21,16 @@ struct VerifyPlan {
     bool walk = false;
     int groups = 0;
     int chunk = 0;
+    bool panel = false;  // Q4_0 weights in the panel layout (walk, 1 tile x 8 waves)
 };
+
+// Q4_0 panel layout: records of 128 features x 8 steps of 128 k, the codes of
+// the 8 steps (8 tiles x 1 KiB each) and then the tiles' scales (1 KiB each).
+constexpr int kPanelFeatures = 128;
+constexpr int kPanelTiles = 8;
+constexpr int kPanelSteps = 8;
+constexpr int kPanelCodeBytes = kPanelSteps * kPanelTiles * 1024;
+constexpr int kPanelRecordBytes = kPanelCodeBytes + kPanelTiles * 1024;
 
 // Workspace of a walk launch: arrival counters (one per workgroup and wave,
 // kept at zero between calls) in a fixed region at the start, then two fp32
@@ -76,6 +85,9 @@ size_t verify_lds_bytes(bool fp8, int tiles, int waves, bool walk);
 size_t verify_walk_workspace(const VerifyPlan &plan, int64_t chunks);
 bool verify_plan_finish(bool fp8, int M, int K, VerifyPlan &plan);
 hipError_t launch_verify(const VerifyLaunch &launch);
+int64_t panel_chunks(int K);
+size_t panel_bytes(int M, int K);
+hipError_t launch_panel_pack(const void *codes, const void *scales, int M, int K, void *panel, hipStream_t stream);
 
 hipError_t launch_w4a8(const W4A8Args &p);
 hipError_t launch_h32_quant(const void *x, int x_dtype, int8_t *q, void *d, int N, int K,

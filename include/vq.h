@@ -69,6 +69,7 @@ extern "C" {
 /* Weight formats, for the query functions. */
 #define VQ_KIND_Q4_0 0
 #define VQ_KIND_FP8_BLK128 1
+#define VQ_KIND_Q4_0_PANEL 2       /* Q4_0 in the panel layout (vq_q4_0_to_panel) */
 
 /* Largest M, K or N accepted by any entry point (indices stay in 32 bits). */
 #define VQ_MAX_DIM (1 << 24)
@@ -204,12 +205,63 @@ int vq_gemm_fp8_blk128_grouped(const vq_verify_problem *problems, int count,
                                int act_dtype, int out_dtype, int64_t n_rows,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Q4_0 panel layout -- the weights of vq_gemm_q4_0 (codes and fp16 block
+ * scales [P4]), rearranged once so that the verify GEMM reads them in long
+ * contiguous runs: every HBM byte is still read once, but each workgroup
+ * streams one 72 KiB record at a time instead of 16-row strips of 64 bytes.
+ * The arithmetic is that of the row-major walk form with one tile per wave
+ * and eight waves: where vq_gemm_q4_0 (or its grouped call) runs that form --
+ * M >= 128, K % 256 == 0, a workspace, the same problems and workgroup cap --
+ * the panel call returns the same bits.
+ *   A panel is 128 consecutive features, a chunk 1024 consecutive k.  With
+ *   P = ceil(M/128) panels and C = ceil(K/1024) chunks, record (p, c) starts
+ *   at byte (p * C + c) * 73728 and holds:
+ *    - bytes [0, 65536): for step s = 0..7 (128 k each), tile t = 0..7 (16
+ *      features each) and lane l = 0..63 (g = l / 16, j = l % 16), 16 bytes
+ *      at 8192 s + 1024 t + 16 l whose dword q (q = 0..3) is dword g (code
+ *      bytes 4g..4g+3) of Q4_0 block 32c + 4s + q of feature 128p + 16t + j;
+ *    - bytes [65536, 73728): for tile t at 65536 + 1024 t, the fp16 scales of
+ *      its 16 features, feature-major, 32 blocks (32c .. 32c + 31) each.
+ *   Features past M and blocks past K/32 hold zeros.
+ *
+ * vq_q4_0_panel_bytes -- size of the panel form of an M x K matrix
+ *   (P * C * 73728 bytes; 0 for invalid sizes).
+ * vq_q4_0_to_panel -- writes the panel form of w_codes/w_scales (the
+ *   vq_gemm_q4_0 layout) into w_panel, which must hold panel_bytes >=
+ *   vq_q4_0_panel_bytes(m, k) bytes (VQ_ERR_BAD_SHAPE otherwise).  One kernel
+ *   on `stream`; the inputs are only read.
+ * vq_gemm_q4_0_panel -- vq_gemm_q4_0 with float activations on panel weights.
+ *   The workspace is required (VQ_ERR_WORKSPACE when NULL or smaller than
+ *   vq_workspace_bytes(VQ_KIND_Q4_0_PANEL, m, k)); any K % 32 == 0 walks.
+ * vq_gemm_q4_0_panel_ex -- the same with at most max_groups persistent
+ *   workgroups (0: as many as the device holds; values above 1024 act as
+ *   1024); max_groups < 0 gives VQ_ERR_BAD_CONFIG.
+ * vq_gemm_q4_0_panel_grouped -- vq_gemm_q4_0_grouped on panel weights:
+ *   problem.w is the panel form, problem.scales is ignored.  Needs the
+ *   workspace vq_workspace_bytes_grouped(VQ_KIND_Q4_0_PANEL, ...) reports.
+ * Sizes and the remaining arguments as for vq_gemm_q4_0.
+ */
+size_t vq_q4_0_panel_bytes(int64_t m, int64_t k);
+int vq_q4_0_to_panel(const void *w_codes, const void *w_scales, int64_t m, int64_t k,
+                     void *w_panel, size_t panel_bytes, void *stream);
+int vq_gemm_q4_0_panel(const void *w_panel, const void *act, int act_dtype,
+                       void *out, int out_dtype, int64_t n_rows, int64_t m, int64_t k,
+                       float alpha, void *workspace, size_t workspace_bytes, void *stream);
+int vq_gemm_q4_0_panel_ex(const void *w_panel, const void *act, int act_dtype,
+                          void *out, int out_dtype, int64_t n_rows, int64_t m, int64_t k,
+                          float alpha, int max_groups, void *workspace, size_t workspace_bytes,
+                          void *stream);
+int vq_gemm_q4_0_panel_grouped(const vq_verify_problem *problems, int count,
+                               int act_dtype, int out_dtype, int64_t n_rows, float alpha,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
 /* Workspace a grouped call with these problems needs (0 if invalid). */
 size_t vq_workspace_bytes_grouped(int kind, const vq_verify_problem *problems, int count);
 
 /* Workspace bytes the default launch shape of an (M, K) verify GEMM uses
- * (kind VQ_KIND_Q4_0 or VQ_KIND_FP8_BLK128; independent of N).  0 for invalid
- * arguments or when the shape only runs one-shot. */
+ * (kind VQ_KIND_Q4_0, VQ_KIND_FP8_BLK128 or VQ_KIND_Q4_0_PANEL; independent
+ * of N).  0 for invalid arguments or when the shape only runs one-shot. */
 size_t vq_workspace_bytes(int kind, int64_t m, int64_t k);
 
 /*

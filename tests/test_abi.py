@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert vq.lib().vq_version() == 200
+    assert vq.lib().vq_version() == 300
     for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert vq.status_string(st) and vq.status_string(st) != "unknown status"
     assert vq.status_string(-99) == "unknown status"
@@ -182,3 +182,63 @@ def test_grouped_workspace_query():
     assert f(vq.KIND_Q4_0, _table(layer + [(A, B, C, D, 4096, 4128)]), 6) == need
     assert f(vq.KIND_Q4_0, _table(layer + [(A, B, C, D, 17, 100)]), 6) == 0   # K % 32 != 0
     assert f(9, _table(layer), 5) == 0
+
+
+def test_panel_size_query():
+    f = vq.lib().vq_q4_0_panel_bytes
+    # records of 128 features x 1024 k: 64 KiB of codes + 8 KiB of scales
+    assert f(17408, 5120) == 136 * 5 * 73728 == 17408 * 5120 // 2 * 9 // 8
+    assert f(128, 1024) == 73728
+    assert f(129, 1056) == 2 * 2 * 73728     # ragged M and K round up to whole records
+    assert f(1, 32) == 73728
+    assert f(0, 1024) == 0 and f(128, 1000) == 0 and f(128, (1 << 24) + 32) == 0
+    assert vq.q4_0_panel_bytes(5120, 17408) == 40 * 17 * 73728
+
+
+def _pk(c=A, s=B, m=256, k=512, p=C, pb=1 << 20):
+    return vq.lib().vq_q4_0_to_panel(c, s, m, k, p, pb, None)
+
+
+def _pg(w=A, x=C, xd=vq.DTYPE_BF16, o=D, od=vq.DTYPE_BF16, n=16, m=256, k=512, groups=0, ws=F, wsb=1 << 30):
+    return vq.lib().vq_gemm_q4_0_panel_ex(w, x, xd, o, od, n, m, k, 1.0, groups, ws, wsb, None)
+
+
+def test_panel_argument_errors():
+    assert _pk(c=None) == vq.VQ_ERR_NULL_POINTER
+    assert _pk(p=None) == vq.VQ_ERR_NULL_POINTER
+    assert _pk(k=500) == vq.VQ_ERR_BAD_SHAPE
+    assert _pk(pb=2 * 73728 - 16) == vq.VQ_ERR_BAD_SHAPE     # (256, 512) needs two records
+    assert _pk(s=B + 2) == vq.VQ_ERR_MISALIGNED
+    assert _pg(w=None) == vq.VQ_ERR_NULL_POINTER
+    assert _pg(xd=vq.DTYPE_I8) == vq.VQ_ERR_BAD_DTYPE
+    assert _pg(od=vq.DTYPE_I8) == vq.VQ_ERR_BAD_DTYPE
+    assert _pg(k=500) == vq.VQ_ERR_BAD_SHAPE
+    assert _pg(n=0) == vq.VQ_ERR_BAD_SHAPE
+    assert _pg(x=C + 8) == vq.VQ_ERR_MISALIGNED
+    assert _pg(groups=-1) == vq.VQ_ERR_BAD_CONFIG
+    assert _pg(ws=None) == vq.VQ_ERR_WORKSPACE            # panels always walk
+    assert _pg(wsb=64) == vq.VQ_ERR_WORKSPACE
+    assert _pg(ws=F + 4) == vq.VQ_ERR_MISALIGNED
+    g = vq.lib().vq_gemm_q4_0_panel
+    assert g(A, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 16, 256, 512, 1.0, None, 0, None) == vq.VQ_ERR_WORKSPACE
+    h = vq.lib().vq_gemm_q4_0_panel_grouped
+    t = _table([(A, None, C, D, 256, 512)])
+    assert h(t, 1, vq.DTYPE_BF16, vq.DTYPE_BF16, 16, 1.0, None, 0, None) == vq.VQ_ERR_WORKSPACE
+    assert h(_table([(A, None, C, D, 256, 500)]), 1, vq.DTYPE_BF16, vq.DTYPE_BF16, 16, 1.0, F, 1 << 30,
+             None) == vq.VQ_ERR_BAD_SHAPE
+    assert h(_table([(None, None, C, D, 256, 512)]), 1, vq.DTYPE_BF16, vq.DTYPE_BF16, 16, 1.0, F, 1 << 30,
+             None) == vq.VQ_ERR_NULL_POINTER
+
+
+def test_panel_workspace_and_shape_queries():
+    # any K % 32 == 0 walks; one panel of 8 single-tile waves per workgroup
+    for m, k in ((256, 512), (17408, 5120), (1, 32), (129, 1056), (5120, 17408)):
+        t, w, walk, used = vq.default_launch_shape("q4_0_panel", m, k)
+        assert (t, w, walk) == (1, 8, 1)
+        assert used == vq.workspace_bytes("q4_0_panel", m, k) == _walk_need(m, k, 1, 8)
+    # where the row-major call walks with the same shape it needs the same workspace
+    assert vq.workspace_bytes("q4_0_panel", 17408, 5120) == vq.workspace_bytes("q4_0", 17408, 5120)
+    f = vq.lib().vq_workspace_bytes_grouped
+    layer = [(A, None, C, D, m, k) for m, k in ((8192, 5120), (5120, 8192), (17408, 5120), (17408, 5120),
+                                                (5120, 17408))]
+    assert f(vq.KIND_Q4_0_PANEL, _table(layer), 5) == f(vq.KIND_Q4_0, _table([(A, B) + r[2:] for r in layer]), 5)
