@@ -7,11 +7,14 @@ with Q4_0 matrices 8192x5120, 5120x8192, 17408x5120 (twice) and 5120x17408
 draft block -- 320 verify GEMMs.  Inputs are drawn on the device with a seeded
 generator and resident in HBM before timing starts.
 
-Each layer's five independent GEMMs go to the library as one grouped call (one
-kernel launch per layer), and the step's 64 launches are replayed as one HIP
-graph, as an engine replays its decode step.  The same step is also timed with
-one library call per matrix (320 launches, eager and graph-replayed) and as
-whole-stack grouped calls; those figures are reported beside the headline.
+The weights are held in the library's panel layout (vq_q4_0_to_panel: the same
+Q4_0 codes and scales, 12.65 GB, rearranged once into 72 KiB records that a
+workgroup reads front to back).  Each layer's five independent GEMMs go to
+the library as one grouped call (one kernel launch per layer), and the step's
+64 launches are replayed as one HIP graph, as an engine replays its decode
+step.  The same step is also timed on the row-major Q4_0 arrays (grouped per
+layer, whole-stack grouped calls, one call per matrix eager and
+graph-replayed); those figures are reported beside the headline.
 
 Prints one JSON line: the stream's sustained HBM GB/s at 16 rows (the value),
 the same at 1 and 8 rows, rows*weights/s, the verify kernel's roofline fraction
@@ -80,13 +83,15 @@ def parse():
 
 
 def build_stack(layers, device):
+    """The stack in both layouts: (layer, M, K, codes, scales, panel) per matrix."""
     import torch
+    import block_quantized_gemm_amd as vq
     import workloads as W
     mats = []
     for layer in range(layers):
         for idx, (m, k) in enumerate(SHAPES):
             codes, scales = W.q4_0_device(m, k, W.seed_of(W.CFG_STREAM, layer, 10 * idx), device)
-            mats.append((layer, m, k, codes, scales))
+            mats.append((layer, m, k, codes, scales, vq.q4_0_to_panel(codes, scales)))
     acts = {}
     for layer in range(layers):
         for k in sorted({k for _, k in SHAPES}):
@@ -97,31 +102,42 @@ def build_stack(layers, device):
 
 
 def algorithmic_bytes(mats, n_rows):
-    w = sum(m * (k // 2) + m * (k // 32) * 2 for _, m, k, _, _ in mats)
-    x = sum(n_rows * k * 2 for _, _, k, _, _ in mats)
-    y = sum(n_rows * m * 2 for _, m, _, _, _ in mats)
+    """Codes, scales, activations and outputs of every GEMM (the same for both
+    layouts: the panel form holds the same bytes)."""
+    w = sum(m * (k // 2) + m * (k // 32) * 2 for _, m, k, *_ in mats)
+    x = sum(n_rows * k * 2 for _, _, k, *_ in mats)
+    y = sum(n_rows * m * 2 for _, m, *_ in mats)
     return w, w + x + y
 
 
 class Stream:
-    """The step in its three launch forms, for a given row count."""
+    """The step in its launch forms, for a given row count and weight layout
+    ("panel" or "row_major")."""
 
-    def __init__(self, vq, mats, acts, outs, n_rows, ws):
-        self.vq, self.mats, self.n = vq, mats, n_rows
+    def __init__(self, vq, mats, acts, outs, n_rows, ws, layout):
+        self.vq, self.mats, self.n, self.layout = vq, mats, n_rows, layout
         self.views = {key: a[:n_rows] for key, a in acts.items()}
         self.oviews = {m: o[:n_rows] for m, o in outs.items()}
         self.ws = ws
         layers = sorted({l for l, *_ in mats})
-        self.layer_calls = [
-            vq.GroupedCall("q4_0", [(c, s, self.views[(l, k)], self.oviews[m]) for l2, m, k, c, s in mats if l2 == l],
-                           workspace=ws)
-            for l in layers]
-        self.whole_call = vq.GroupedCall(
-            "q4_0", [(c, s, self.views[(l, k)], self.oviews[m]) for l, m, k, c, s in mats], workspace=ws)
+
+        def problem(l, m, k, c, s, p):
+            if layout == "panel":
+                return (p, m, self.views[(l, k)], self.oviews[m])
+            return (c, s, self.views[(l, k)], self.oviews[m])
+        kind = "q4_0_panel" if layout == "panel" else "q4_0"
+        self.layer_calls = [vq.GroupedCall(kind, [problem(*t) for t in mats if t[0] == l], workspace=ws)
+                            for l in layers]
+        self.whole_call = vq.GroupedCall(kind, [problem(*t) for t in mats], workspace=ws)
 
     def per_call(self, stream):
-        for layer, m, k, codes, scales in self.mats:
-            self.vq.gemm_q4_0(codes, scales, self.views[(layer, k)], self.oviews[m], workspace=self.ws, stream=stream)
+        for layer, m, k, codes, scales, panel in self.mats:
+            if self.layout == "panel":
+                self.vq.gemm_q4_0_panel(panel, m, k, self.views[(layer, k)], self.oviews[m], workspace=self.ws,
+                                        stream=stream)
+            else:
+                self.vq.gemm_q4_0(codes, scales, self.views[(layer, k)], self.oviews[m], workspace=self.ws,
+                                  stream=stream)
 
     def per_layer(self, stream):
         for call in self.layer_calls:
@@ -197,40 +213,53 @@ def cpu_baseline(budget_s):
                        "matrices for F = %s; %.1f s of fp64 scalar C on %d threads" % (sample, spent, threads))
 
 
+def _layout_of(kernel_name):
+    """The weight layout a walk-kernel dispatch ran on (its last template
+    argument is the panel flag), or None for other kernels."""
+    if "vq::walk_kernel<" not in kernel_name:
+        return None
+    return "panel" if kernel_name.split(">")[0].rstrip().endswith("true") else "row_major"
+
+
 def traffic_from(fetch_dir, write_dir):
-    """Per-launch HBM bytes of the verify kernel from two counter runs of
-    --profile-run, each scaled by what the same counter reads for the plain
-    copy of COPY_BYTES in that run."""
+    """Per-launch HBM bytes of the verify kernel, per weight layout, from two
+    counter runs of --profile-run, each scaled by what the same counter reads
+    for the plain copy of COPY_BYTES in that run."""
     def per_kernel(d, counter):
-        vals = {"verify": [], "copy": []}
+        vals = {"panel": [], "row_major": [], "copy": []}
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(path)):
                 if r["Counter_Name"] != counter:
                     continue
                 name = r["Kernel_Name"]
-                if "vq::walk_kernel" in name:
-                    vals["verify"].append(float(r["Counter_Value"]))
+                lay = _layout_of(name)
+                if lay:
+                    vals[lay].append(float(r["Counter_Value"]))
                 elif "copyBuffer" in name:
                     vals["copy"].append(float(r["Counter_Value"]))
-        if not vals["verify"] or not vals["copy"]:
-            raise SystemExit("no %s rows for the verify kernel and the copy in %s" % (counter, d))
+        if not vals["panel"] or not vals["row_major"] or not vals["copy"]:
+            raise SystemExit("no %s rows for both verify layouts and the copy in %s" % (counter, d))
         # the calibration copies are the largest device-to-device copies of the run
         top = max(vals["copy"])
         cal = [v for v in vals["copy"] if v >= 0.9 * top]
-        return sum(vals["verify"]) / len(vals["verify"]), sum(cal) / len(cal)
+        avg = {k: sum(v) / len(v) for k, v in vals.items() if k != "copy"}
+        return avg, sum(cal) / len(cal)
     fv, fc = per_kernel(fetch_dir, "FETCH_SIZE")
     wv, wc = per_kernel(write_dir, "WRITE_SIZE")
     fetch_scale, write_scale = COPY_BYTES / (fc * 1024), COPY_BYTES / (wc * 1024)
     rec = {
         "kernel_source_hash": kernel_source_hash(),
         "workload": "grouped per-layer launch, 5 stream matrices, 16 bf16 rows",
-        "hbm_bytes_per_launch": round(fv * 1024 * fetch_scale + wv * 1024 * write_scale),
-        "read_bytes_per_launch": round(fv * 1024 * fetch_scale),
-        "write_bytes_per_launch": round(wv * 1024 * write_scale),
-        "fetch_kib_raw": fv, "write_kib_raw": wv,
         "copy_fetch_kib": fc, "copy_write_kib": wc,
         "fetch_scale": fetch_scale, "write_scale": write_scale,
     }
+    for lay in ("panel", "row_major"):
+        rec[lay] = {
+            "hbm_bytes_per_launch": round(fv[lay] * 1024 * fetch_scale + wv[lay] * 1024 * write_scale),
+            "read_bytes_per_launch": round(fv[lay] * 1024 * fetch_scale),
+            "write_bytes_per_launch": round(wv[lay] * 1024 * write_scale),
+            "fetch_kib_raw": fv[lay], "write_kib_raw": wv[lay],
+        }
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
@@ -341,15 +370,17 @@ def main():
 
     layers = min(args.layers, 8) if args.profile_run else args.layers
     mats, acts, outs = build_stack(layers, dev)
-    layer_mats = mats[:len(SHAPES)]
-    ws = vq.Workspace(vq.GroupedCall("q4_0", [(c, s, acts[(0, k)], outs[m]) for _, m, k, c, s in mats[:32]],
+    ws = vq.Workspace(vq.GroupedCall("q4_0", [(c, s, acts[(0, k)], outs[m]) for _, m, k, c, s, _ in mats[:32]],
                                      workspace=None).workspace_bytes + (1 << 20), dev)
-    streams = {n: Stream(vq, mats, acts, outs, n, ws) for n in (16, 8, 1)}
+    streams = {n: Stream(vq, mats, acts, outs, n, ws, "panel") for n in (16, 8, 1)}
+    row_major = {n: Stream(vq, mats, acts, outs, n, ws, "row_major") for n in (16, 1)}
 
     if args.profile_run:
         with torch.cuda.stream(stream):
             for _ in range(3):
                 streams[16].per_layer(stream)
+            for _ in range(3):
+                row_major[16].per_layer(stream)
         torch.cuda.synchronize()
         a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -365,17 +396,23 @@ def main():
     for n in rows:
         ms[n] = time_ms(streams[n].per_layer, stream, args.steps if n == 16 else max(2, args.steps // 2),
                         args.warmup, graph=True)
-    extra = {"grouped_per_layer_graph": ms[16]}
+    extra = {"panel_grouped_per_layer_graph": ms[16]}
+    rm_ms = {}
     if not args.headline_only:
         half = max(2, args.steps // 2)
-        extra["grouped_whole_stack_graph"] = time_ms(streams[16].whole, stream, half, args.warmup, True)
-        extra["per_call_graph"] = time_ms(streams[16].per_call, stream, half, args.warmup, True)
-        extra["per_call_eager"] = time_ms(streams[16].per_call, stream, half, args.warmup, False)
-    if not args.headline_only:
+        extra["panel_grouped_whole_stack_graph"] = time_ms(streams[16].whole, stream, half, args.warmup, True)
+        extra["panel_per_call_graph"] = time_ms(streams[16].per_call, stream, half, args.warmup, True)
+        for n in (16, 1):
+            rm_ms[n] = time_ms(row_major[n].per_layer, stream, half, args.warmup, True)
+        extra["row_major_grouped_per_layer_graph"] = rm_ms[16]
+        extra["row_major_grouped_whole_stack_graph"] = time_ms(row_major[16].whole, stream, half, args.warmup,
+                                                               True)
+        extra["row_major_per_call_graph"] = time_ms(row_major[16].per_call, stream, half, args.warmup, True)
+        extra["row_major_per_call_eager"] = time_ms(row_major[16].per_call, stream, half, args.warmup, False)
         extra_fp8 = fp8_forms(stream, args)
     w_bytes, alg16 = algorithmic_bytes(mats, 16)
     gbs = {n: algorithmic_bytes(mats, n)[1] / (ms[n] * 1e-3) / 1e9 for n in ms}
-    n_weights = sum(m * k for _, m, k, _, _ in mats)
+    n_weights = sum(m * k for _, m, k, *_ in mats)
     per_launch_us = ms[16] * 1e3 / n_launch
     achieved = alg16 / n_launch / (per_launch_us * 1e-6) / 1e9
 
@@ -384,7 +421,7 @@ def main():
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
         if t.get("kernel_source_hash") == kernel_source_hash():
-            traffic = t.get("hbm_bytes_per_launch")
+            traffic = t.get("panel", {}).get("hbm_bytes_per_launch")
 
     result = {
         "metric": METRIC,
@@ -401,8 +438,9 @@ def main():
         "data": "synthetic (seeded on-device draws: Q4_0 codes uniform, fp16 scales U[0.001,0.02], bf16 rows N(0,1))",
         "config": {
             "workload": "Q4_0 per-token weight stream: %d layers x (8192x5120, 5120x8192, 17408x5120 x2, "
-                        "5120x17408), 16-row bf16 draft block per layer; each layer's 5 GEMMs one grouped "
-                        "call, the step's %d launches replayed as one HIP graph" % (args.layers, n_launch),
+                        "5120x17408), 16-row bf16 draft block per layer; weights in the library's panel "
+                        "layout (same bytes as row-major Q4_0); each layer's 5 GEMMs one grouped call, the "
+                        "step's %d launches replayed as one HIP graph" % (args.layers, n_launch),
             "weight_bytes": w_bytes,
             "n_rows": 16,
         },
@@ -410,12 +448,15 @@ def main():
         "gbs_by_rows": {str(n): round(gbs[n], 2) for n in rows},
         "ms_by_rows": {str(n): round(ms[n], 4) for n in rows},
         "t16_over_t1": round(ms[16] / ms[1], 4) if 1 in ms else None,
+        "row_major_gbs_by_rows": {str(n): round(algorithmic_bytes(mats, n)[1] / (t * 1e-3) / 1e9, 2)
+                                  for n, t in rm_ms.items()},
+        "row_major_t16_over_t1": round(rm_ms[16] / rm_ms[1], 4) if rm_ms else None,
         "rows_weights_per_s": 16 * n_weights / (ms[16] * 1e-3),
         "launch_forms_gbs_16_rows": {k: round(alg16 / (v * 1e-3) / 1e9, 2) for k, v in extra.items()},
         "fp8_blk128_gbs_16_rows": None if args.headline_only else extra_fp8,
         "roofline": {
             "bound": "hbm",
-            "kernel": "vq::walk_kernel (Q4_0, bf16 activations, grouped per layer)",
+            "kernel": "vq::walk_kernel (Q4_0 panel layout, bf16 activations, grouped per layer)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
