@@ -31,19 +31,19 @@
 //    workgroup covers a tile group of TG = T * W tiles.  Weights stream with
 //    16-byte raw buffer loads (rows past M read as zeros) PF steps of 128 k
 //    ahead of the math, in registers.
-//  * Activations (16 rows) are staged in LDS, row-major, with buffer loads
-//    that write LDS directly; every staged element serves the TG tiles.  Q4_0
-//    block scales are staged the same way.
-//  * With a workspace (the normal case), K is cut into slices of at most 8
-//    steps and the stream kernel runs persistent workgroups, each walking a
-//    run of equal-size items (tile group x slice) in slice-major order: the
-//    weight pipeline never drains between items, an activation slice is
-//    staged once per run of items that share it, each wave prefetches its own
-//    scales one item ahead, and each item's fp32 partial tiles go to the
-//    workspace with plain stores that nothing waits for.  A second, small
-//    kernel then adds every output's slices in the fixed order 0, 1, ...,
-//    S-1, scales by alpha and rounds: no atomics, no flags, the same result
-//    on every run.
+//  * Activations (16 rows) are staged in LDS with buffer loads that write LDS
+//    directly; every staged element serves the TG tiles.  Q4_0 block scales
+//    are staged the same way.
+//  * With a workspace (the normal case) the walk kernel runs persistent
+//    workgroups, each walking one contiguous share of the launch's chunks
+//    (tile group x 8 steps): the weight pipeline never drains between
+//    chunks, the next chunk's activations and scales load into the other of
+//    two LDS buffers, a tile group inside the share is summed in registers
+//    over all of K, and a tile group cut between two shares is finished by
+//    the last of its workgroups to arrive, from fp32 pieces in the workspace
+//    added in share order (the same result on every run).
+//  * Q4_0 weights come row-major or in the panel layout, where each chunk of
+//    a 128-feature tile group is one 72 KiB record read front to back.
 //  * Without a workspace the one-shot kernel gives each workgroup a whole
 //    tile group over all of K, staged chunk by chunk.
 #include "vq_device.h"

@@ -104,8 +104,9 @@ __device__ __forceinline__ u32x4 q4_operand(uint32_t v) {
 // Raw buffer loads.  A buffer resource carries a byte size; the hardware
 // returns zeros for any lane whose offset falls outside it, which is how rows
 // past M or N are masked without divergent branches.  Offsets: a per-lane
-// VGPR part and a wave-uniform SGPR part.  Weight bytes are read once, so they
-// use the non-temporal policy (aux = 2).
+// VGPR part and a wave-uniform SGPR part.  The verify kernels read weights
+// with the default policy: non-temporal (aux = 2) and sc1 loads measured
+// slower on the weight stream.
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kAuxStream = 2;  // nt
