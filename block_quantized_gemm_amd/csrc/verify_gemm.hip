@@ -109,10 +109,9 @@ __device__ __forceinline__ int steps_of(bool fp8, int K) { return fp8 ? (K >> 7)
 
 // ---------------------------------------------------------------------------
 // The math of one step of 128 k for one wave's T tiles.
-//   row  -- LDS: activation row j (= lane & 15); element e of the staged
-//           chunk sits at byte ((o0 + 2e') ^ swz) from it, where o0 is the
-//           step's byte offset and e' the element within the step (swz
-//           permutes 16-byte pieces, 0 for an unswizzled layout)
+//   row  -- LDS: activation row j (= lane & 15); element e' of the step sits
+//           at byte o0 + 2e' from it (o0: the step's byte offset in the
+//           staged chunk)
 //   sc   -- LDS (Q4_0): scale row of feature j of tile 0 at the step's first
 //           block; tile t's row is 16 * t * scrow halves further
 //   w    -- the step's weight registers; ts -- FP8 tile scales
@@ -120,12 +119,12 @@ __device__ __forceinline__ int steps_of(bool fp8, int K) { return fp8 ? (K >> 7)
 //           dword g of block q), as the panel layout stores them
 // ---------------------------------------------------------------------------
 template <int ACT, bool FP8, int T, int WB, bool PRE = false>
-__device__ __forceinline__ void step_math(const uint8_t *row, int o0, int swz, int g, const uint16_t *sc,
+__device__ __forceinline__ void step_math(const uint8_t *row, int o0, int g, const uint16_t *sc,
                                           int scrow, const u32x4 (&w)[T][WB], const float (&ts)[T],
                                           f32x4 (&acc)[T]) {
     using A16 = Act16<ACT>;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    auto at = [&](int byte) { return row + ((o0 + byte) ^ swz); };
+    auto at = [&](int byte) { return row + o0 + byte; };
     // A operand of lane (g, r): row r; Q4_0 block q: x[4g..4g+3] and
     // x[16+4g..16+4g+3] of the block (the order q4_operand gives the codes);
     // FP8 MFMA u: x[32g + 8u .. +8] of the step
@@ -344,7 +343,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(T >= 4 ?
     auto compute = [&](auto U, int st, int c0) {
         const uint16_t *sc =
             reinterpret_cast<const uint16_t *>(sc_lds) + ((wave * T) * 16 + j) * scrow + 4 * (st - c0);
-        step_math<ACT, FP8, T, WB>(act_lds + j * kActPitch, (st - c0) * (2 * kStepK), 0, g, sc, scrow, wb[U.value],
+        step_math<ACT, FP8, T, WB>(act_lds + j * kActPitch, (st - c0) * (2 * kStepK), g, sc, scrow, wb[U.value],
                                    tsb[U.value], acc);
     };
 
@@ -422,17 +421,18 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(T >= 4 ?
 // the pieces in range order and writes the outputs.
 // ---------------------------------------------------------------------------
 constexpr int kWalkSteps = 8;                   // steps per chunk
-constexpr int kActBuf = 16 * kWalkSteps * 256;  // one activation buffer: 16 rows x 1024 k, 32 KiB
+constexpr int kActBuf = kActLdsBytes;  // one activation buffer: 16 rows x 1024 k at a pitch of kActPitch
 
-// Activation chunk into one buffer, rows of 2 KiB with no padding: 16-byte
-// piece p of row r goes to slot p ^ (r & 7) of the row, which spreads the
-// rows' reads of one piece over the LDS banks.  A load instruction into LDS
-// writes lane l's 16 bytes to slot l of its 1 KiB destination, so the
-// permutation is made on the source side: the lane of slot l fetches piece
-// l ^ (r & 7), in the same 128-byte line.
+// Activation chunk into one buffer, row r at r * kActPitch: the 16 bytes of
+// padding per row spread the 16 rows' reads of one element over the LDS
+// banks, and keep every read at a constant offset from the lane's row.
+// Instruction (row r, half h) moves 64 consecutive 16-byte pieces (1 KiB of
+// whole cache lines); a load instruction into LDS writes lane l's 16 bytes to
+// byte 16 l of its destination.  The 32 instructions are shared out over the
+// W waves; pieces past the chunk or past K, and rows past N, read zeros.
 template <int W>
-__device__ __forceinline__ void stage_act_swz(uint8_t *buf, rsrc_t ra, int K, int s_first, int nc, int wave,
-                                              int lane) {
+__device__ __forceinline__ void stage_act_rows(uint8_t *buf, rsrc_t ra, int K, int s_first, int nc, int wave,
+                                               int lane) {
     const int kb = s_first * kStepK;
 #pragma unroll
     for (int i = 0; i < (32 + W - 1) / W; ++i) {
@@ -440,9 +440,9 @@ __device__ __forceinline__ void stage_act_swz(uint8_t *buf, rsrc_t ra, int K, in
         if (32 % W != 0 && inst >= 32)
             break;
         const int r = inst >> 1, h = inst & 1;
-        const int p = (64 * h + lane) ^ (r & 7);
+        const int p = 64 * h + lane;
         const bool ok = p < 16 * nc && kb + 8 * p < K;
-        bload16_lds(ra, buf + r * 2048 + h * 1024, ok ? r * K * 2 + 2 * kb + 16 * p : kOut);
+        bload16_lds(ra, buf + r * kActPitch + h * 1024, ok ? r * K * 2 + 2 * kb + 16 * p : kOut);
     }
 }
 
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int steps = steps_of(FP8, a.K);
         const int s0 = r.c * CH;
         const rsrc_t ra = make_rsrc(a.act, real ? (uint32_t)nrows * (uint32_t)a.K * 2u : 0u);
-        stage_act_swz<W>(lds + buf * kActBuf, ra, a.K, s0, min(CH, steps - s0), wave, lane);
+        stage_act_rows<W>(lds + buf * kActBuf, ra, a.K, s0, min(CH, steps - s0), wave, lane);
     };
     auto scales_for = [&](const ChunkRef &r, bool real, int buf) {
         if constexpr (PANEL) {  // this wave's 1 KiB of the record's scale rows
@@ -639,8 +639,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     lds_barrier();
 
     int par = 0;
-    const uint8_t *row = lds + j * 2048;
-    const int swz = (j & 7) << 4;
+    const uint8_t *row = lds + j * kActPitch;
     for (;;) {
         // The next chunk's activations and scales go into the other buffers
         // (free: every wave passed the barrier after the chunk that used
@@ -661,8 +660,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             const int st0 = to_next ? 0 : (rd + 1) * PF;
             static_for<PF>([&](auto U) {
                 const int st = rd * PF + U.value;
-                step_math<ACT, FP8, T, WB, PANEL>(abuf, st * (2 * kStepK), swz, g, sc0 + 4 * st, scrow,
-                                                  wb[U.value], tsb[U.value], acc);
+                step_math<ACT, FP8, T, WB, PANEL>(abuf, st * (2 * kStepK), g, sc0 + 4 * st, scrow, wb[U.value],
+                                                  tsb[U.value], acc);
                 __builtin_amdgcn_sched_barrier(0);
                 issue(U, src, st0 + U.value);
                 __builtin_amdgcn_sched_barrier(0);
@@ -705,23 +704,33 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // ---- pieces: count in (per wave: each wave owns its T tiles), and the
     // last arrival adds the pieces in range order.  The pieces were written
     // with agent-coherent stores that are complete after this wait.
+    // Both sides' arrivals go out before either count is looked at: one
+    // round trip to the coherence point instead of two.
     wait_vmcnt<0>();
+    int b0s[2] = {0, 0}, b1s[2] = {0, 0};
+    uint32_t old[2] = {0u, 0u};
 #pragma unroll
     for (int side = 0; side < 2; ++side) {
         if (pend_pi[side] < 0)
             continue;
         const KProblem &a = grp.p[pend_pi[side]];
         const int first = a.item0 + pend_tg[side] * a.cpt;
-        const int b0 = range_owner(grp, first, G), b1 = range_owner(grp, first + a.cpt - 1, G);
-        uint32_t *cnt = grp.cnt + b0 * W + wave;
-        uint32_t old = 0;
+        b0s[side] = range_owner(grp, first, G);
+        b1s[side] = range_owner(grp, first + a.cpt - 1, G);
         if (lane == 0)
-            old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old = __builtin_amdgcn_readfirstlane(old);
-        if (old != (uint32_t)(b1 - b0))
+            old[side] = __hip_atomic_fetch_add(grp.cnt + b0s[side] * W + wave, 1u, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int side = 0; side < 2; ++side) {
+        if (pend_pi[side] < 0)
+            continue;
+        const KProblem &a = grp.p[pend_pi[side]];
+        const int b0 = b0s[side], b1 = b1s[side];
+        if (__builtin_amdgcn_readfirstlane(old[side]) != (uint32_t)(b1 - b0))
             continue;
         if (lane == 0)  // every piece has arrived: leave the counter at zero for the next call
-            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(grp.cnt + b0 * W + wave, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         f32x4 sum[T];
         for (int wg = b0; wg <= b1; ++wg) {
             const int sd = wg < b1 ? 1 : 0;
