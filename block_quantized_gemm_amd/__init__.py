@@ -60,6 +60,8 @@ SIGNATURES = {
     "vq_gemm_q4_0_panel": (_I, [_P, _P, _I, _P, _I, _I64, _I64, _I64, _F, _P, _SZ, _P]),
     "vq_gemm_q4_0_panel_ex": (_I, [_P, _P, _I, _P, _I, _I64, _I64, _I64, _F, _I, _P, _SZ, _P]),
     "vq_gemm_q4_0_panel_grouped": (_I, [_P, _I, _I, _I, _I64, _F, _P, _SZ, _P]),
+    "vq_greedy_verify": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "vq_greedy_workspace_bytes": (_SZ, [_I64, _I64]),
     "vq_status_string": (ctypes.c_char_p, [_I]),
     "vq_version": (_I, []),
 }
@@ -414,6 +416,49 @@ def hadamard32_quant_int8(x, q_out, scales_out, *, stream=None):
                                         _dev_ptr(scales_out, "scales_out"), N, K, _stream(stream))
     _check(st, "vq_hadamard32_quant_int8")
     return q_out, scales_out
+
+
+def greedy_workspace_bytes(n_rows: int, vocab: int) -> int:
+    """Workspace bytes of greedy_verify for a block of n_rows over vocab (0 if invalid)."""
+    return int(lib().vq_greedy_workspace_bytes(n_rows, vocab))
+
+
+def greedy_verify(logits, draft, tokens_out=None, count_out=None, *, workspace="auto", stream=None):
+    """Greedy acceptance of a draft block: logits float32 / float16 / bfloat16
+    [n][V], draft int32 [n - 1].  Returns (tokens_out int32 [n], count_out
+    int32 [1]) on the device: the target's choice per row and the number of
+    committed tokens (tokens_out[:count] are committed).  workspace: "auto"
+    (a cached one per device and stream) or a Workspace."""
+    torch = _torch()
+    n, v = logits.shape
+    if draft is None:
+        if n != 1:
+            raise ValueError("draft must hold n_rows - 1 tokens")
+    elif draft.dtype != torch.int32 or draft.numel() != n - 1:
+        raise ValueError("draft must be int32 with n_rows - 1 tokens")
+    if tokens_out is None:
+        tokens_out = torch.empty(n, dtype=torch.int32, device=logits.device)
+    if count_out is None:
+        count_out = torch.empty(1, dtype=torch.int32, device=logits.device)
+    need = greedy_workspace_bytes(n, v)
+    sh = _stream(stream)
+    if isinstance(workspace, Workspace):
+        ws = workspace
+    elif workspace == "auto":
+        key = ("greedy", str(logits.device), sh)
+        with _auto_lock:
+            ws = _auto_ws.get(key)
+            if ws is None or ws.nbytes < need:
+                ws = Workspace(need, logits.device)
+                _auto_ws[key] = ws
+    else:
+        raise TypeError("workspace must be a Workspace or 'auto'")
+    dptr = _dev_ptr(draft, "draft") if (draft is not None and draft.numel()) else None
+    st = lib().vq_greedy_verify(_dev_ptr(logits, "logits"), _dtype_code(logits), n, v, dptr,
+                                _dev_ptr(tokens_out, "tokens_out"), _dev_ptr(count_out, "count_out"),
+                                ws.ptr(), ws.nbytes, sh)
+    _check(st, "vq_greedy_verify")
+    return tokens_out, count_out
 
 
 def default_launch_shape(kind: str, m: int, k: int, workspace_bytes=None):

@@ -441,6 +441,35 @@ size_t vq_workspace_bytes_grouped(int kind, const vq_verify_problem *problems, i
     return need;
 }
 
+size_t vq_greedy_workspace_bytes(int64_t n_rows, int64_t vocab) {
+    if (n_rows < 1 || n_rows > VQ_MAX_GREEDY_ROWS || !dim_ok(vocab))
+        return 0;
+    return vq::greedy_workspace_bytes((int)n_rows, (int)vocab);
+}
+
+int vq_greedy_verify(const void *logits, int logits_dtype, int64_t n_rows, int64_t vocab, const int32_t *draft,
+                     int32_t *tokens_out, int32_t *count_out, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    if (!logits || !tokens_out || !count_out || (n_rows > 1 && !draft))
+        return VQ_ERR_NULL_POINTER;
+    if (logits_dtype != VQ_DTYPE_F32 && !float_act(logits_dtype))
+        return VQ_ERR_BAD_DTYPE;
+    if (n_rows < 1 || n_rows > VQ_MAX_GREEDY_ROWS || !dim_ok(vocab))
+        return VQ_ERR_BAD_SHAPE;
+    if (!aligned16(logits) || !aligned16(tokens_out) || !aligned16(count_out) || (draft && !aligned16(draft)) ||
+        (workspace && !aligned16(workspace)))
+        return VQ_ERR_MISALIGNED;
+    if (!workspace || workspace_bytes < vq::greedy_workspace_bytes((int)n_rows, (int)vocab))
+        return VQ_ERR_WORKSPACE;
+    const int dev = check_device();
+    if (dev != VQ_OK)
+        return dev;
+    return vq::launch_greedy_verify(logits, logits_dtype, (int)n_rows, (int)vocab, draft, tokens_out, count_out,
+                                    workspace, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? VQ_OK
+               : VQ_ERR_LAUNCH;
+}
+
 const char *vq_status_string(int status) {
     switch (status) {
     case VQ_OK: return "ok";

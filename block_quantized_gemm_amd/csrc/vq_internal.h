@@ -89,6 +89,13 @@ int64_t panel_chunks(int K);
 size_t panel_bytes(int M, int K);
 hipError_t launch_panel_pack(const void *codes, const void *scales, int M, int K, void *panel, hipStream_t stream);
 
+// Greedy verification: segments per row of the argmax pass, the workspace
+// (one 8-byte key per row and segment) and the launch of both kernels.
+int greedy_segments(int vocab);
+size_t greedy_workspace_bytes(int n_rows, int vocab);
+hipError_t launch_greedy_verify(const void *logits, int dtype, int n_rows, int vocab, const int32_t *draft,
+                                int32_t *tokens, int32_t *count, void *workspace, hipStream_t stream);
+
 hipError_t launch_w4a8(const W4A8Args &p);
 hipError_t launch_h32_quant(const void *x, int x_dtype, int8_t *q, void *d, int N, int K,
                             hipStream_t stream);

@@ -300,6 +300,36 @@ int vq_default_launch_shape(int kind, int64_t m, int64_t k, size_t workspace_byt
                             int *tiles_per_wave, int *waves_per_group, int *walk,
                             size_t *workspace_used);
 
+/*
+ * vq_greedy_verify -- greedy acceptance of a verified draft block [P1]
+ * ("A block-diffusion drafter, verified exactly", "What 'lossless' means
+ * here, precisely": a drafted token is committed only where the target's own
+ * greedy choice is the same token, so the output is plain greedy decoding's).
+ *   logits    [n_rows][vocab], logits_dtype F32, F16 or BF16: the target's
+ *             scores for the block positions; row 0 follows the last
+ *             committed token, row i the drafted token i - 1 (the library's
+ *             reading of the block layout).
+ *   draft     int32 [n_rows - 1]: the drafted tokens (may be NULL when
+ *             n_rows == 1).
+ *   tokens_out int32 [n_rows]: the target's choice for every row, the argmax
+ *             of the row: its first NaN if it holds one, else the first of its
+ *             largest values (-0 and +0 equal).
+ *   count_out int32 [1]: a + 1, where a is the number of leading positions
+ *             i < n_rows - 1 with draft[i] == tokens_out[i]; the committed
+ *             tokens are tokens_out[0 .. a] (the accepted drafts, then the
+ *             target's own token at the first disagreement, or the bonus token
+ *             after a fully accepted block).
+ *   workspace vq_greedy_workspace_bytes(n_rows, vocab) bytes of device memory,
+ *             any contents (VQ_ERR_WORKSPACE if NULL or smaller).
+ * Sizes: 1 <= n_rows <= VQ_MAX_GREEDY_ROWS, 1 <= vocab <= VQ_MAX_DIM.  Outputs
+ * are written on `stream`; they are exact (no rounding is involved).
+ */
+#define VQ_MAX_GREEDY_ROWS 4096
+int vq_greedy_verify(const void *logits, int logits_dtype, int64_t n_rows, int64_t vocab,
+                     const int32_t *draft, int32_t *tokens_out, int32_t *count_out,
+                     void *workspace, size_t workspace_bytes, void *stream);
+size_t vq_greedy_workspace_bytes(int64_t n_rows, int64_t vocab);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *vq_status_string(int status);
 

@@ -25,6 +25,7 @@ _LIB_PATH = os.path.join(_HERE, "libvq_oracle.so")
 
 F16 = 1
 BF16 = 2
+F32 = 3
 
 _lock = threading.Lock()
 _lib = None
@@ -83,6 +84,8 @@ def _load():
         lib.vqo_h32_matrix.argtypes = [P]
         lib.vqo_h32_quant_int8.restype = ctypes.c_int
         lib.vqo_h32_quant_int8.argtypes = [P, ctypes.c_int, I64, I64, P, P]
+        lib.vqo_greedy_verify.restype = I64
+        lib.vqo_greedy_verify.argtypes = [P, ctypes.c_int, I64, I64, P, P]
         _lib = lib
         return lib
 
@@ -215,3 +218,20 @@ def h32_quant_int8(x_bits, x_dtype, N, K):
     d = np.empty((N, K // 32), dtype=np.uint16)
     st = _load().vqo_h32_quant_int8(_ptr(x), int(x_dtype), N, K, _ptr(q), _ptr(d))
     return q, d, int(st)
+
+
+# ---------------------------------------------------------------- greedy verification
+
+def greedy_verify(logits, dtype, draft):
+    """(target choice per row, number of committed tokens) for logits [n][V]
+    (float32 values for F32, uint16 bit patterns for F16 / BF16) and drafted
+    tokens [n - 1]; see vqo_greedy_verify."""
+    lib = _load()
+    lg = _c(logits, np.float32 if dtype == F32 else np.uint16)
+    n, v = lg.shape
+    d = _c(np.asarray(draft, dtype=np.int32).reshape(-1), np.int32)
+    if d.size != n - 1:
+        raise ValueError("draft must hold n_rows - 1 tokens")
+    target = np.zeros(n, dtype=np.int32)
+    count = lib.vqo_greedy_verify(_ptr(lg), dtype, n, v, _ptr(d) if d.size else None, _ptr(target))
+    return target, int(count)

@@ -38,6 +38,12 @@
  *    restored by alpha = 1/32.
  *  - int8 activation quantizer: d = fp16_rne(amax / 127) computed in fp32,
  *    q = clamp(rint_half_even(u / d), -127, 127), amax == 0 gives d = 0, q = 0.
+ *  - greedy verification: logits row i is the target's prediction for block
+ *    position i (row 0 follows the last committed token, row i the drafted
+ *    token i - 1); the target's choice in a row is its argmax, the first NaN
+ *    if the row holds one, else the first of its largest values (-0 and +0
+ *    equal); the committed tokens are the leading drafted tokens that equal
+ *    the target's choices, then the target's own choice at the next position.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
  * fp-contract is off so that the fp32 quantizer emulation performs exactly one
@@ -49,6 +55,7 @@
 
 #define VQO_F16 1
 #define VQO_BF16 2
+#define VQO_F32 3
 
 /* ------------------------------------------------------------------ */
 /* Closed-form decoders                                                */
@@ -355,4 +362,49 @@ int vqo_h32_quant_int8(const uint16_t *x, int x_dtype, int64_t N, int64_t K,
         }
     }
     return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Greedy verification of a draft block                                */
+/* ------------------------------------------------------------------ */
+
+/* [P1] "A block-diffusion drafter, verified exactly" and "What 'lossless'
+ * means here, precisely": the drafter proposes, the target checks every
+ * position in one batched forward, and a proposal is committed only where the
+ * target's own greedy choice is the same token, so the output is what plain
+ * greedy decoding would produce.  logits: [n_rows][vocab] in dtype (VQO_F32,
+ * VQO_F16 or VQO_BF16 bit patterns); draft: [n_rows - 1] proposed tokens.
+ * Writes the target's choice of every row to target[] and returns the number
+ * of committed tokens (accepted prefix + 1). */
+int64_t vqo_greedy_verify(const void *logits, int dtype, int64_t n_rows, int64_t vocab,
+                          const int32_t *draft, int32_t *target)
+{
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t best = -1;
+        double bv = 0.0;
+        for (int64_t v = 0; v < vocab; ++v) {
+            const int64_t i = r * vocab + v;
+            double x;
+            if (dtype == VQO_F32) {
+                float f;
+                memcpy(&f, (const char *)logits + 4 * i, 4);
+                x = (double)f;
+            } else {
+                x = act_to_f64((const uint16_t *)logits, dtype, i);
+            }
+            if (isnan(x)) {          /* a NaN is the choice: the first one */
+                best = v;
+                break;
+            }
+            if (best < 0 || x > bv) { /* strictly larger: ties keep the first */
+                best = v;
+                bv = x;
+            }
+        }
+        target[r] = (int32_t)best;
+    }
+    int64_t a = 0;
+    while (a < n_rows - 1 && draft[a] == target[a])
+        ++a;
+    return a + 1;
 }

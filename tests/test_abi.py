@@ -242,3 +242,28 @@ def test_panel_workspace_and_shape_queries():
     layer = [(A, None, C, D, m, k) for m, k in ((8192, 5120), (5120, 8192), (17408, 5120), (17408, 5120),
                                                 (5120, 17408))]
     assert f(vq.KIND_Q4_0_PANEL, _table(layer), 5) == f(vq.KIND_Q4_0, _table([(A, B) + r[2:] for r in layer]), 5)
+
+
+def test_greedy_argument_errors_and_workspace_query():
+    f = vq.lib().vq_greedy_verify
+    ws = vq.lib().vq_greedy_workspace_bytes
+    # one 8-byte key per row and segment of at most 4096 entries (up to 128 segments)
+    assert ws(16, 151936) == 16 * 38 * 8
+    assert ws(1, 1) == 8 and ws(4096, 1 << 24) == 4096 * 128 * 8
+    assert ws(0, 10) == 0 and ws(4097, 10) == 0 and ws(4, 0) == 0
+    big = 1 << 30
+
+    def call(lg=A, dt=vq.DTYPE_F32, n=16, v=1000, d=B, t=C, c=D, w=F, wb=big):
+        return f(lg, dt, n, v, d, t, c, w, wb, None)
+    assert call(lg=None) == vq.VQ_ERR_NULL_POINTER
+    assert call(d=None) == vq.VQ_ERR_NULL_POINTER
+    assert call(c=None) == vq.VQ_ERR_NULL_POINTER
+    assert call(dt=vq.DTYPE_I8) == vq.VQ_ERR_BAD_DTYPE
+    assert call(n=0) == vq.VQ_ERR_BAD_SHAPE
+    assert call(n=4097) == vq.VQ_ERR_BAD_SHAPE
+    assert call(v=0) == vq.VQ_ERR_BAD_SHAPE
+    assert call(t=C + 4) == vq.VQ_ERR_MISALIGNED
+    assert call(w=None) == vq.VQ_ERR_WORKSPACE
+    assert call(wb=16 * 8 - 8) == vq.VQ_ERR_WORKSPACE
+    if not torch.cuda.is_available():
+        assert call(n=1, d=None) == vq.VQ_ERR_DEVICE   # a one-row block needs no draft

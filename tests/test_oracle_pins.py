@@ -421,3 +421,48 @@ def test_w4a8_equals_dequantised_matmul():
     what = _int4_twos_complement(_unpack_codes(codes, K)) * np.repeat(_np_f16(wsc), 32, axis=1)
     ref = (xhat @ what.T) / 32
     assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+# ------------------------------------------------------------ greedy verification
+
+
+def test_greedy_choice_matches_numpy_argmax():
+    """The target's choice per row is numpy's argmax (first maximum, a NaN wins,
+    -0 equals +0), for float32 and for the 16-bit formats."""
+    g = np.random.Generator(np.random.PCG64(51))
+    n, v = 9, 3001
+    x = g.standard_normal((n, v)).astype(np.float32)
+    x[1, [17, 2000]] = 9.0                  # a tie: the first index
+    x[2, 40] = np.nan                       # a NaN: chosen
+    x[2, 41] = np.inf
+    x[3] = -np.inf
+    x[3, [5, 3]] = [-0.0, 0.0]              # -0 == +0: the first of them (3)
+    x[4] = np.float32(-1.0)                 # all equal: index 0
+    t, _ = oracle.greedy_verify(x, oracle.F32, np.zeros(n - 1, np.int32))
+    assert np.array_equal(t, np.argmax(x, axis=1))
+    assert t[1] == 17 and t[2] == 40 and t[3] == 3 and t[4] == 0
+    for dt, conv in ((oracle.BF16, W.f32_to_bf16_bits), (oracle.F16, W.f32_to_f16_bits)):
+        bits = conv(np.nan_to_num(x, nan=0.0, posinf=60000.0, neginf=-60000.0))
+        vals = torch.from_numpy(bits.view(np.int16).copy()).view(
+            torch.bfloat16 if dt == oracle.BF16 else torch.float16).float().numpy()
+        t16, _ = oracle.greedy_verify(bits, dt, np.zeros(n - 1, np.int32))
+        assert np.array_equal(t16, np.argmax(vals, axis=1)), dt
+
+
+def test_greedy_commits_the_accepted_prefix_plus_one():
+    """One-hot logits fix the target's choices; the number of committed tokens is
+    the length of the matching draft prefix plus the target's own next token."""
+    n, v = 16, 50
+    choice = np.array([(7 * i + 3) % v for i in range(n)], dtype=np.int32)
+    logits = np.full((n, v), -1.0, dtype=np.float32)
+    logits[np.arange(n), choice] = 4.0
+    for a in (0, 1, 5, 14, 15):
+        draft = choice[:n - 1].copy()
+        if a < n - 1:
+            draft[a] = (draft[a] + 1) % v       # first disagreement at position a
+            draft[a + 1:] = 0                   # later proposals do not matter
+        t, count = oracle.greedy_verify(logits, oracle.F32, draft)
+        assert np.array_equal(t, choice)
+        assert count == a + 1
+    t, count = oracle.greedy_verify(logits[:1], oracle.F32, np.zeros(0, np.int32))
+    assert count == 1 and t[0] == choice[0]   # a block of one row commits the target's token
