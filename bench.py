@@ -276,9 +276,10 @@ INT8_MFMA_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, published
 
 
 def fp8_forms(stream, args):
-    """The FP8 block-scaled verify GEMM at the FP8 workload's two shapes, 16
-    rows, one call per matrix graph-replayed; enough distinct copies of the
-    weights that a step reads more than the 256 MB Infinity Cache holds."""
+    """The FP8 block-scaled verify GEMM at the FP8 workload's two shapes and
+    row counts (1, 4, 16), one call per matrix graph-replayed; enough distinct
+    copies of the weights that a step reads more than the 256 MB Infinity
+    Cache holds."""
     import numpy as np
     import torch
     import block_quantized_gemm_amd as vq
@@ -290,20 +291,57 @@ def fp8_forms(stream, args):
         w0 = torch.from_numpy(f["w"]).to(dev)
         s0 = torch.from_numpy(f["tscales"]).to(dev)
         x = torch.from_numpy(f["act"].view(np.int16).copy()).to(dev).view(torch.bfloat16)
-        per_call = m * k + 4 * ((m + 127) // 128) * (k // 128) + 16 * k * 2 + 16 * m * 2
         copies = max(1, -(-(600 << 20) // (m * k)))
         ws = [w0] + [w0.clone() for _ in range(copies - 1)]
-        out = torch.empty((16, m), dtype=torch.bfloat16, device=dev)
         wsp = vq.Workspace(vq.workspace_bytes("fp8", m, k), dev)
+        by_rows = {}
+        for n in (1, 4, 16):
+            per_call = m * k + 4 * ((m + 127) // 128) * (k // 128) + n * k * 2 + n * m * 2
+            xn = x[:n].contiguous()
+            out = torch.empty((n, m), dtype=torch.bfloat16, device=dev)
 
-        def step(s, ws=ws, s0=s0, x=x, out=out, wsp=wsp):
-            for w in ws:
-                vq.gemm_fp8_blk128(w, s0, x, out, workspace=wsp, stream=s)
+            def step(s, ws=ws, s0=s0, xn=xn, out=out, wsp=wsp):
+                for w in ws:
+                    vq.gemm_fp8_blk128(w, s0, xn, out, workspace=wsp, stream=s)
 
-        t = time_ms(step, stream, max(2, args.steps // 2), args.warmup, graph=True)
-        res["%dx%d" % (m, k)] = round(copies * per_call / (t * 1e-3) / 1e9, 2)
+            t = time_ms(step, stream, max(2, args.steps // 2), args.warmup, graph=True)
+            by_rows[str(n)] = round(copies * per_call / (t * 1e-3) / 1e9, 2)
+        res["%dx%d" % (m, k)] = by_rows
         del ws
     return res
+
+
+GREEDY_VOCAB = 151936  # a synthetic vocabulary of 151,936 entries
+
+
+def greedy_form(stream, args):
+    """Greedy verification of a 16-row block over bf16 logits [16][V]: time per
+    call, one call per copy graph-replayed over enough copies of the logits
+    that a step reads them from HBM; bytes = the logits read once."""
+    import torch
+    import block_quantized_gemm_amd as vq
+    dev = torch.device("cuda:0")
+    n, v = 16, GREEDY_VOCAB
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    lg0 = torch.randn((n, v), generator=g, device=dev).to(torch.bfloat16)
+    copies = -(-(600 << 20) // lg0.numel() // 2)
+    lgs = [lg0] + [lg0.clone() for _ in range(copies - 1)]
+    draft = torch.zeros(n - 1, dtype=torch.int32, device=dev)
+    tokens = torch.empty(n, dtype=torch.int32, device=dev)
+    count = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = vq.Workspace(vq.greedy_workspace_bytes(n, v), dev)
+
+    def step(s):
+        for lg in lgs:
+            vq.greedy_verify(lg, draft, tokens, count, workspace=ws, stream=s)
+
+    t = time_ms(step, stream, max(2, args.steps // 2), args.warmup, graph=True)
+    us = t * 1e3 / copies
+    gbs = n * v * 2 / (us * 1e-6) / 1e9
+    del lgs
+    return {"rows": n, "vocab": v, "logits_dtype": "bf16", "us_per_call": round(us, 2), "gbs": round(gbs, 2),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def prefill_bench(args):
@@ -416,6 +454,7 @@ def main():
         extra["row_major_per_call_graph"] = time_ms(row_major[16].per_call, stream, half, args.warmup, True)
         extra["row_major_per_call_eager"] = time_ms(row_major[16].per_call, stream, half, args.warmup, False)
         extra_fp8 = fp8_forms(stream, args)
+        greedy = greedy_form(stream, args)
     w_bytes, alg16 = algorithmic_bytes(mats, 16)
     gbs = {n: algorithmic_bytes(mats, n)[1] / (ms[n] * 1e-3) / 1e9 for n in ms}
     n_weights = sum(m * k for _, m, k, *_ in mats)
@@ -459,7 +498,8 @@ def main():
         "row_major_t16_over_t1": round(rm_ms[16] / rm_ms[1], 4) if rm_ms else None,
         "rows_weights_per_s": 16 * n_weights / (ms[16] * 1e-3),
         "launch_forms_gbs_16_rows": {k: round(alg16 / (v * 1e-3) / 1e9, 2) for k, v in extra.items()},
-        "fp8_blk128_gbs_16_rows": None if args.headline_only else extra_fp8,
+        "fp8_blk128_gbs_by_rows": None if args.headline_only else extra_fp8,
+        "greedy_verify": None if args.headline_only else greedy,
         "roofline": {
             "bound": "hbm",
             "kernel": "vq::walk_kernel (Q4_0 panel layout, bf16 activations, grouped per layer)",

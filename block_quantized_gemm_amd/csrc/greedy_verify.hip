@@ -81,41 +81,89 @@ __device__ __forceinline__ uint64_t block_max(uint64_t k, uint64_t *red) {
     return m;
 }
 
-// One workgroup per (segment, row): the best key of logits[row][seg * len ..].
+// Best key of 8 consecutive elements of one 16-byte load (two for fp32),
+// indices from v.
+template <int DT>
+__device__ __forceinline__ uint64_t best_of_8(const void *row, int v) {
+    uint64_t best = 0;
+    if constexpr (DT == VQ_DTYPE_F32) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(static_cast<const float *>(row) + v);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(static_cast<const float *>(row) + v + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // copy the element out first: a bit_cast of a vector element read
+            // element 0 whatever i was, with this compiler
+            const uint32_t ai = a[i], bi = b[i];
+            const uint64_t ka = key_of(__builtin_bit_cast(float, ai), v + i);
+            const uint64_t kb = key_of(__builtin_bit_cast(float, bi), v + 4 + i);
+            best = ka > best ? ka : best;
+            best = kb > best ? kb : best;
+        }
+    } else {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(row) + v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint16_t h = (uint16_t)(a[i >> 1] >> (16 * (i & 1)));
+            const float x = DT == VQ_DTYPE_BF16 ? __builtin_bit_cast(float, (uint32_t)h << 16)
+                                                : static_cast<float>(__builtin_bit_cast(_Float16, h));
+            const uint64_t k = key_of(x, v + i);
+            best = k > best ? k : best;
+        }
+    }
+    return best;
+}
+
+// One workgroup per (segment, row): the best key of the row's elements
+// [seg * seg_len, (seg + 1) * seg_len); seg_len is a multiple of 8, so a
+// segment of a row that starts 16-byte aligned is read with 16-byte loads
+// (scalar loads for an unaligned row and for the row's last few elements).
 template <int DT>
 __global__ __launch_bounds__(kGvThreads) void argmax_segments(const void *logits, int vocab, int seg_len,
                                                               uint64_t *part) {
     __shared__ uint64_t red[kGvThreads / 64];
+    constexpr int kElem = DT == VQ_DTYPE_F32 ? 4 : 2;
     const int seg = (int)blockIdx.x, row = (int)blockIdx.y;
     const int v0 = seg * seg_len, v1 = min(vocab, v0 + seg_len);
-    const int64_t base = (int64_t)row * vocab;
+    const char *rowp = static_cast<const char *>(logits) + (int64_t)row * vocab * kElem;
+    const bool vec = (reinterpret_cast<uintptr_t>(rowp) & 15) == 0;
     uint64_t best = 0;  // below every element's key: the high word of a key is at least key(-inf) > 0
-    for (int v = v0 + (int)threadIdx.x; v < v1; v += kGvThreads) {
-        const uint64_t k = key_of(logit_at<DT>(logits, base + v), v);
-        best = k > best ? k : best;
+    for (int v = v0 + 8 * (int)threadIdx.x; v < v1; v += 8 * kGvThreads) {
+        if (vec && v + 8 <= v1) {
+            const uint64_t k = best_of_8<DT>(rowp, v);
+            best = k > best ? k : best;
+        } else {
+            for (int i = v; i < min(v + 8, v1); ++i) {
+                const uint64_t k = key_of(logit_at<DT>(rowp, i), i);
+                best = k > best ? k : best;
+            }
+        }
     }
     best = block_max(best, red);
     if (threadIdx.x == 0)
         part[(int64_t)row * gridDim.x + seg] = best;
 }
 
-// One workgroup: every row's choice from its segments, then the committed
-// count: the leading rows whose drafted token equals the choice, plus one.
-__global__ __launch_bounds__(kGvThreads) void greedy_finish(const uint64_t *part, int nseg, int n_rows,
-                                                            const int32_t *draft, int32_t *tokens,
-                                                            int32_t *count) {
-    __shared__ uint64_t red[kGvThreads / 64];
+// One workgroup: every row's choice from its segments (one wave per row at a
+// time, the rows in parallel), then the committed count: the leading rows
+// whose drafted token equals the choice, plus one.
+constexpr int kFinishThreads = 1024;
+
+__global__ __launch_bounds__(kFinishThreads) void greedy_finish(const uint64_t *part, int nseg, int n_rows,
+                                                                const int32_t *draft, int32_t *tokens,
+                                                                int32_t *count) {
     __shared__ int first_miss;
+    const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
     if (threadIdx.x == 0)
         first_miss = n_rows - 1;
-    for (int r = 0; r < n_rows; ++r) {
+    __syncthreads();
+    for (int r = wave; r < n_rows; r += kFinishThreads / 64) {
         uint64_t best = 0;
-        for (int s = (int)threadIdx.x; s < nseg; s += kGvThreads) {
+        for (int s = lane; s < nseg; s += 64) {
             const uint64_t k = part[(int64_t)r * nseg + s];
             best = k > best ? k : best;
         }
-        best = block_max(best, red);
-        if (threadIdx.x == 0) {
+        best = wave_max(best);
+        if (lane == 0) {
             const int32_t choice = (int32_t)~(uint32_t)best;
             tokens[r] = choice;
             if (r < n_rows - 1 && draft[r] != choice)
@@ -131,10 +179,10 @@ template <int DT>
 hipError_t launch_dt(const void *logits, int n_rows, int vocab, const int32_t *draft, int32_t *tokens,
                      int32_t *count, uint64_t *part, hipStream_t stream) {
     const int nseg = greedy_segments(vocab);
-    const int seg_len = (vocab + nseg - 1) / nseg;
+    const int seg_len = ((vocab + nseg - 1) / nseg + 7) & ~7;  // whole 16-byte loads inside a segment
     hipLaunchKernelGGL(argmax_segments<DT>, dim3(nseg, n_rows), dim3(kGvThreads), 0, stream, logits, vocab, seg_len,
                        part);
-    hipLaunchKernelGGL(greedy_finish, dim3(1), dim3(kGvThreads), 0, stream, part, nseg, n_rows, draft, tokens,
+    hipLaunchKernelGGL(greedy_finish, dim3(1), dim3(kFinishThreads), 0, stream, part, nseg, n_rows, draft, tokens,
                        count);
     return hipGetLastError();
 }
