@@ -61,6 +61,7 @@ SIGNATURES = {
     "vq_gemm_q4_0_panel_ex": (_I, [_P, _P, _I, _P, _I, _I64, _I64, _I64, _F, _I, _P, _SZ, _P]),
     "vq_gemm_q4_0_panel_grouped": (_I, [_P, _I, _I, _I, _I64, _F, _P, _SZ, _P]),
     "vq_greedy_verify": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "vq_q4_0_rotate_h32": (_I, [_P, _P, _I64, _I64, _P, _P, _P]),
     "vq_greedy_workspace_bytes": (_SZ, [_I64, _I64]),
     "vq_status_string": (ctypes.c_char_p, [_I]),
     "vq_version": (_I, []),
@@ -416,6 +417,25 @@ def hadamard32_quant_int8(x, q_out, scales_out, *, stream=None):
                                         _dev_ptr(scales_out, "scales_out"), N, K, _stream(stream))
     _check(st, "vq_hadamard32_quant_int8")
     return q_out, scales_out
+
+
+def q4_0_rotate_h32(codes, scales, codes_out=None, scales_out=None, *, stream=None):
+    """The offline H32 rotation of Q4_0 weights for the W4A8 path: returns the
+    rotated, requantized (codes uint8 [M][K/2], scales float16 [M][K/32])."""
+    torch = _torch()
+    M, K = codes.shape[0], codes.shape[1] * 2
+    _check_2d(scales, "scales", (M, K // 32))
+    if codes_out is None:
+        codes_out = torch.empty_like(codes)
+    if scales_out is None:
+        scales_out = torch.empty_like(scales)
+    _check_2d(codes_out, "codes_out", (M, K // 2))
+    _check_2d(scales_out, "scales_out", (M, K // 32))
+    st = lib().vq_q4_0_rotate_h32(_dev_ptr(codes, "codes"), _dev_ptr(scales, "scales"), M, K,
+                                  _dev_ptr(codes_out, "codes_out"), _dev_ptr(scales_out, "scales_out"),
+                                  _stream(stream))
+    _check(st, "vq_q4_0_rotate_h32")
+    return codes_out, scales_out
 
 
 def greedy_workspace_bytes(n_rows: int, vocab: int) -> int:

@@ -89,6 +89,98 @@ __global__ __launch_bounds__(256) void h32_quant_kernel(const uint16_t *__restri
     }
 }
 
+// ---------------------------------------------------------------------------
+// Offline rotation of Q4_0 weights (same section of the same page: the weights
+// are rotated once, offline, by the same transform, so that the rotated
+// product divided by 32 is the plain one; the pages' tool turns a plain Q4_0
+// file into the rotated one).  Per (row, 32-block), 8 lanes as above: lane p
+// holds k = 4p .. 4p + 3, i.e. dword p & 3 of the block's 16 code bytes, low
+// nibbles for p < 4 and high nibbles for p >= 4 (byte i holds k = i and
+// k = 16 + i).  Dequantize exactly (fp16 scale times q - 8), rotate with the
+// butterflies above, then requantize by the Q4_0 rule: m = the value of
+// largest magnitude (the first one on ties), d = m / -8, id = d != 0 ? 1 / d
+// : 0, q = min(15, trunc(x * id + 8.5)), each step one IEEE fp32 operation
+// (contraction into FMAs is off in this kernel), d stored as fp16 with
+// round-to-nearest-even.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void q4_rotate_h32_kernel(const uint32_t *__restrict__ codes,
+                                                             const uint16_t *__restrict__ scales,
+                                                             uint32_t *__restrict__ codes_out,
+                                                             uint16_t *__restrict__ scales_out,
+                                                             int64_t total_blocks) {
+    // every multiply and add below is its own IEEE operation: a fused
+    // u * id + 8.5 would round once instead of twice and move some codes
+#pragma clang fp contract(off)
+    const int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t blk = gl >> 3;  // (row, block); a row's blocks are contiguous in both arrays
+    const int p = (int)(gl & 7);
+    const bool valid = blk < total_blocks;
+
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+        const uint32_t word = codes[blk * 4 + (p & 3)];
+        const float d0 = h2f(scales[blk]);
+        const uint32_t nib = p < 4 ? word : word >> 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = d0 * (float)((int)((nib >> (8 * i)) & 0xFu) - 8);  // exact
+    }
+    // h = 1, 2 in registers, h = 4, 8, 16 across the 8 lanes
+    const float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
+    float u[4] = {a0 + a2, a1 + a3, a0 - a2, a1 - a3};
+#pragma unroll
+    for (int mask = 1; mask <= 4; mask <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            u[i] = butterfly(u[i], p, mask);
+    }
+    // the value of largest magnitude, the first on ties: max of
+    // (|u| bits, 31 - k, sign) over the block
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t ub = __builtin_bit_cast(uint32_t, u[i]);
+        const uint64_t key = ((uint64_t)(ub & 0x7FFFFFFFu) << 32) | ((uint32_t)(31 - (4 * p + i)) << 1) | (ub >> 31);
+        best = key > best ? key : best;
+    }
+#pragma unroll
+    for (int mask = 1; mask <= 4; mask <<= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)best, mask, 64);
+        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), mask, 64);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        best = o > best ? o : best;
+    }
+    // a block of zeros has m = +0 (whatever the zeros' signs), so d = -0
+    const uint32_t mag = (uint32_t)(best >> 32);
+    const float m = mag == 0 ? 0.0f : __builtin_bit_cast(float, mag | ((uint32_t)(best & 1u) << 31));
+    const float d = m / -8.0f;
+    const float id = d != 0.0f ? 1.0f / d : 0.0f;  // correctly rounded (IEEE fp32 division)
+    uint32_t q4 = 0;                                // this lane's 4 codes, one per byte
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float t = u[i] * id;
+        const float r = t + 8.5f;
+        const int qi = (int)r;                      // r >= 0: truncation is floor
+        q4 |= (uint32_t)(qi > 15 ? 15 : qi) << (8 * i);
+    }
+    const uint32_t hi4 = __shfl_xor(q4, 4, 64);     // lanes p and p + 4 share the code bytes
+    if (valid && p < 4) {
+        codes_out[blk * 4 + p] = q4 | (hi4 << 4);
+        if (p == 0)
+            scales_out[blk] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(d));
+    }
+}
+
+hipError_t launch_q4_rotate_h32(const void *codes, const void *scales, int M, int K, void *codes_out,
+                                void *scales_out, hipStream_t stream) {
+    const int64_t total_blocks = (int64_t)M * (K / 32);
+    const int64_t grid = (total_blocks * 8 + 255) / 256;
+    hipLaunchKernelGGL(q4_rotate_h32_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       static_cast<const uint32_t *>(codes), static_cast<const uint16_t *>(scales),
+                       static_cast<uint32_t *>(codes_out), static_cast<uint16_t *>(scales_out), total_blocks);
+    return hipGetLastError();
+}
+
 hipError_t launch_h32_quant(const void *x, int x_dtype, int8_t *q, void *d, int N, int K,
                             hipStream_t stream) {
     const int64_t total_blocks = (int64_t)N * (K / 32);

@@ -336,6 +336,23 @@ int vq_hadamard32_quant_int8(const void *x, int x_dtype, int8_t *q_out, void *sc
                : VQ_ERR_LAUNCH;
 }
 
+int vq_q4_0_rotate_h32(const void *w_codes, const void *w_scales, int64_t m, int64_t k, void *codes_out,
+                       void *scales_out, void *stream) {
+    if (!w_codes || !w_scales || !codes_out || !scales_out)
+        return VQ_ERR_NULL_POINTER;
+    if (!dim_ok(m) || !dim_ok(k) || k % 32 != 0)
+        return VQ_ERR_BAD_SHAPE;
+    if (!aligned16(w_codes) || !aligned16(w_scales) || !aligned16(codes_out) || !aligned16(scales_out))
+        return VQ_ERR_MISALIGNED;
+    const int dev = check_device();
+    if (dev != VQ_OK)
+        return dev;
+    return vq::launch_q4_rotate_h32(w_codes, w_scales, (int)m, (int)k, codes_out, scales_out,
+                                    static_cast<hipStream_t>(stream)) == hipSuccess
+               ? VQ_OK
+               : VQ_ERR_LAUNCH;
+}
+
 static bool query_ok(int kind, int64_t m, int64_t k) {
     return (kind == VQ_KIND_Q4_0 || kind == VQ_KIND_FP8_BLK128 || kind == VQ_KIND_Q4_0_PANEL) && dim_ok(m) &&
            dim_ok(k) && k % (kind == VQ_KIND_FP8_BLK128 ? 128 : 32) == 0;

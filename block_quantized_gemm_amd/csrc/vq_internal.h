@@ -99,5 +99,7 @@ hipError_t launch_greedy_verify(const void *logits, int dtype, int n_rows, int v
 hipError_t launch_w4a8(const W4A8Args &p);
 hipError_t launch_h32_quant(const void *x, int x_dtype, int8_t *q, void *d, int N, int K,
                             hipStream_t stream);
+hipError_t launch_q4_rotate_h32(const void *codes, const void *scales, int M, int K, void *codes_out,
+                                void *scales_out, hipStream_t stream);
 
 }  // namespace vq

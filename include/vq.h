@@ -171,6 +171,30 @@ int vq_hadamard32_quant_int8(const void *x, int x_dtype,
                              int64_t n_rows, int64_t k, void *stream);
 
 /*
+ * vq_q4_0_rotate_h32 -- the offline weight rotation of the W4A8 path [P4]
+ * ("we rotate the weights the same way once, offline, so the product is
+ * unchanged"; the pages' tool turns a plain Q4_0 file into the rotated one).
+ * For every row and 32-block of the Q4_0 matrix (w_codes, w_scales), in the
+ * layout of vq_gemm_q4_0:
+ *   x = d * (q - 8) exactly in fp32, then u = H32 x by the butterflies of
+ *   vq_hadamard32_quant_int8 (fp32, h = 1, 2, 4, 8, 16);
+ *   m = the u of largest magnitude (the first on ties; +0 for a block of
+ *   zeros), d' = m / -8, id = d' != 0 ? 1 / d' : 0,
+ *   q' = min(15, trunc(u * id + 8.5)) -- the Q4_0 rule of the GGUF files the
+ *   pages use (the library's reading); every step one IEEE fp32 operation;
+ *   written as Q4_0: codes_out u8 [M][K/2], scales_out f16 [M][K/32] = d'
+ *   rounded to nearest even.
+ * Then vq_gemm_q4_0 with these weights, int8 activations from
+ * vq_hadamard32_quant_int8 and alpha = 1/32 approximates the unrotated
+ * product; the rotated weights carry a requantization error of at most one
+ * level (half a level inside the range).  Input scales must be finite; a
+ * rotated scale beyond the fp16 range is stored as +-inf.  Outputs must not
+ * alias inputs.  Sizes: 1 <= M, K <= VQ_MAX_DIM, K % 32 == 0.
+ */
+int vq_q4_0_rotate_h32(const void *w_codes, const void *w_scales, int64_t m, int64_t k,
+                       void *codes_out, void *scales_out, void *stream);
+
+/*
  * Grouped verify GEMMs -- several independent problems in as few kernel
  * launches as possible ([P1]: a block is verified by one batched pass over
  * all the weights; [P3]: the decode step is replayed as one HIP graph).  A

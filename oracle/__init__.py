@@ -84,6 +84,8 @@ def _load():
         lib.vqo_h32_matrix.argtypes = [P]
         lib.vqo_h32_quant_int8.restype = ctypes.c_int
         lib.vqo_h32_quant_int8.argtypes = [P, ctypes.c_int, I64, I64, P, P]
+        lib.vqo_q4_0_rotate_h32.restype = None
+        lib.vqo_q4_0_rotate_h32.argtypes = [P, P, I64, I64, P, P]
         lib.vqo_greedy_verify.restype = I64
         lib.vqo_greedy_verify.argtypes = [P, ctypes.c_int, I64, I64, P, P]
         _lib = lib
@@ -235,3 +237,17 @@ def greedy_verify(logits, dtype, draft):
     target = np.zeros(n, dtype=np.int32)
     count = lib.vqo_greedy_verify(_ptr(lg), dtype, n, v, _ptr(d) if d.size else None, _ptr(target))
     return target, int(count)
+
+
+# ---------------------------------------------------------------- offline H32 rotation of Q4_0 weights
+
+def q4_0_rotate_h32(codes, scales, M, K):
+    """(codes, scales) of the H32-rotated, requantized Q4_0 matrix; see
+    vqo_q4_0_rotate_h32."""
+    lib = _load()
+    c = _c(codes, np.uint8)
+    s = _c(scales, np.uint16)
+    co = np.zeros((M, K // 2), dtype=np.uint8)
+    so = np.zeros((M, K // 32), dtype=np.uint16)
+    lib.vqo_q4_0_rotate_h32(_ptr(c), _ptr(s), M, K, _ptr(co), _ptr(so))
+    return co, so

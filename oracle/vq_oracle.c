@@ -38,6 +38,13 @@
  *    restored by alpha = 1/32.
  *  - int8 activation quantizer: d = fp16_rne(amax / 127) computed in fp32,
  *    q = clamp(rint_half_even(u / d), -127, 127), amax == 0 gives d = 0, q = 0.
+ *  - H32 rotation of Q4_0 weights ([P4]: "we rotate the weights the same way
+ *    once, offline"; the pages' tool makes a rotated Q4_0 file from a plain
+ *    one): per 32-block, dequantize exactly in fp32, H32 by the butterflies
+ *    above, requantize to Q4_0 by the rule of the GGUF Q4_0 format the pages'
+ *    files use: m = the block's value of largest magnitude (the first one on
+ *    ties), d = m / -8, id = d != 0 ? 1 / d : 0, q = min(15, trunc(x * id +
+ *    8.5)), each a single fp32 operation, d stored as fp16_rne(d).
  *  - greedy verification: logits row i is the target's prediction for block
  *    position i (row 0 follows the last committed token, row i the drafted
  *    token i - 1); the target's choice in a row is its argmax, the first NaN
@@ -407,4 +414,50 @@ int64_t vqo_greedy_verify(const void *logits, int dtype, int64_t n_rows, int64_t
     while (a < n_rows - 1 && draft[a] == target[a])
         ++a;
     return a + 1;
+}
+
+/* ------------------------------------------------------------------ */
+/* Offline H32 rotation of Q4_0 weights                                */
+/* ------------------------------------------------------------------ */
+
+/* [P4] "Prompt processing: 4-bit activations, rotated first": the weights
+ * are rotated once, offline, by the same 32-point Walsh-Hadamard transform
+ * as the activations, so that the rotated product (divided by 32) equals the
+ * plain one.  Input and output: Q4_0 codes [M][K/2] and fp16 scales [M][K/32]
+ * in the layout read by vqo_q4_0_code.  Per block, in fp32: exact dequantized
+ * values, the butterflies of vqo_fwht32_f32, then the Q4_0 rule stated in the
+ * header (every step one IEEE fp32 operation; fp-contract is off). */
+void vqo_q4_0_rotate_h32(const uint8_t *codes, const uint16_t *scales, int64_t M, int64_t K,
+                         uint8_t *codes_out, uint16_t *scales_out)
+{
+    const int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float d0 = (float)vqo_f16_to_f64(scales[m * nb + b]);
+            float x[32];
+            for (int j = 0; j < 32; ++j)
+                x[j] = d0 * (float)(vqo_q4_0_code(codes, K, m, 32 * b + j) - 8); /* exact */
+            vqo_fwht32_f32(x);
+            float amax = 0.0f, mx = 0.0f;
+            for (int j = 0; j < 32; ++j)
+                if (fabsf(x[j]) > amax) {        /* strictly larger: the first on ties */
+                    amax = fabsf(x[j]);
+                    mx = x[j];
+                }
+            const float d = mx / -8.0f;
+            const float id = d != 0.0f ? 1.0f / d : 0.0f;
+            uint8_t q[32];
+            for (int j = 0; j < 32; ++j) {
+                const float t = x[j] * id;
+                const float u = t + 8.5f;
+                const int qi = (int)u;            /* u >= 0: truncation is floor */
+                q[j] = (uint8_t)(qi > 15 ? 15 : qi);
+            }
+            /* byte i of the block: k = i in the low nibble, k = 16 + i in the high */
+            for (int i = 0; i < 16; ++i)
+                codes_out[m * (K / 2) + 16 * b + i] = (uint8_t)(q[i] | (q[16 + i] << 4));
+            scales_out[m * nb + b] = vqo_f32_to_f16_rne(d);
+        }
+    }
 }

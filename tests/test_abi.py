@@ -267,3 +267,14 @@ def test_greedy_argument_errors_and_workspace_query():
     assert call(wb=16 * 8 - 8) == vq.VQ_ERR_WORKSPACE
     if not torch.cuda.is_available():
         assert call(n=1, d=None) == vq.VQ_ERR_DEVICE   # a one-row block needs no draft
+
+
+def test_rotate_argument_errors():
+    f = vq.lib().vq_q4_0_rotate_h32
+    assert f(None, B, 256, 512, C, D, None) == vq.VQ_ERR_NULL_POINTER
+    assert f(A, B, 256, 512, C, None, None) == vq.VQ_ERR_NULL_POINTER
+    assert f(A, B, 256, 500, C, D, None) == vq.VQ_ERR_BAD_SHAPE
+    assert f(A, B, 0, 512, C, D, None) == vq.VQ_ERR_BAD_SHAPE
+    assert f(A, B + 2, 256, 512, C, D, None) == vq.VQ_ERR_MISALIGNED
+    if not torch.cuda.is_available():
+        assert f(A, B, 256, 512, C, D, None) == vq.VQ_ERR_DEVICE

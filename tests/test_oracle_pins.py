@@ -466,3 +466,88 @@ def test_greedy_commits_the_accepted_prefix_plus_one():
         assert count == a + 1
     t, count = oracle.greedy_verify(logits[:1], oracle.F32, np.zeros(0, np.int32))
     assert count == 1 and t[0] == choice[0]   # a block of one row commits the target's token
+
+
+# ------------------------------------------------------------ offline H32 rotation of Q4_0 weights
+
+
+def _dequant_np(codes, scales, M, K):
+    q = _unpack_codes(codes, K).astype(np.float64)
+    return (q - 8) * np.repeat(_np_f16(scales), 32, axis=1)
+
+
+def test_rotation_requantizes_to_the_nearest_level():
+    """Per block: the rotated values are H32 w (exact here: every value is the
+    block scale times an integer); the new scale is fp16(m / -8) for the value
+    m of largest magnitude; every code is the nearest of the 16 levels d (q - 8)
+    (rounding half up, 15 at the top), checked in fp64 away from exact ties."""
+    import scipy.linalg
+    g = np.random.Generator(np.random.PCG64(61))
+    M, K = 24, 256
+    codes = g.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    scales = W.f32_to_f16_bits(g.lognormal(-5, 0.5, size=(M, K // 32)) * g.choice([-1, 1], size=(M, K // 32)))
+    codes[3, 16:32] = 0x88                       # a block of zeros (codes 8)
+    co, so = oracle.q4_0_rotate_h32(codes, scales, M, K)
+    H = scipy.linalg.hadamard(32).astype(np.float64)
+    w = _dequant_np(codes, scales, M, K).reshape(M, K // 32, 32)
+    x = w @ H.T                                   # H32 applied to every block
+    qn = _unpack_codes(co, K).reshape(M, K // 32, 32)
+    dn = _np_f16(so)
+    for m in range(M):
+        for b in range(K // 32):
+            xb = x[m, b]
+            j = int(np.argmax(np.abs(xb)))       # first of the largest magnitudes
+            d = xb[j] / -8.0
+            assert dn[m, b] == np.float64(np.float16(d)), (m, b)
+            if d == 0:
+                assert (qn[m, b] == 8).all()
+                continue
+            t = xb / d + 8.5
+            ref = np.minimum(15, np.floor(t))
+            near_tie = np.abs(t - np.round(t)) < 1e-5
+            assert np.array_equal(qn[m, b][~near_tie], ref[~near_tie]), (m, b)
+            assert qn[m, b][j] == 0
+    assert dn[3, 1] == 0 and (qn[3, 1] == 8).all()
+
+
+def test_rotation_round_trips_one_hot_blocks_and_keeps_products():
+    """A block c * e_0 rotates to c in every position, which requantizes exactly
+    (code 0 at d = c / -8), so H32 of the result / 32 gives the block back; a
+    block c * e_j with j > 0 rotates to +-c, and the -c side lands on the top
+    code 15 (7 d = -7c/8: the 16 levels stop at +7); for general blocks the
+    rotated product / 32 stays within the requantization bound of the plain
+    product."""
+    import scipy.linalg
+    H = scipy.linalg.hadamard(32).astype(np.float64)
+    M, K = 8, 32
+    codes = np.full((M, K // 2), 0x88, dtype=np.uint8)
+    codes[:, 0] = 0x8F                           # code 15 (+7 d) at k = 0
+    codes[5, 0] = 0x80                           # code 0 (-8 d) at k = 0
+    scales = W.f32_to_f16_bits(np.array([[2.0 ** -e] for e in range(4, 12)]))
+    co, so = oracle.q4_0_rotate_h32(codes, scales, M, K)
+    w = _dequant_np(codes, scales, M, K)
+    wr = _dequant_np(co, so, M, K)
+    assert np.array_equal(wr @ H.T / 32, w)
+    one = np.full((1, 16), 0x88, dtype=np.uint8)
+    one[0, 3] = 0x8F                             # c * e_3
+    co, so = oracle.q4_0_rotate_h32(one, np.array([[0x2C00]], np.uint16), 1, 32)
+    c = 7 * 2.0 ** -4
+    assert np.array_equal(_dequant_np(co, so, 1, 32)[0], np.where(H[:, 3] > 0, c, -7 * c / 8))
+    g = np.random.Generator(np.random.PCG64(62))
+    M, K = 16, 512
+    codes = g.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    scales = W.f32_to_f16_bits(g.lognormal(-5, 0.5, size=(M, K // 32)))
+    co, so = oracle.q4_0_rotate_h32(codes, scales, M, K)
+    w = _dequant_np(codes, scales, M, K).reshape(M, K // 32, 32)
+    wr = _dequant_np(co, so, M, K).reshape(M, K // 32, 32)
+    # requantization error per element: half a level inside the range, and up
+    # to a whole level where -m lands on the top code 15; the stored scale is
+    # d rounded to fp16, which moves the levels by up to 8 * 2^-11 of a level
+    err = np.abs(wr - w @ H.T)
+    assert (err <= np.abs(_np_f16(so))[..., None] * 1.005).all()
+    xv = g.standard_normal((3, K))
+    xr = (xv.reshape(3, K // 32, 32) @ H.T).reshape(3, K)
+    plain = xv @ w.reshape(M, K).T
+    rotated = xr @ wr.reshape(M, K).T / 32
+    bound = (np.abs(xr) @ (np.abs(_np_f16(so)).repeat(32, axis=1)).T) / 32
+    assert (np.abs(rotated - plain) <= bound * 1.005).all()
