@@ -354,13 +354,17 @@ def prefill_bench(args):
     p = W.prefill()
     N, M, K = p["N"], p["M"], p["K"]
     dev = torch.device("cuda:0")
-    codes = torch.from_numpy(p["codes"]).to(dev)
-    scales = torch.from_numpy(p["scales"].view(np.int16).copy()).to(dev).view(torch.float16)
+    codes0 = torch.from_numpy(p["codes"]).to(dev)
+    scales0 = torch.from_numpy(p["scales"].view(np.int16).copy()).to(dev).view(torch.float16)
     x = torch.from_numpy(p["act"].view(np.int16).copy()).to(dev).view(torch.bfloat16)
     q = torch.empty((N, K), dtype=torch.int8, device=dev)
     d = torch.empty((N, K // 32), dtype=torch.float16, device=dev)
     out = torch.empty((N, M), dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream()
+    # the path's weights: the plain Q4_0 matrix rotated once, offline
+    codes = torch.empty_like(codes0)
+    scales = torch.empty_like(scales0)
+    t_rot = time_ms(lambda s: vq.q4_0_rotate_h32(codes0, scales0, codes, scales, stream=s), stream, 3, 1, graph=False)
 
     def quant(s):
         vq.hadamard32_quant_int8(x, q, d, stream=s)
@@ -377,6 +381,14 @@ def prefill_bench(args):
     t_b = time_ms(both, stream, args.steps, args.warmup, graph=True)
     ops = 2.0 * N * M * K
     tops = ops / (t_g * 1e-3) / 1e12
+    # error of the rotated W4A8 result against the bf16-row verify GEMM on the
+    # plain weights (itself within ~1e-6 of the exact product)
+    with torch.cuda.stream(stream):
+        both(stream)
+    ref = torch.empty((N, M), dtype=torch.float32, device=dev)
+    vq.gemm_q4_0(codes0, scales0, x, ref, stream=stream)
+    torch.cuda.synchronize()
+    rel = float(torch.linalg.norm((out - ref).double()) / torch.linalg.norm(ref.double()))
     result = {
         "metric": "W4A8 prefill int8-MFMA TOPS",
         "value": round(tops, 2),
@@ -385,10 +397,12 @@ def prefill_bench(args):
         "dtype": "i8",
         "data": "synthetic (Q4_0 codes uniform, fp16 scales lognormal; bf16 rows Student-t with outlier channels)",
         "config": {"workload": "W4A8 prefill: %d bf16 rows x K=%d, H32 int8 quantizer, then Q4_0 %d x %d "
-                               "int8-MFMA GEMM, fp32 out" % (N, K, M, K)},
+                               "(H32-rotated offline) int8-MFMA GEMM, fp32 out" % (N, K, M, K)},
         "gemm_us": round(t_g * 1e3, 2),
         "quantizer_us": round(t_q * 1e3, 2),
         "quantizer_plus_gemm_us": round(t_b * 1e3, 2),
+        "offline_rotation_us": round(t_rot * 1e3, 2),
+        "rel_error_vs_bf16_rows": round(rel, 4),
         "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_MFMA_PEAK_TOPS, "unit": "TOPS",
                      "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "ops_per_launch": ops},
     }
