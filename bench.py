@@ -273,6 +273,7 @@ def traffic_from(fetch_dir, write_dir):
 
 
 INT8_MFMA_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA, published
 
 
 def fp8_forms(stream, args):
@@ -389,6 +390,7 @@ def prefill_bench(args):
     vq.gemm_q4_0(codes0, scales0, x, ref, stream=stream)
     torch.cuda.synchronize()
     rel = float(torch.linalg.norm((out - ref).double()) / torch.linalg.norm(ref.double()))
+    fp8 = fp8_prefill_form(stream, args, N)
     result = {
         "metric": "W4A8 prefill int8-MFMA TOPS",
         "value": round(tops, 2),
@@ -405,8 +407,38 @@ def prefill_bench(args):
         "rel_error_vs_bf16_rows": round(rel, 4),
         "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_MFMA_PEAK_TOPS, "unit": "TOPS",
                      "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "ops_per_launch": ops},
+        "fp8_prefill": fp8,
     }
     print(json.dumps(result))
+
+
+def fp8_prefill_form(stream, args, N):
+    """The FP8 block-scaled GEMM over N bf16 rows at 17408 x 5120 (the FP8
+    workload's distributions) on the MFMA-tiled kernel, against the bf16 MFMA
+    peak; the verify kernel on the same rows (16 at a time) for context."""
+    import numpy as np
+    import torch
+    import block_quantized_gemm_amd as vq
+    import workloads as W
+    dev = torch.device("cuda:0")
+    f = W.fp8(M=17408, K=5120, N=16)
+    M, K = f["M"], f["K"]
+    w = torch.from_numpy(f["w"]).to(dev)
+    ts = torch.from_numpy(f["tscales"]).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    x = torch.randn((N, K), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((N, M), dtype=torch.bfloat16, device=dev)
+    t_p = time_ms(lambda s: vq.gemm_fp8_blk128_prefill(w, ts, x, out, stream=s), stream, args.steps, args.warmup, True)
+    t_v = time_ms(lambda s: vq.gemm_fp8_blk128(w, ts, x, out, stream=s), stream, max(2, args.steps // 2),
+                  args.warmup, True)
+    flops = 2.0 * N * M * K
+    tf = flops / (t_p * 1e-3) / 1e12
+    return {"workload": "FP8 block-scaled prefill: %d bf16 rows x 17408 x 5120, bf16 out" % N,
+            "gemm_us": round(t_p * 1e3, 2), "tflops": round(tf, 2),
+            "verify_kernel_us": round(t_v * 1e3, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "flops_per_launch": flops}}
 
 
 def main():

@@ -47,6 +47,7 @@ SIGNATURES = {
     "vq_gemm_q4_0": (_I, [_P, _P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _F, _P, _SZ, _P]),
     "vq_gemm_fp8_blk128": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
     "vq_hadamard32_quant_int8": (_I, [_P, _I, _P, _P, _I64, _I64, _P]),
+    "vq_gemm_fp8_blk128_prefill": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P]),
     "vq_workspace_bytes": (_SZ, [_I, _I64, _I64]),
     "vq_gemm_q4_0_ex": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _F, _I, _I, _I, _P, _SZ, _P]),
     "vq_gemm_fp8_blk128_ex": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _I, _I, _I, _P, _SZ, _P]),
@@ -318,6 +319,22 @@ def gemm_q4_0_panel(panel, m: int, k: int, x, out, *, alpha: float = 1.0, worksp
         st = L.vq_gemm_q4_0_panel(_dev_ptr(panel, "panel"), _dev_ptr(x, "x"), _dtype_code(x),
                                   _dev_ptr(out, "out"), _dtype_code(out), N, m, k, float(alpha), wp, wn, sh)
         _check(st, "vq_gemm_q4_0_panel")
+    return out
+
+
+def gemm_fp8_blk128_prefill(w, tile_scales, x, out, *, stream=None):
+    """gemm_fp8_blk128 for prompt-sized row counts (the MFMA-tiled kernel):
+    w uint8 [M][K] (E4M3FN), tile_scales float32 [ceil(M/128)][K/128], x
+    float16 / bfloat16 [N][K], out float16 / bfloat16 / float32 [N][M]."""
+    N, K = x.shape
+    M = w.shape[0]
+    _check_2d(w, "w", (M, K))
+    _check_2d(tile_scales, "tile_scales", ((M + 127) // 128, K // 128))
+    _check_2d(out, "out", (N, M))
+    st = lib().vq_gemm_fp8_blk128_prefill(_dev_ptr(w, "w"), _dev_ptr(tile_scales, "tile_scales"), _dev_ptr(x, "x"),
+                                          _dtype_code(x), _dev_ptr(out, "out"), _dtype_code(out), N, M, K,
+                                          _stream(stream))
+    _check(st, "vq_gemm_fp8_blk128_prefill")
     return out
 
 

@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libvq.so")
 
-SOURCES = ["verify_gemm.hip", "w4a8_gemm.hip", "h32_quant.hip", "greedy_verify.hip", "vq_api.cpp"]
+SOURCES = ["verify_gemm.hip", "w4a8_gemm.hip", "fp8_prefill.hip", "h32_quant.hip", "greedy_verify.hip",
+           "vq_api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -306,6 +306,23 @@ int vq_gemm_fp8_blk128(const void *w_e4m3, const float *w_tile_scales, const voi
                       1.0f, 0, 0, 0, workspace, workspace_bytes, stream);
 }
 
+int vq_gemm_fp8_blk128_prefill(const void *w_e4m3, const float *w_tile_scales, const void *act, int act_dtype,
+                               void *out, int out_dtype, int64_t n_rows, int64_t m, int64_t k, void *stream) {
+    const int st = check_problem(true, w_e4m3, w_tile_scales, act, out, m, k);
+    if (st != VQ_OK)
+        return st;
+    if (!float_act(act_dtype) || !out_ok(out_dtype))
+        return VQ_ERR_BAD_DTYPE;
+    if (!dim_ok(n_rows))
+        return VQ_ERR_BAD_SHAPE;
+    const int dev = check_device();
+    if (dev != VQ_OK)
+        return dev;
+    const vq::Fp8PrefillArgs p{w_e4m3, w_tile_scales, act, act_dtype, out, out_dtype, (int)n_rows, (int)m, (int)k,
+                               static_cast<hipStream_t>(stream)};
+    return vq::launch_fp8_prefill(p) == hipSuccess ? VQ_OK : VQ_ERR_LAUNCH;
+}
+
 int vq_gemm_fp8_blk128_ex(const void *w_e4m3, const float *w_tile_scales, const void *act,
                           int act_dtype, void *out, int out_dtype, int64_t n_rows, int64_t m,
                           int64_t k, int tiles_per_wave, int waves_per_group, int max_groups,

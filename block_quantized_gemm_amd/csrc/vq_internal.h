@@ -97,6 +97,19 @@ hipError_t launch_greedy_verify(const void *logits, int dtype, int n_rows, int v
                                 int32_t *tokens, int32_t *count, void *workspace, hipStream_t stream);
 
 hipError_t launch_w4a8(const W4A8Args &p);
+
+// Arguments of one FP8 prefill launch (16-bit activations, many rows).
+struct Fp8PrefillArgs {
+    const void *w;
+    const float *tile_scales;
+    const void *act;
+    int act_dtype;
+    void *out;
+    int out_dtype;
+    int N, M, K;
+    hipStream_t stream;
+};
+hipError_t launch_fp8_prefill(const Fp8PrefillArgs &p);
 hipError_t launch_h32_quant(const void *x, int x_dtype, int8_t *q, void *d, int N, int K,
                             hipStream_t stream);
 hipError_t launch_q4_rotate_h32(const void *codes, const void *scales, int M, int K, void *codes_out,

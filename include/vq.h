@@ -153,6 +153,23 @@ int vq_gemm_fp8_blk128(const void *w_e4m3, const float *w_tile_scales,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * vq_gemm_fp8_blk128_prefill -- the product of vq_gemm_fp8_blk128 for
+ * prompt-sized row counts [P3: "custom block-scaled FP8 GEMM"]: the verify
+ * kernels stream the weights once per 16 rows, this one tiles 128 rows x 128
+ * features per workgroup on the 16-bit MFMA (compute-bound at hundreds of
+ * rows).  Same arguments, layouts and sizes as vq_gemm_fp8_blk128, no
+ * workspace.  Arithmetic: E4M3 converted exactly to the activation type,
+ * exact products, fp32 sums over each 128-k tile, then one fp32 FMA with the
+ * tile scale per output and tile in ascending k -- a row's outputs depend only
+ * on that row and the weights (bit-identical for any N), but they may differ
+ * in the last bits from vq_gemm_fp8_blk128's.
+ */
+int vq_gemm_fp8_blk128_prefill(const void *w_e4m3, const float *w_tile_scales,
+                               const void *act, int act_dtype,
+                               void *out, int out_dtype,
+                               int64_t n_rows, int64_t m, int64_t k, void *stream);
+
+/*
  * vq_hadamard32_quant_int8 -- per (row n, 32-block b) of x [N][K] [P4]:
  *   u   = H32 x_b in fp32, H32 the +-1 Sylvester Walsh-Hadamard matrix applied
  *         as radix-2 butterflies h = 1, 2, 4, 8, 16 in that order

@@ -278,3 +278,13 @@ def test_rotate_argument_errors():
     assert f(A, B + 2, 256, 512, C, D, None) == vq.VQ_ERR_MISALIGNED
     if not torch.cuda.is_available():
         assert f(A, B, 256, 512, C, D, None) == vq.VQ_ERR_DEVICE
+
+
+def test_fp8_prefill_argument_errors():
+    f = vq.lib().vq_gemm_fp8_blk128_prefill
+    assert f(None, B, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 512, 256, 512, None) == vq.VQ_ERR_NULL_POINTER
+    assert f(A, B, C, vq.DTYPE_I8, D, vq.DTYPE_BF16, 512, 256, 512, None) == vq.VQ_ERR_BAD_DTYPE
+    assert f(A, B, C, vq.DTYPE_BF16, D, vq.DTYPE_I8, 512, 256, 512, None) == vq.VQ_ERR_BAD_DTYPE
+    assert f(A, B, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 512, 256, 480, None) == vq.VQ_ERR_BAD_SHAPE
+    assert f(A, B, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 0, 256, 512, None) == vq.VQ_ERR_BAD_SHAPE
+    assert f(A, B, C + 2, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 512, 256, 512, None) == vq.VQ_ERR_MISALIGNED
