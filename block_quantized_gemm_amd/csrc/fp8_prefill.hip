@@ -9,18 +9,22 @@
 //
 // Arithmetic: every E4M3 code converts exactly to bf16 / fp16 (hardware
 // conversion); the MFMA 16x16x32 multiplies it by the activations exactly and
-// sums in fp32.  Features [128 i, 128 i + 128) of a workgroup and the 128 k
-// of one chunk lie in one scale tile, so a chunk's four MFMA steps accumulate
-// a partial that is added to the output with one fp32 FMA with that tile's
-// scale -- the order the verify kernels use for each output too.
+// sums in fp32.  A 16-feature tile and the 128 k of one chunk lie in one
+// scale tile, so MFMA steps within a chunk accumulate a partial that is added
+// to the output with one fp32 FMA with that tile's scale.
 //
-// Tiling: a workgroup of 4 waves computes 128 rows x 128 features; wave
-// (wr, wf) takes rows 64 wr .. +64 and features 64 wf .. +64 as 4 x 4 MFMA
-// tiles.  K moves in chunks of 128: the chunk's activations (128 rows x 256 B)
-// and weights (128 features x 128 B) are loaded into registers while the
-// previous chunk is computed from LDS, then written to the other of two LDS
-// buffers (rows padded by 16 bytes against bank conflicts).  k-slot group g of
-// the MFMA covers k = 32 s + 8 g .. +7 of step s for both operands.
+// Tiling: a workgroup of 8 waves computes 128 rows x 288 features (18 MFMA
+// tiles; 17408 features make 61 columns, so a 512-row prompt is one round of
+// 244 workgroups on 256 CUs).  Wave (fg, rg, kh) takes features 144 fg ..
+// +144, rows 64 rg .. +64, and the MFMA steps 2 kh, 2 kh + 1 of every 128-k
+// chunk: for each output tile it sums its two steps on the MFMA and adds that
+// partial, times the chunk's tile scale, with one fp32 FMA; the two k halves
+// are added at the end (kh 0 + kh 1, fixed order), so each row's arithmetic
+// is independent of N.  Chunks (activations 128 rows x 256 B, codes 288
+// features x 128 B) are loaded straight into LDS (16 B per lane, no
+// registers) one chunk ahead, into the other of two stages; 16-byte pieces
+// are XOR-swizzled by row and by feature so that the operand reads are free
+// of bank conflicts.
 #include "vq_device.h"
 #include "vq_internal.h"
 
@@ -28,132 +32,161 @@ namespace vq {
 
 namespace {
 
-constexpr int kPfRows = 128, kPfFeats = 128, kPfK = 128;  // per workgroup and chunk
-constexpr int kPfAPitch = 2 * kPfK + 16;                  // activation bytes per row in LDS
-constexpr int kPfBPitch = kPfK + 16;                      // weight bytes per feature in LDS
-constexpr int kPfABytes = kPfRows * kPfAPitch;
-constexpr int kPfBBytes = kPfFeats * kPfBPitch;
-constexpr int kPfBuf = kPfABytes + kPfBBytes;
+constexpr int kPfRows = 128, kPfFeats = 288, kPfK = 128;  // per workgroup and chunk
+constexpr int kPfThreads = 512;
+constexpr int kPfFeatTiles = kPfFeats / 2 / 16;  // 9 tiles per wave
+constexpr int kPfAStage = kPfRows * 2 * kPfK;    // 16-bit rows, 256 B each
+constexpr int kPfBStage = kPfFeats * kPfK;       // E4M3 codes, 128 B per feature
+constexpr int kPfStage = kPfAStage + kPfBStage;
+constexpr int kPfLds = 2 * kPfStage;
+constexpr int kPfRedBytes = 4 * 2 * kPfFeatTiles * 4 * 64 * 4;  // k-half exchange, half of the row tiles
+static_assert(kPfRedBytes <= kPfLds, "reduction area");
 constexpr int kPfOut = 0x7FFFFFF0;  // past every range below: the load returns zeros
 
 template <int ACT>
-__global__ __launch_bounds__(256) void fp8_prefill_kernel(const uint8_t *__restrict__ w, const float *__restrict__ ts,
-                                                          const uint16_t *__restrict__ x, void *__restrict__ out,
-                                                          int out_dtype, int N, int M, int K) {
+__global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *__restrict__ w,
+                                                                 const float *__restrict__ ts,
+                                                                 const uint16_t *__restrict__ x,
+                                                                 void *__restrict__ out, int out_dtype, int N, int M,
+                                                                 int K) {
     using A16 = Act16<ACT>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int t = threadIdx.x, lane = t & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
-    const int wr = wave >> 1, wf = wave & 1;
+    const int lane = threadIdx.x & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
+    const int fg = wave & 1, rg = (wave >> 1) & 1, kh = wave >> 2;
     const int fb = blockIdx.x * kPfFeats, rb = blockIdx.y * kPfRows;
-    const int nch = K / kPfK;
+    const int nch = K / kPfK, nft = (M + 127) / 128;
     const int rows = min(kPfRows, N - rb), feats = min(kPfFeats, M - fb);
-    const float *trow = ts + (size_t)(fb / 128) * nch;  // this workgroup's scale tiles, one per chunk
 
-    // Activation rows in two halves of 64 (each range below 2^31 bytes), the
-    // weights of this workgroup's features; loads past them read zeros.
-    const rsrc_t ra0 = make_rsrc(x + (size_t)rb * K, (uint32_t)min(rows, 64) * (uint32_t)K * 2u);
-    const rsrc_t ra1 = make_rsrc(x + (size_t)(rb + 64) * K * (rows > 64), (uint32_t)max(rows - 64, 0) * (uint32_t)K * 2u);
-    const rsrc_t rw = make_rsrc(w + (size_t)fb * K, (uint32_t)feats * (uint32_t)K);
-
-    // one chunk: 8 activation pieces and 4 weight pieces of 16 bytes per thread
-    u32x4 ga[8], gb[4];
-    auto load_chunk = [&](int c) {
+    // Ranges: activation rows in groups of 32, codes in groups of 64
+    // features (each below 2^30 bytes); rows past N and features past M read
+    // zeros.  A wave load covers 4 rows x 256 B or 8 features x 128 B.
+    rsrc_t ra[4], rw[5];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        ra[m] = make_rsrc(x + (size_t)(rb + 32 * m) * K, (uint32_t)max(0, min(32, rows - 32 * m)) * (uint32_t)K * 2u);
+#pragma unroll
+    for (int m = 0; m < 5; ++m)
+        rw[m] = make_rsrc(w + (size_t)(fb + 64 * m) * K, (uint32_t)max(0, min(64, feats - 64 * m)) * (uint32_t)K);
+    // Lane offsets of the chunk loads (the chunk's k offset goes in the
+    // wave-uniform part).  Activation load i = wave + 8 m covers rows 4 i ..
+    // 4 i + 3 of range m (row 4 wave + lane / 16 there); code load i = wave +
+    // 8 m (< 36) covers features 8 i .. 8 i + 7 of range m (8 wave + lane / 8).
+    // The swizzle terms depend on the row or feature mod 16 only, the same
+    // for every m.
+    const int a_row = 4 * wave + (lane >> 4), b_feat = 8 * wave + (lane >> 3);
+    const int a_voff = a_row * K * 2 + 16 * ((lane & 15) ^ (a_row & 15));
+    const int b_voff = b_feat * K + 16 * ((lane & 7) ^ ((b_feat >> 1) & 7));
+    auto issue = [&](int c, int stage) {
+        uint8_t *st = lds + stage * kPfStage;
         const int k0 = c * kPfK;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int p = t + 256 * i, row = p >> 4, col = 2 * k0 + 16 * (p & 15);  // bytes
-            ga[i] = bload16<kAuxCached>(i < 4 ? ra0 : ra1, (row & 63) * K * 2 + col, 0);
-        }
+        for (int m = 0; m < 4; ++m)
+            bload16_lds(ra[m], st + 1024 * (wave + 8 * m), a_voff, 2 * k0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = t + 256 * i, f = p >> 3, col = k0 + 16 * (p & 7);
-            gb[i] = bload16<kAuxCached>(rw, f * K + col, 0);
-        }
-    };
-    auto store_chunk = [&](int buf) {
-        uint8_t *base = lds + buf * kPfBuf;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int p = t + 256 * i;
-            *reinterpret_cast<u32x4 *>(base + (p >> 4) * kPfAPitch + 16 * (p & 15)) = ga[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = t + 256 * i;
-            *reinterpret_cast<u32x4 *>(base + kPfABytes + (p >> 3) * kPfBPitch + 16 * (p & 7)) = gb[i];
-        }
+        for (int m = 0; m < 5; ++m)
+            if (wave + 8 * m < 36)
+                bload16_lds(rw[m], st + kPfAStage + 1024 * (wave + 8 * m), b_voff, k0);
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[4][kPfFeatTiles];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int ft = 0; ft < 4; ++ft)
+        for (int ft = 0; ft < kPfFeatTiles; ++ft)
             acc[rt][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    // this wave's scale tile of each feature tile (clamped: tiles past M
+    // multiply zeros)
+    int tile_of[kPfFeatTiles];
+#pragma unroll
+    for (int ft = 0; ft < kPfFeatTiles; ++ft)
+        tile_of[ft] = min((fb + fg * 144 + ft * 16) >> 7, nft - 1) * nch;
+    const int b_sw = (j >> 1) & 7;
 
-    load_chunk(0);
+    issue(0, 0);
     wait_vmcnt<0>();
-    store_chunk(0);
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
         if (c + 1 < nch)
-            load_chunk(c + 1);
-        const uint8_t *base = lds + (c & 1) * kPfBuf;
-        const uint8_t *abase = base + (wr * 64 + j) * kPfAPitch + 16 * g;
-        const uint8_t *bbase = base + kPfABytes + (wf * 64 + j) * kPfBPitch + 8 * g;
-        const float s = trow[c];
-        f32x4 part[4][4];
-#pragma unroll
-        for (int st = 0; st < kPfK / 32; ++st) {
-            u32x4 bop[4];
-#pragma unroll
-            for (int ft = 0; ft < 4; ++ft) {
-                const u32x2 wv = *reinterpret_cast<const u32x2 *>(bbase + ft * 16 * kPfBPitch + 32 * st);
-                bop[ft] = u32x4{A16::template fp8x2<false>(wv[0]), A16::template fp8x2<true>(wv[0]),
-                                A16::template fp8x2<false>(wv[1]), A16::template fp8x2<true>(wv[1])};
-            }
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const u32x4 aop = *reinterpret_cast<const u32x4 *>(abase + rt * 16 * kPfAPitch + 64 * st);
-#pragma unroll
-                for (int ft = 0; ft < 4; ++ft)
-                    part[rt][ft] = A16::mfma(aop, bop[ft], st == 0 ? zero4 : part[rt][ft]);
-            }
-        }
+            issue(c + 1, (c + 1) & 1);
+        const uint8_t *st = lds + (c & 1) * kPfStage;
+        const uint8_t *as = st + (rg * 64 + j) * 256;
+        const uint8_t *bs = st + kPfAStage + (fg * 144 + j) * 128 + 8 * (g & 1);
+        u32x4 a[4][2];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int ft = 0; ft < 4; ++ft)
+            for (int s2 = 0; s2 < 2; ++s2)  // step 2 kh + s2: bytes 64 step + 16 g
+                a[rt][s2] = *reinterpret_cast<const u32x4 *>(as + rt * 16 * 256 + 16 * ((4 * (2 * kh + s2) + g) ^ j));
+        float sc[kPfFeatTiles];  // the chunk's tile scale of each feature tile (scalar loads)
+#pragma unroll
+        for (int ft = 0; ft < kPfFeatTiles; ++ft)
+            sc[ft] = ts[tile_of[ft] + c];
+#pragma unroll
+        for (int ft = 0; ft < kPfFeatTiles; ++ft) {
+            u32x4 b[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {  // bytes 32 step + 8 g
+                const u32x2 wv = *reinterpret_cast<const u32x2 *>(bs + ft * 16 * 128 +
+                                                                  16 * ((2 * (2 * kh + s2) + (g >> 1)) ^ b_sw));
+                b[s2] = u32x4{A16::template fp8x2<false>(wv[0]), A16::template fp8x2<true>(wv[0]),
+                              A16::template fp8x2<false>(wv[1]), A16::template fp8x2<true>(wv[1])};
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const f32x4 part = A16::mfma(a[rt][1], b[1], A16::mfma(a[rt][0], b[0], zero4));
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    acc[rt][ft][r] = __builtin_fmaf(s, part[rt][ft][r], acc[rt][ft][r]);
-        if (c + 1 < nch) {
-            wait_vmcnt<0>();
-            store_chunk((c + 1) & 1);
+                    acc[rt][ft][r] = __builtin_fmaf(sc[ft], part[r], acc[rt][ft][r]);
+            }
         }
+        // unconditional (nothing is outstanding after the last chunk): a
+        // branch here let the compiler sink the scale FMAs past it, keeping
+        // every partial tile live at once
+        wait_vmcnt<0>();
         __syncthreads();
     }
 
+    // k halves: kh 1 hands its accumulators over through LDS, half of the
+    // row tiles at a time; kh 0 adds them and writes the outputs.
+    float *red = reinterpret_cast<float *>(lds);
+    const int pair = fg + 2 * rg;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int h = 0; h < 2; ++h) {
+        if (kh == 1) {
 #pragma unroll
-        for (int ft = 0; ft < 4; ++ft) {
-            const int f = fb + wf * 64 + ft * 16 + j;
+            for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = rb + wr * 64 + rt * 16 + 4 * g + r;
-                if (row < N && f < M)
-                    store_out(out, out_dtype, (size_t)row * M + f, acc[rt][ft][r]);
-            }
+                for (int ft = 0; ft < kPfFeatTiles; ++ft)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        red[(((pair * 2 + r2) * kPfFeatTiles + ft) * 4 + r) * 64 + lane] = acc[2 * h + r2][ft][r];
         }
+        __syncthreads();
+        if (kh == 0) {
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+                for (int ft = 0; ft < kPfFeatTiles; ++ft) {
+                    const int f = fb + fg * 144 + ft * 16 + j;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = rb + rg * 64 + (2 * h + r2) * 16 + 4 * g + r;
+                        const float v =
+                            acc[2 * h + r2][ft][r] + red[(((pair * 2 + r2) * kPfFeatTiles + ft) * 4 + r) * 64 + lane];
+                        if (row < N && f < M)
+                            store_out(out, out_dtype, (size_t)row * M + f, v);
+                    }
+                }
+        }
+        __syncthreads();
+    }
 }
 
 template <int ACT>
 hipError_t launch_act(const Fp8PrefillArgs &p) {
-    const size_t shm = 2 * (size_t)kPfBuf;
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(fp8_prefill_kernel<ACT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) != hipSuccess)
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kPfLds) != hipSuccess)
         return hipErrorInvalidValue;
     const int gx = (p.M + kPfFeats - 1) / kPfFeats;
     const int groups = (p.N + kPfRows - 1) / kPfRows;
@@ -163,7 +196,7 @@ hipError_t launch_act(const Fp8PrefillArgs &p) {
         const uint16_t *x = static_cast<const uint16_t *>(p.act) + (size_t)g0 * kPfRows * p.K;
         void *out = static_cast<char *>(p.out) + (size_t)g0 * kPfRows * p.M * out_elem_bytes(p.out_dtype);
         const int n = std::min(p.N - g0 * kPfRows, gy * kPfRows);
-        hipLaunchKernelGGL(fp8_prefill_kernel<ACT>, dim3(gx, gy), dim3(256), shm, p.stream,
+        hipLaunchKernelGGL(fp8_prefill_kernel<ACT>, dim3(gx, gy), dim3(kPfThreads), kPfLds, p.stream,
                            static_cast<const uint8_t *>(p.w), p.tile_scales, x, out, p.out_dtype, n, p.M, p.K);
     }
     return hipGetLastError();
