@@ -48,12 +48,15 @@ __global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *
                                                                  const float *__restrict__ ts,
                                                                  const uint16_t *__restrict__ x,
                                                                  void *__restrict__ out, int out_dtype, int N, int M,
-                                                                 int K) {
+                                                                 int K, int row_groups) {
     using A16 = Act16<ACT>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int lane = threadIdx.x & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
     const int fg = wave & 1, rg = (wave >> 1) & 1, kh = wave >> 2;
-    const int fb = blockIdx.x * kPfFeats, rb = blockIdx.y * kPfRows;
+    // tiles in column order (the row groups of one feature column are
+    // consecutive), numbered so that each XCD holds a run of whole columns
+    const int tile = xcd_run_index((int)blockIdx.x, (int)gridDim.x);
+    const int fb = tile / row_groups * kPfFeats, rb = tile % row_groups * kPfRows;
     const int nch = K / kPfK, nft = (M + 127) / 128;
     const int rows = min(kPfRows, N - rb), feats = min(kPfFeats, M - fb);
 
@@ -95,20 +98,25 @@ __global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *
         for (int ft = 0; ft < kPfFeatTiles; ++ft)
             acc[rt][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    // this wave's scale tile of each feature tile (clamped: tiles past M
-    // multiply zeros)
-    int tile_of[kPfFeatTiles];
-#pragma unroll
-    for (int ft = 0; ft < kPfFeatTiles; ++ft)
-        tile_of[ft] = min((fb + fg * 144 + ft * 16) >> 7, nft - 1) * nch;
+    // Tile scales: lane ft (< 9) of each wave loads the chunk's scale of the
+    // wave's feature tile ft (its 128-feature scale tile, clamped: tiles past
+    // M multiply zeros), one chunk ahead like the operands; the FMAs read it
+    // back with a lane read.  (A scalar load here would share its wait
+    // counter with the LDS reads and stall every one of them.)
+    const rsrc_t rts = make_rsrc(ts, (uint32_t)nft * (uint32_t)nch * 4u);
+    const int ts_off = lane < kPfFeatTiles ? min((fb + fg * 144 + lane * 16) >> 7, nft - 1) * nch * 4 : kPfOut;
     const int b_sw = (j >> 1) & 7;
 
     issue(0, 0);
+    uint32_t scale_next = bload4<kAuxCached>(rts, ts_off, 0);
     wait_vmcnt<0>();
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch)
+        const uint32_t scale_bits = scale_next;
+        if (c + 1 < nch) {
             issue(c + 1, (c + 1) & 1);
+            scale_next = bload4<kAuxCached>(rts, ts_off, 4 * (c + 1));
+        }
         const uint8_t *st = lds + (c & 1) * kPfStage;
         const uint8_t *as = st + (rg * 64 + j) * 256;
         const uint8_t *bs = st + kPfAStage + (fg * 144 + j) * 128 + 8 * (g & 1);
@@ -118,10 +126,10 @@ __global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)  // step 2 kh + s2: bytes 64 step + 16 g
                 a[rt][s2] = *reinterpret_cast<const u32x4 *>(as + rt * 16 * 256 + 16 * ((4 * (2 * kh + s2) + g) ^ j));
-        float sc[kPfFeatTiles];  // the chunk's tile scale of each feature tile (scalar loads)
+        float sc[kPfFeatTiles];  // the chunk's tile scale of each feature tile
 #pragma unroll
         for (int ft = 0; ft < kPfFeatTiles; ++ft)
-            sc[ft] = ts[tile_of[ft] + c];
+            sc[ft] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(scale_bits, ft));
 #pragma unroll
         for (int ft = 0; ft < kPfFeatTiles; ++ft) {
             u32x4 b[2];
@@ -190,14 +198,14 @@ hipError_t launch_act(const Fp8PrefillArgs &p) {
         return hipErrorInvalidValue;
     const int gx = (p.M + kPfFeats - 1) / kPfFeats;
     const int groups = (p.N + kPfRows - 1) / kPfRows;
-    constexpr int kMaxGridY = 65535;
-    for (int g0 = 0; g0 < groups; g0 += kMaxGridY) {
-        const int gy = std::min(kMaxGridY, groups - g0);
+    const int per_launch = std::max(1, (1 << 30) / gx);  // row groups per launch (grid below 2^30)
+    for (int g0 = 0; g0 < groups; g0 += per_launch) {
+        const int gy = std::min(per_launch, groups - g0);
         const uint16_t *x = static_cast<const uint16_t *>(p.act) + (size_t)g0 * kPfRows * p.K;
         void *out = static_cast<char *>(p.out) + (size_t)g0 * kPfRows * p.M * out_elem_bytes(p.out_dtype);
         const int n = std::min(p.N - g0 * kPfRows, gy * kPfRows);
-        hipLaunchKernelGGL(fp8_prefill_kernel<ACT>, dim3(gx, gy), dim3(kPfThreads), kPfLds, p.stream,
-                           static_cast<const uint8_t *>(p.w), p.tile_scales, x, out, p.out_dtype, n, p.M, p.K);
+        hipLaunchKernelGGL(fp8_prefill_kernel<ACT>, dim3(gx * gy), dim3(kPfThreads), kPfLds, p.stream,
+                           static_cast<const uint8_t *>(p.w), p.tile_scales, x, out, p.out_dtype, n, p.M, p.K, gy);
     }
     return hipGetLastError();
 }

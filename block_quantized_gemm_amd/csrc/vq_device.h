@@ -220,6 +220,15 @@ __device__ __forceinline__ void pipeline(int ns, LoadF &&load, ComputeF &&comput
     });
 }
 
+// Workgroups of a 1-D grid go to the 8 XCDs in turn (workgroup b to XCD
+// b % 8).  The index returned numbers them so that the workgroups of one XCD
+// hold a contiguous run of indices [0, G): tiles that share operands, given
+// consecutive indices, then share that XCD's L2.
+__device__ __forceinline__ int xcd_run_index(int b, int G) {
+    const int xcd = b & 7, loc = b >> 3, n = G >> 3, extra = G & 7;
+    return xcd * n + min(xcd, extra) + loc;
+}
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 // ---------------------------------------------------------------------------

@@ -79,12 +79,15 @@ __global__ __launch_bounds__(kW4Threads) void w4a8_kernel(const uint8_t *__restr
                                                           const int8_t *__restrict__ qx,
                                                           const uint16_t *__restrict__ xscales,
                                                           void *__restrict__ out, int out_dtype, int N, int M,
-                                                          int K, float alpha) {
+                                                          int K, float alpha, int row_groups) {
     using F16 = Act16<VQ_DTYPE_F16>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x, lane = t & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
     const int fg = wave & 1, rg = (wave >> 1) & 1, kh = wave >> 2;
-    const int fb = blockIdx.x * kW4Feats, rb = blockIdx.y * kW4Rows;
+    // tiles in column order (the row groups of one feature column are
+    // consecutive), numbered so that each XCD holds a run of whole columns
+    const int tile = xcd_run_index((int)blockIdx.x, (int)gridDim.x);
+    const int fb = tile / row_groups * kW4Feats, rb = tile % row_groups * kW4Rows;
     const int NB = K >> 5, KH = K >> 1;
     const int nch = (NB + kW4Blocks - 1) / kW4Blocks;
     const int rows = min(kW4Rows, N - rb), feats = min(kW4Feats, M - fb);
@@ -256,16 +259,16 @@ hipError_t launch_w4a8(const W4A8Args &p) {
         return hipErrorInvalidValue;
     const int gx = (p.M + kW4Feats - 1) / kW4Feats;
     const int groups = (p.N + kW4Rows - 1) / kW4Rows;
-    constexpr int kMaxGridY = 65535;
-    for (int g0 = 0; g0 < groups; g0 += kMaxGridY) {
-        const int gy = std::min(kMaxGridY, groups - g0);
+    const int per_launch = std::max(1, (1 << 30) / gx);  // row groups per launch (grid below 2^30)
+    for (int g0 = 0; g0 < groups; g0 += per_launch) {
+        const int gy = std::min(per_launch, groups - g0);
         const int8_t *qx = reinterpret_cast<const int8_t *>(p.qx) + (size_t)g0 * kW4Rows * p.K;
         const uint16_t *xs = reinterpret_cast<const uint16_t *>(p.xscales) + (size_t)g0 * kW4Rows * (p.K / 32);
         void *out = static_cast<char *>(p.out) + (size_t)g0 * kW4Rows * p.M * out_elem_bytes(p.out_dtype);
         const int n = std::min(p.N - g0 * kW4Rows, gy * kW4Rows);
-        hipLaunchKernelGGL(w4a8_kernel, dim3(gx, gy), dim3(kW4Threads), kW4Lds, p.stream,
+        hipLaunchKernelGGL(w4a8_kernel, dim3(gx * gy), dim3(kW4Threads), kW4Lds, p.stream,
                            reinterpret_cast<const uint8_t *>(p.codes), reinterpret_cast<const uint16_t *>(p.wscales),
-                           qx, xs, out, p.out_dtype, n, p.M, p.K, p.alpha);
+                           qx, xs, out, p.out_dtype, n, p.M, p.K, p.alpha, gy);
     }
     return hipGetLastError();
 }
