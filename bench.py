@@ -73,7 +73,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", action="store_true",
                     help="instead of the stream: time the prefill-sized W4A8 path (H32 int8 quantizer over 512 "
-                         "bf16 rows x 5120, then the int8-MFMA GEMM against Q4_0 17408 x 5120) and print its "
+                         "bf16 rows x 5120, then the W4A8 GEMM against Q4_0 17408 x 5120) and print its "
                          "own JSON line against the int8 MFMA roofline")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline form (grouped per layer, 16 rows), so that a kernel trace of "
@@ -399,14 +399,17 @@ def prefill_bench(args):
         "dtype": "i8",
         "data": "synthetic (Q4_0 codes uniform, fp16 scales lognormal; bf16 rows Student-t with outlier channels)",
         "config": {"workload": "W4A8 prefill: %d bf16 rows x K=%d, H32 int8 quantizer, then Q4_0 %d x %d "
-                               "(H32-rotated offline) int8-MFMA GEMM, fp32 out" % (N, K, M, K)},
+                               "(H32-rotated offline) W4A8 GEMM (exact integer block dots on the 16-bit MFMA), "
+                               "fp32 out" % (N, K, M, K)},
         "gemm_us": round(t_g * 1e3, 2),
         "quantizer_us": round(t_q * 1e3, 2),
         "quantizer_plus_gemm_us": round(t_b * 1e3, 2),
         "offline_rotation_us": round(t_rot * 1e3, 2),
         "rel_error_vs_bf16_rows": round(rel, 4),
         "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_MFMA_PEAK_TOPS, "unit": "TOPS",
-                     "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "ops_per_launch": ops},
+                     "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "ops_per_launch": ops,
+                     # the integer dots run on the fp16 16x16x32 MFMA, whose dense peak is the bf16/fp16 one
+                     "mfma_used": "f16 16x16x32", "frac_of_mfma_used": round(tops / BF16_MFMA_PEAK_TFLOPS, 4)},
         "fp8_prefill": fp8,
     }
     print(json.dumps(result))
