@@ -48,10 +48,10 @@ bool dim_ok(int64_t v) { return v >= 1 && v <= VQ_MAX_DIM; }
 
 // Default launch shape for an (M, K) verify GEMM.  With room for its
 // workspace, the walk form: workgroups of eight single-tile waves (a
-// workgroup stages each activation element once for 8 tiles; two such
-// workgroups share a CU, 16 waves, which hides the per-chunk barrier better
-// than four two-tile waves), as many persistent workgroups as the device
-// holds, each walking an equal share of the chunks.  Small M uses smaller
+// workgroup stages each activation element once for 8 tiles; one workgroup
+// per CU, its double-buffered activation rows taking half of the LDS), as
+// many persistent workgroups as the device holds, each walking an equal
+// share of the chunks.  Small M uses smaller
 // workgroups.  Otherwise (no workspace, or a Q4_0 K that is not a multiple of
 // 256) the one-shot form: one workgroup of four single-tile waves per tile
 // group over all of K.  A function of (M, K, workspace capacity) only, never
