@@ -98,7 +98,8 @@ def test_prefill_config_parity_sampled():
     assert fro < 1e-5        # only fp32-vs-fp64 scale arithmetic differs
 
 
-@pytest.mark.parametrize("M,K,N", [(17, 64, 1), (300, 480, 65), (64, 4128, 3), (200, 256, 300), (130, 160, 129)])
+@pytest.mark.parametrize("M,K,N", [(17, 64, 1), (300, 480, 65), (64, 4128, 3), (200, 256, 300), (130, 160, 129),
+                                   (1500, 256, 650)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_w4a8_ragged_parity(M, K, N, out_dtype):
     g = np.random.Generator(np.random.PCG64(M + K + N))
