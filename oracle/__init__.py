@@ -84,6 +84,10 @@ def _load():
         lib.vqo_h32_matrix.argtypes = [P]
         lib.vqo_h32_quant_int8.restype = ctypes.c_int
         lib.vqo_h32_quant_int8.argtypes = [P, ctypes.c_int, I64, I64, P, P]
+        lib.vqo_h32_quant_int4.restype = ctypes.c_int
+        lib.vqo_h32_quant_int4.argtypes = [P, ctypes.c_int, I64, I64, P, P]
+        lib.vqo_block_quant.restype = ctypes.c_int
+        lib.vqo_block_quant.argtypes = [P, ctypes.c_int, I64, I64, ctypes.c_int, ctypes.c_int, P, P]
         lib.vqo_q4_0_rotate_h32.restype = None
         lib.vqo_q4_0_rotate_h32.argtypes = [P, P, I64, I64, P, P]
         lib.vqo_greedy_verify.restype = I64
@@ -219,6 +223,27 @@ def h32_quant_int8(x_bits, x_dtype, N, K):
     q = np.empty((N, K), dtype=np.int8)
     d = np.empty((N, K // 32), dtype=np.uint16)
     st = _load().vqo_h32_quant_int8(_ptr(x), int(x_dtype), N, K, _ptr(q), _ptr(d))
+    return q, d, int(st)
+
+
+def h32_quant_int4(x_bits, x_dtype, N, K):
+    """The 4-bit quantizer: returns (q int8 [N][K] holding codes in [-7, 7],
+    d fp16-bits uint16 [N][K/32], status)."""
+    x = _c(x_bits, np.uint16)
+    q = np.empty((N, K), dtype=np.int8)
+    d = np.empty((N, K // 32), dtype=np.uint16)
+    st = _load().vqo_h32_quant_int4(_ptr(x), int(x_dtype), N, K, _ptr(q), _ptr(d))
+    return q, d, int(st)
+
+
+def block_quant(x_bits, x_dtype, N, K, qmax, rotate):
+    """Either quantizer rule with any symmetric bound, with or without the
+    H32 rotation (rotate = False quantizes the plain blocks); see
+    vqo_block_quant."""
+    x = _c(x_bits, np.uint16)
+    q = np.empty((N, K), dtype=np.int8)
+    d = np.empty((N, K // 32), dtype=np.uint16)
+    st = _load().vqo_block_quant(_ptr(x), int(x_dtype), N, K, int(qmax), int(bool(rotate)), _ptr(q), _ptr(d))
     return q, d, int(st)
 
 

@@ -38,6 +38,8 @@
  *    restored by alpha = 1/32.
  *  - int8 activation quantizer: d = fp16_rne(amax / 127) computed in fp32,
  *    q = clamp(rint_half_even(u / d), -127, 127), amax == 0 gives d = 0, q = 0.
+ *    The 4-bit quantizer of the same section is the same rule with 7 in place
+ *    of 127 (symmetric 4-bit codes, stored one per byte).
  *  - H32 rotation of Q4_0 weights ([P4]: "we rotate the weights the same way
  *    once, offline"; the pages' tool makes a rotated Q4_0 file from a plain
  *    one): per 32-block, dequantize exactly in fp32, H32 by the butterflies
@@ -330,28 +332,33 @@ void vqo_h32_matrix(int8_t *h)
             h[i * 32 + j] = (__builtin_popcount((unsigned)(i & j)) & 1) ? -1 : 1;
 }
 
-/* Per (row, 32-block): u = H32 x (fp32), amax = max |u|,
- * d = fp16_rne(amax / 127), q = clamp(rint(u / d), -127, 127).
+/* Per (row, 32-block): u = H32 x in fp32 (or u = x when rotate == 0),
+ * amax = max |u|, d = fp16_rne(amax / qmax), q = clamp(rint(u / d), -qmax,
+ * qmax).  qmax = 127 is the int8 quantizer, qmax = 7 the 4-bit one ([P4]
+ * "Prompt processing": only the activations are rounded to 4 bits; read here
+ * as the int8 rule with the symmetric 4-bit range, codes one per byte).
  * Returns 0, or -1 if some d overflows fp16 (then outputs are partial). */
-int vqo_h32_quant_int8(const uint16_t *x, int x_dtype, int64_t N, int64_t K,
-                       int8_t *q, uint16_t *d)
+int vqo_block_quant(const uint16_t *x, int x_dtype, int64_t N, int64_t K, int qmax, int rotate,
+                    int8_t *q, uint16_t *d)
 {
     int64_t nb = K / 32;
     int bad = 0;
+    const float qm = (float)qmax;
 #pragma omp parallel for schedule(static) reduction(| : bad)
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t b = 0; b < nb; ++b) {
             float u[32];
             for (int j = 0; j < 32; ++j)
                 u[j] = (float)act_to_f64(x, x_dtype, n * K + 32 * b + j); /* exact */
-            vqo_fwht32_f32(u);
+            if (rotate)
+                vqo_fwht32_f32(u);
             float amax = 0.0f;
             for (int j = 0; j < 32; ++j) {
                 float a = fabsf(u[j]);
                 if (a > amax)
                     amax = a;
             }
-            float d32 = amax / 127.0f;
+            float d32 = amax / qm;
             uint16_t dh = vqo_f32_to_f16_rne(d32);
             if ((dh & 0x7c00u) == 0x7c00u)
                 bad = 1;
@@ -361,14 +368,28 @@ int vqo_h32_quant_int8(const uint16_t *x, int x_dtype, int64_t N, int64_t K,
                 float r = 0.0f;
                 if (df != 0.0f) {
                     r = nearbyintf(u[j] / df);                /* ties to even */
-                    if (r > 127.0f) r = 127.0f;
-                    if (r < -127.0f) r = -127.0f;
+                    if (r > qm) r = qm;
+                    if (r < -qm) r = -qm;
                 }
                 q[n * K + 32 * b + j] = (int8_t)r;
             }
         }
     }
     return bad ? -1 : 0;
+}
+
+/* The H32-rotated int8 quantizer (codes in [-127, 127]). */
+int vqo_h32_quant_int8(const uint16_t *x, int x_dtype, int64_t N, int64_t K,
+                       int8_t *q, uint16_t *d)
+{
+    return vqo_block_quant(x, x_dtype, N, K, 127, 1, q, d);
+}
+
+/* The H32-rotated 4-bit quantizer (codes in [-7, 7], one per byte). */
+int vqo_h32_quant_int4(const uint16_t *x, int x_dtype, int64_t N, int64_t K,
+                       int8_t *q, uint16_t *d)
+{
+    return vqo_block_quant(x, x_dtype, N, K, 7, 1, q, d);
 }
 
 /* ------------------------------------------------------------------ */
