@@ -390,6 +390,31 @@ def prefill_bench(args):
     vq.gemm_q4_0(codes0, scales0, x, ref, stream=stream)
     torch.cuda.synchronize()
     rel = float(torch.linalg.norm((out - ref).double()) / torch.linalg.norm(ref.double()))
+    # the 4-bit activation codes of the same section (W4A4 numerics): the same
+    # GEMM on codes in [-7, 7]
+    q4 = torch.empty_like(q)
+    d4 = torch.empty_like(d)
+    out4 = torch.empty_like(out)
+
+    def quant4(s):
+        vq.hadamard32_quant_int4(x, q4, d4, stream=s)
+
+    def gemm4(s):
+        vq.gemm_q4_0(codes, scales, q4, out4, x_scales=d4, alpha=1.0 / 32, stream=s)
+
+    t_q4 = time_ms(quant4, stream, args.steps, args.warmup, graph=True)
+    t_g4 = time_ms(gemm4, stream, args.steps, args.warmup, graph=True)
+    with torch.cuda.stream(stream):
+        quant4(stream)
+        gemm4(stream)
+    torch.cuda.synchronize()
+    rel4 = float(torch.linalg.norm((out4 - ref).double()) / torch.linalg.norm(ref.double()))
+    tops4 = ops / (t_g4 * 1e-3) / 1e12
+    w4a4 = {"workload": "4-bit activation codes (H32, bound 7) of the same rows, the same GEMM",
+            "quantizer_us": round(t_q4 * 1e3, 2), "gemm_us": round(t_g4 * 1e3, 2), "tops": round(tops4, 2),
+            "rel_error_vs_bf16_rows": round(rel4, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tops4, 2), "peak": INT8_MFMA_PEAK_TOPS, "unit": "TOPS",
+                         "frac": round(tops4 / INT8_MFMA_PEAK_TOPS, 4)}}
     fp8 = fp8_prefill_form(stream, args, N)
     result = {
         "metric": "W4A8 prefill int8-MFMA TOPS",
@@ -410,6 +435,7 @@ def prefill_bench(args):
                      "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "ops_per_launch": ops,
                      # the integer dots run on the fp16 16x16x32 MFMA, whose dense peak is the bf16/fp16 one
                      "mfma_used": "f16 16x16x32", "frac_of_mfma_used": round(tops / BF16_MFMA_PEAK_TFLOPS, 4)},
+        "w4a4": w4a4,
         "fp8_prefill": fp8,
     }
     print(json.dumps(result))

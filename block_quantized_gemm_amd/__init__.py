@@ -47,6 +47,7 @@ SIGNATURES = {
     "vq_gemm_q4_0": (_I, [_P, _P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _F, _P, _SZ, _P]),
     "vq_gemm_fp8_blk128": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
     "vq_hadamard32_quant_int8": (_I, [_P, _I, _P, _P, _I64, _I64, _P]),
+    "vq_hadamard32_quant_int4": (_I, [_P, _I, _P, _P, _I64, _I64, _P]),
     "vq_gemm_fp8_blk128_prefill": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P]),
     "vq_workspace_bytes": (_SZ, [_I, _I64, _I64]),
     "vq_gemm_q4_0_ex": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _F, _I, _I, _I, _P, _SZ, _P]),
@@ -433,6 +434,20 @@ def hadamard32_quant_int8(x, q_out, scales_out, *, stream=None):
     st = lib().vq_hadamard32_quant_int8(_dev_ptr(x, "x"), _dtype_code(x), _dev_ptr(q_out, "q_out"),
                                         _dev_ptr(scales_out, "scales_out"), N, K, _stream(stream))
     _check(st, "vq_hadamard32_quant_int8")
+    return q_out, scales_out
+
+
+def hadamard32_quant_int4(x, q_out, scales_out, *, stream=None):
+    """The 4-bit quantizer: per 32-block u = H32 x (fp32), d = fp16(amax/7),
+    q = clamp(rint(u/d), +-7), codes one per byte (gemm_q4_0 reads them as int8).
+
+    x: float16 / bfloat16 [N][K]; q_out: int8 [N][K]; scales_out: float16 [N][K/32]."""
+    N, K = x.shape
+    _check_2d(q_out, "q_out", (N, K))
+    _check_2d(scales_out, "scales_out", (N, K // 32))
+    st = lib().vq_hadamard32_quant_int4(_dev_ptr(x, "x"), _dtype_code(x), _dev_ptr(q_out, "q_out"),
+                                        _dev_ptr(scales_out, "scales_out"), N, K, _stream(stream))
+    _check(st, "vq_hadamard32_quant_int4")
     return q_out, scales_out
 
 

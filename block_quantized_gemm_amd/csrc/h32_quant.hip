@@ -1,5 +1,5 @@
-// h32_quant.hip -- Walsh-Hadamard-32 rotation fused into the int8 activation
-// quantizer.
+// h32_quant.hip -- Walsh-Hadamard-32 rotation fused into the int8 (and
+// 4-bit) activation quantizer.
 //
 // "Qwen3.8-27B at 45.7 tok/s: DFlash2 in 1bit serve, and 4-bit activations
 // with a Hadamard rotation", section "Prompt processing: 4-bit activations,
@@ -11,8 +11,10 @@
 // Butterfly stages h = 1, 2 are in-register, h = 4, 8, 16 exchange with lanes
 // p ^ 1, p ^ 2, p ^ 4.  Each stage computes (x_i + x_{i+h}, x_i - x_{i+h})
 // with single IEEE fp32 adds, in the fixed order h = 1, 2, 4, 8, 16.  Then
-// amax over the block, d = fp16_rne(amax / 127) with a correctly rounded
-// division, q = clamp(rint(u / d), -127, 127).  Every operation is one IEEE
+// amax over the block, d = fp16_rne(amax / QMAX) with a correctly rounded
+// division, q = clamp(rint(u / d), -QMAX, QMAX): QMAX = 127 for int8 codes,
+// 7 for the 4-bit codes of the same section (only the activations are
+// rounded to 4 bits; stored one per byte, so the same GEMM reads them).  Every operation is one IEEE
 // rounding (no FMA contraction is possible: there are no multiplies), so the
 // codes and scales are reproducible bit for bit on any IEEE implementation.
 #include "vq_device.h"
@@ -34,7 +36,7 @@ __device__ __forceinline__ float butterfly(float own, int p, int mask) {
     return (p & mask) ? (other - own) : (own + other);
 }
 
-template <int XD>
+template <int XD, int QMAX>
 __global__ __launch_bounds__(256) void h32_quant_kernel(const uint16_t *__restrict__ x,
                                                          int8_t *__restrict__ q,
                                                          uint16_t *__restrict__ d,
@@ -69,14 +71,14 @@ __global__ __launch_bounds__(256) void h32_quant_kernel(const uint16_t *__restri
     am = fmaxf(am, __shfl_xor(am, 2, 64));
     am = fmaxf(am, __shfl_xor(am, 4, 64));
 
-    const float d32 = am / 127.0f;  // correctly rounded (built with fp32 IEEE division)
+    const float d32 = am / (float)QMAX;  // correctly rounded (built with fp32 IEEE division)
     const _Float16 dh = static_cast<_Float16>(d32);
     const float df = static_cast<float>(dh);
     int8_t q0 = 0, q1 = 0, q2 = 0, q3 = 0;
     if (df != 0.0f) {
         auto code = [df](float u) -> int8_t {
             const float r = rintf(u / df);
-            return static_cast<int8_t>(fminf(fmaxf(r, -127.0f), 127.0f));
+            return static_cast<int8_t>(fminf(fmaxf(r, -(float)QMAX), (float)QMAX));
         };
         q0 = code(u0); q1 = code(u1); q2 = code(u2); q3 = code(u3);
     }
@@ -181,20 +183,28 @@ hipError_t launch_q4_rotate_h32(const void *codes, const void *scales, int M, in
     return hipGetLastError();
 }
 
-hipError_t launch_h32_quant(const void *x, int x_dtype, int8_t *q, void *d, int N, int K,
+template <int QMAX>
+hipError_t launch_quant_q(const void *x, int x_dtype, int8_t *q, void *d, int64_t total_blocks, int64_t grid,
+                          hipStream_t stream) {
+    if (x_dtype == VQ_DTYPE_BF16)
+        hipLaunchKernelGGL((h32_quant_kernel<VQ_DTYPE_BF16, QMAX>), dim3((unsigned)grid), dim3(256), 0, stream,
+                           reinterpret_cast<const uint16_t *>(x), q, reinterpret_cast<uint16_t *>(d), total_blocks);
+    else
+        hipLaunchKernelGGL((h32_quant_kernel<VQ_DTYPE_F16, QMAX>), dim3((unsigned)grid), dim3(256), 0, stream,
+                           reinterpret_cast<const uint16_t *>(x), q, reinterpret_cast<uint16_t *>(d), total_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_h32_quant(const void *x, int x_dtype, int8_t *q, void *d, int N, int K, int qmax,
                             hipStream_t stream) {
     const int64_t total_blocks = (int64_t)N * (K / 32);
     const int64_t lanes = total_blocks * 8;
     const int64_t grid = (lanes + 255) / 256;
-    if (x_dtype == VQ_DTYPE_BF16)
-        hipLaunchKernelGGL(h32_quant_kernel<VQ_DTYPE_BF16>, dim3((unsigned)grid), dim3(256), 0, stream,
-                           reinterpret_cast<const uint16_t *>(x), q, reinterpret_cast<uint16_t *>(d),
-                           total_blocks);
-    else
-        hipLaunchKernelGGL(h32_quant_kernel<VQ_DTYPE_F16>, dim3((unsigned)grid), dim3(256), 0, stream,
-                           reinterpret_cast<const uint16_t *>(x), q, reinterpret_cast<uint16_t *>(d),
-                           total_blocks);
-    return hipGetLastError();
+    if (qmax == 127)
+        return launch_quant_q<127>(x, x_dtype, q, d, total_blocks, grid, stream);
+    if (qmax == 7)
+        return launch_quant_q<7>(x, x_dtype, q, d, total_blocks, grid, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace vq

@@ -334,8 +334,12 @@ int vq_gemm_fp8_blk128_ex(const void *w_e4m3, const float *w_tile_scales, const 
                       stream);
 }
 
-int vq_hadamard32_quant_int8(const void *x, int x_dtype, int8_t *q_out, void *scales_out,
-                             int64_t n_rows, int64_t k, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int run_quant(const void *x, int x_dtype, int8_t *q_out, void *scales_out, int64_t n_rows, int64_t k, int qmax,
+              void *stream) {
     if (!x || !q_out || !scales_out)
         return VQ_ERR_NULL_POINTER;
     if (!float_act(x_dtype))
@@ -347,10 +351,24 @@ int vq_hadamard32_quant_int8(const void *x, int x_dtype, int8_t *q_out, void *sc
     const int dev = check_device();
     if (dev != VQ_OK)
         return dev;
-    return vq::launch_h32_quant(x, x_dtype, q_out, scales_out, (int)n_rows, (int)k,
+    return vq::launch_h32_quant(x, x_dtype, q_out, scales_out, (int)n_rows, (int)k, qmax,
                                 static_cast<hipStream_t>(stream)) == hipSuccess
                ? VQ_OK
                : VQ_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vq_hadamard32_quant_int8(const void *x, int x_dtype, int8_t *q_out, void *scales_out,
+                             int64_t n_rows, int64_t k, void *stream) {
+    return run_quant(x, x_dtype, q_out, scales_out, n_rows, k, 127, stream);
+}
+
+int vq_hadamard32_quant_int4(const void *x, int x_dtype, int8_t *q_out, void *scales_out,
+                             int64_t n_rows, int64_t k, void *stream) {
+    return run_quant(x, x_dtype, q_out, scales_out, n_rows, k, 7, stream);
 }
 
 int vq_q4_0_rotate_h32(const void *w_codes, const void *w_scales, int64_t m, int64_t k, void *codes_out,
@@ -519,6 +537,6 @@ const char *vq_status_string(int status) {
     }
 }
 
-int vq_version(void) { return 300; }
+int vq_version(void) { return 310; }
 
 }  // extern "C"

@@ -110,7 +110,8 @@ struct Fp8PrefillArgs {
     hipStream_t stream;
 };
 hipError_t launch_fp8_prefill(const Fp8PrefillArgs &p);
-hipError_t launch_h32_quant(const void *x, int x_dtype, int8_t *q, void *d, int N, int K,
+// qmax: 127 (int8 codes) or 7 (4-bit codes, one per byte)
+hipError_t launch_h32_quant(const void *x, int x_dtype, int8_t *q, void *d, int N, int K, int qmax,
                             hipStream_t stream);
 hipError_t launch_q4_rotate_h32(const void *codes, const void *scales, int M, int K, void *codes_out,
                                 void *scales_out, hipStream_t stream);

@@ -116,9 +116,10 @@ extern "C" {
  *            act_scales must be NULL.
  *   act_dtype I8: the W4A8 path [P4, "exact int8 path"].  act is int8 q_x
  *            [N][K] and act_scales is f16 [N][K/32] (as written by
- *            vq_hadamard32_quant_int8); x[n][k] = act_scales[n][k/32] *
+ *            vq_hadamard32_quant_int8, or _int4 for 4-bit codes);
+ *            x[n][k] = act_scales[n][k/32] *
  *            q_x[n][k].  Each 32-block dot sum (q - 8) * q_x is formed exactly
- *            in int32 before the fp32 scale products.  For weights and
+ *            (an integer) before the fp32 scale products.  For weights and
  *            activations both rotated by the unnormalised H32, pass
  *            alpha = 1/32 to restore the unrotated product.  The workspace is
  *            not used on this path.
@@ -184,6 +185,22 @@ int vq_gemm_fp8_blk128_prefill(const void *w_e4m3, const float *w_tile_scales,
  * K % 32 == 0.
  */
 int vq_hadamard32_quant_int8(const void *x, int x_dtype,
+                             int8_t *q_out, void *scales_out,
+                             int64_t n_rows, int64_t k, void *stream);
+
+/*
+ * vq_hadamard32_quant_int4 -- the 4-bit activation quantizer of the same
+ * section [P4] ("only the activations are rounded to 4 bits", after the same
+ * H32 rotation): identical to vq_hadamard32_quant_int8 with 7 in place of
+ * 127 (the library's reading: the symmetric 4-bit range),
+ *   d   = fp16_rne(fp32(max_j |u_j|) / 7)          -> scales_out [N][K/32] f16
+ *   q_j = clamp(rint_half_even(u_j / d), -7, 7)     -> q_out [N][K] int8
+ * Codes are stored one per byte, so vq_gemm_q4_0 with act_dtype I8 consumes
+ * them unchanged (the W4A4 product; gfx950 has no int4 matrix instruction,
+ * so the GEMM is the W4A8 one).  Same sizes, errors and reproducibility as
+ * the int8 quantizer.
+ */
+int vq_hadamard32_quant_int4(const void *x, int x_dtype,
                              int8_t *q_out, void *scales_out,
                              int64_t n_rows, int64_t k, void *stream);
 

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert vq.lib().vq_version() == 300
+    assert vq.lib().vq_version() == 310
     for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert vq.status_string(st) and vq.status_string(st) != "unknown status"
     assert vq.status_string(-99) == "unknown status"
@@ -75,11 +75,11 @@ def test_fp8_argument_errors():
 
 
 def test_quant_argument_errors():
-    f = vq.lib().vq_hadamard32_quant_int8
-    assert f(None, vq.DTYPE_BF16, B, C, 4, 64, None) == vq.VQ_ERR_NULL_POINTER
-    assert f(A, vq.DTYPE_F32, B, C, 4, 64, None) == vq.VQ_ERR_BAD_DTYPE
-    assert f(A, vq.DTYPE_BF16, B, C, 4, 48, None) == vq.VQ_ERR_BAD_SHAPE
-    assert f(A, vq.DTYPE_BF16, B + 2, C, 4, 64, None) == vq.VQ_ERR_MISALIGNED
+    for f in (vq.lib().vq_hadamard32_quant_int8, vq.lib().vq_hadamard32_quant_int4):
+        assert f(None, vq.DTYPE_BF16, B, C, 4, 64, None) == vq.VQ_ERR_NULL_POINTER
+        assert f(A, vq.DTYPE_F32, B, C, 4, 64, None) == vq.VQ_ERR_BAD_DTYPE
+        assert f(A, vq.DTYPE_BF16, B, C, 4, 48, None) == vq.VQ_ERR_BAD_SHAPE
+        assert f(A, vq.DTYPE_BF16, B + 2, C, 4, 64, None) == vq.VQ_ERR_MISALIGNED
 
 
 def _ex(t, w, s, ws=None, wsb=0, k=512):
