@@ -29,7 +29,7 @@ def _run(w, ts, bits, act="bf16", out="bf16"):
 
 
 @pytest.mark.parametrize("N,M,K", [(1, 17, 128), (129, 129, 256), (300, 200, 384), (512, 512, 1024),
-                                   (64, 1000, 2048), (1000, 1200, 256)])
+                                   (64, 1000, 2048), (1000, 1200, 256), (5, 1, 128), (2, 288, 128)])
 def test_ragged_shapes_parity(N, M, K):
     g = np.random.Generator(np.random.PCG64(801 + N + M))
     f = W.fp8(M=M, K=K, N=16)

@@ -99,7 +99,7 @@ def test_prefill_config_parity_sampled():
 
 
 @pytest.mark.parametrize("M,K,N", [(17, 64, 1), (300, 480, 65), (64, 4128, 3), (200, 256, 300), (130, 160, 129),
-                                   (1500, 256, 650)])
+                                   (1500, 256, 650), (1, 32, 1), (288, 32, 2)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_w4a8_ragged_parity(M, K, N, out_dtype):
     g = np.random.Generator(np.random.PCG64(M + K + N))
