@@ -489,8 +489,13 @@ def main():
 
     layers = min(args.layers, 8) if args.profile_run else args.layers
     mats, acts, outs = build_stack(layers, dev)
-    ws = vq.Workspace(vq.GroupedCall("q4_0", [(c, s, acts[(0, k)], outs[m]) for _, m, k, c, s, _ in mats[:32]],
-                                     workspace=None).workspace_bytes + (1 << 20), dev)
+    # one workspace for every call below: the larger of the two layouts' needs
+    # (panel tile groups are 256 features wide, their pieces twice the size)
+    need = max(vq.GroupedCall("q4_0", [(c, s, acts[(0, k)], outs[m]) for _, m, k, c, s, _ in mats[:32]],
+                              workspace=None).workspace_bytes,
+               vq.GroupedCall("q4_0_panel", [(p, m, acts[(0, k)], outs[m]) for _, m, k, _, _, p in mats[:32]],
+                              workspace="auto").workspace_bytes)
+    ws = vq.Workspace(need + (1 << 20), dev)
     streams = {n: Stream(vq, mats, acts, outs, n, ws, "panel") for n in (16, 8, 1)}
     row_major = {n: Stream(vq, mats, acts, outs, n, ws, "row_major") for n in (16, 1)}
 

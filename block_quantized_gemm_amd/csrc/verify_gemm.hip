@@ -430,16 +430,17 @@ constexpr int kActBuf = kActLdsBytes;  // one activation buffer: 16 rows x 1024 
 // whole cache lines); a load instruction into LDS writes lane l's 16 bytes to
 // byte 16 l of its destination.  The 32 instructions are shared out over the
 // W waves; pieces past the chunk or past K, and rows past N, read zeros.
-template <int W>
+template <int W, int HALVES = 2>
 __device__ __forceinline__ void stage_act_rows(uint8_t *buf, rsrc_t ra, int K, int s_first, int nc, int wave,
                                                int lane) {
     const int kb = s_first * kStepK;
+    constexpr int kInsts = 16 * HALVES;
 #pragma unroll
-    for (int i = 0; i < (32 + W - 1) / W; ++i) {
+    for (int i = 0; i < (kInsts + W - 1) / W; ++i) {
         const int inst = wave + W * i;
-        if (32 % W != 0 && inst >= 32)
+        if (kInsts % W != 0 && inst >= kInsts)
             break;
-        const int r = inst >> 1, h = inst & 1;
+        const int r = inst / HALVES, h = inst % HALVES;
         const int p = 64 * h + lane;
         const bool ok = p < 16 * nc && kb + 8 * p < K;
         bload16_lds(ra, buf + r * kActPitch + h * 1024, ok ? r * K * 2 + 2 * kb + 16 * p : kOut);
@@ -496,15 +497,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int TG = T * W;
     constexpr int WB = FP8 ? 2 : 1;
     constexpr int kStepBytes = FP8 ? 128 : 64;
-    constexpr int CH = kWalkSteps;
+    constexpr int CH = PANEL ? kPanelSteps : kWalkSteps;
     constexpr int SIW = FP8 ? 0 : T;       // scale loads per wave per chunk: 16 feature rows x 64 bytes each
     constexpr int kScBuf = SIW * 1024;     // one wave's scale buffer
     constexpr int scrow = 4 * CH;          // scales per feature row in the buffer
     constexpr int kIssueLoads = PF * T * WB;
     constexpr int kCoherent = 0x10;        // sc1: agent-coherent, no cache maintenance needed
     static_assert(CH % PF == 0, "chunks hold whole pipeline rounds");
-    static_assert(scale_pieces(4) * 2 == CH, "scale rows of one chunk");
-    static_assert(!PANEL || (!FP8 && T == 1 && W == kPanelTiles && CH == kPanelSteps), "one panel per tile group");
+    static_assert(PANEL || scale_pieces(4) * 2 == CH, "scale rows of one chunk");
+    static_assert(!PANEL || (!FP8 && T == kPanelWaveTiles && W == kPanelWaves && CH == kPanelSteps &&
+                             T * kPanelTileScaleBytes == 1024),
+                  "one panel record per chunk, one 1 KiB scale load per wave");
 
     const int lane = threadIdx.x & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
     const int G = (int)gridDim.x;
@@ -534,10 +537,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         src.wrow = FP8 ? K : (K >> 1);
         src.steps = steps_of(FP8, K);
         src.s0 = r.c * CH;
-        if constexpr (PANEL) {  // the chunk's record; wave w's 1 KiB of step s at 8 KiB * s + 1 KiB * w
+        if constexpr (PANEL) {  // the chunk's record; tile t of step s at 16 KiB * s + 1 KiB * t
             src.rw = make_rsrc(a.w + ((size_t)r.tg * a.cpt + r.c) * kPanelRecordBytes,
                                real ? (uint32_t)kPanelRecordBytes : 0u);
-            src.vw = wave * 1024 + 16 * lane;
+            src.vw = wave * T * 1024 + 16 * lane;
             return src;
         }
         const int fwv = (r.tg * TG + wave * T) * 16;
@@ -564,7 +567,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                 wb[U.value][t][h] = bload16<kAuxCached>(
                     src.rw,
                     !ok ? kOut
-                        : PANEL ? src.vw + kPanelTiles * 1024 * st
+                        : PANEL ? src.vw + kPanelTiles * 1024 * st + 1024 * t
                                 : src.vw + kStepBytes * gs + t * 16 * src.wrow + 16 * h,
                     0);
             if constexpr (FP8)
@@ -580,10 +583,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int steps = steps_of(FP8, a.K);
         const int s0 = r.c * CH;
         const rsrc_t ra = make_rsrc(a.act, real ? (uint32_t)nrows * (uint32_t)a.K * 2u : 0u);
-        stage_act_rows<W>(lds + buf * kActBuf, ra, a.K, s0, min(CH, steps - s0), wave, lane);
+        stage_act_rows<W, CH / 4>(lds + buf * kActBuf, ra, a.K, s0, min(CH, steps - s0), wave, lane);
     };
     auto scales_for = [&](const ChunkRef &r, bool real, int buf) {
-        if constexpr (PANEL) {  // this wave's 1 KiB of the record's scale rows
+        if constexpr (PANEL) {  // this wave's 1 KiB of the record's scale rows (its T tiles)
             const KProblem &a = grp.p[r.pi];
             const rsrc_t rs = make_rsrc(a.w + ((size_t)r.tg * a.cpt + r.c) * kPanelRecordBytes,
                                         real ? (uint32_t)kPanelRecordBytes : 0u);
@@ -746,19 +749,21 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// Q4_0 panel layout.  A panel is 128 consecutive features (8 tiles of 16), a
-// chunk 8 steps of 128 k; record (panel p, chunk c) of a matrix with C chunks
+// Q4_0 panel layout.  A panel is 256 consecutive features (16 tiles of 16), a
+// chunk 4 steps of 128 k; record (panel p, chunk c) of a matrix with C chunks
 // per panel starts at byte (p * C + c) * kPanelRecordBytes and holds
-//   codes:  for step s, tile t, lane l = 16 g + j, at 8 KiB * s + 1 KiB * t +
+//   codes:  for step s, tile t, lane l = 16 g + j, at 16 KiB * s + 1 KiB * t +
 //           16 l: dword q (q = 0..3) is dword g (bytes 4g..4g+3) of block
-//           4 (8c + s) + q of feature 128p + 16t + j -- what the lane would
-//           hold after loading block 4 (8c + s) + g and the lane-group
+//           4 (4c + s) + q of feature 256p + 16t + j -- what the lane would
+//           hold after loading block 4 (4c + s) + g and the lane-group
 //           transpose;
-//   scales: at 64 KiB + 1 KiB * t: the fp16 scales of the tile's 16 features,
-//           feature-major, 32 blocks (32c .. 32c + 31) each.
-// Features past M and blocks past K/32 are zeros.  A workgroup of 8 waves
-// reads one record per chunk front to back: 8 KiB per step, then the scales.
-// The repack runs once per matrix; every thread writes one 16-byte piece.
+//   scales: at 64 KiB + 512 B * t: the fp16 scales of the tile's 16 features,
+//           feature-major, 16 blocks (16c .. 16c + 15) each.
+// Features past M and blocks past K/32 are zeros.  A workgroup of 8 waves (2
+// tiles each) reads one record per chunk front to back: 16 KiB per step, then
+// the scales; each staged activation chunk (16 rows x 512 k) serves 256
+// features.  The repack runs once per matrix; every thread writes one 16-byte
+// piece.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void panel_pack_kernel(const uint32_t *codes, const uint16_t *scales, int M,
                                                          int K, int chunks, int64_t pieces, u32x4 *panel) {
@@ -770,19 +775,21 @@ __global__ __launch_bounds__(256) void panel_pack_kernel(const uint32_t *codes, 
         const int p = (int)(rec / chunks), c = (int)(rec - (int64_t)p * chunks);
         u32x4 v = {0u, 0u, 0u, 0u};
         if (in < kCodePieces) {
-            const int s = in >> 9, t = (in >> 6) & 7, l = in & 63, g = l >> 4, j = l & 15;
-            const int m = 128 * p + 16 * t + j;
+            const int s = in / (kPanelTiles * 64), t = (in >> 6) % kPanelTiles, l = in & 63, g = l >> 4, j = l & 15;
+            const int m = kPanelFeatures * p + 16 * t + j;
             if (m < M) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int blk = 4 * (8 * c + s) + q;
+                    const int blk = 4 * (kPanelSteps * c + s) + q;
                     if (blk < NB)
                         v[q] = codes[(size_t)m * (K >> 3) + 4 * blk + g];
                 }
             }
         } else {
-            const int t = (in - kCodePieces) >> 6, l = (in - kCodePieces) & 63;
-            const int m = 128 * p + 16 * t + (l >> 2), b0 = 32 * c + 8 * (l & 3);
+            constexpr int kTilePieces = kPanelTileScaleBytes / 16, kFeatPieces = kTilePieces / 16;
+            const int t = (in - kCodePieces) / kTilePieces, l = (in - kCodePieces) % kTilePieces;
+            const int m = kPanelFeatures * p + 16 * t + l / kFeatPieces,
+                      b0 = 4 * kPanelSteps * c + 8 * (l % kFeatPieces);
             if (m < M) {
                 uint32_t h[8];
 #pragma unroll
@@ -823,9 +830,8 @@ int resident_groups(Kern kern, int threads, size_t shm) {
     return n * device_cus();
 }
 
-// Walk-kernel pipeline depth: steps of weight loads in flight per wave.  Two
-// workgroups share a CU (the double-buffered activations take 64 KiB of LDS
-// each), so each wave keeps 8 KiB of weights or more in flight.
+// Walk-kernel pipeline depth: steps of weight loads in flight per wave (one
+// workgroup per CU; 4 steps of 1-2 tiles or 2 steps of wider ones).
 __host__ __device__ constexpr int walk_depth(bool fp8, int T) { return (fp8 ? 2 * T : T) >= 4 ? 2 : 4; }
 
 template <int ACT, bool FP8, int T, int W, bool PANEL = false>
@@ -859,7 +865,8 @@ hipError_t launch_tw(const VerifyLaunch &l) {
         k.K = q.K;
         k.chunk = q.plan.chunk;
         k.ntg = verify_tile_groups(q.M, TG);
-        k.cpt = (verify_steps(FP8, q.K) + kWalkSteps - 1) / kWalkSteps;
+        constexpr int kChunk = PANEL ? kPanelSteps : kWalkSteps;
+        k.cpt = (verify_steps(FP8, q.K) + kChunk - 1) / kChunk;
         k.item0 = (int)items;
         items += walk ? (int64_t)k.ntg * k.cpt : k.ntg;
     }
@@ -936,7 +943,8 @@ int verify_steps(bool fp8, int K) { return fp8 ? K / 128 : (K / 32 + 3) / 4; }
 int verify_tile_groups(int M, int tiles_per_group) { return verify_tile_groups_dev(M, tiles_per_group); }
 
 int64_t verify_chunks(bool fp8, const VerifyPlan &pl, int M, int K) {
-    return (int64_t)verify_tile_groups(M, pl.tiles * pl.waves) * ((verify_steps(fp8, K) + kWalkSteps - 1) / kWalkSteps);
+    const int chunk = pl.panel ? kPanelSteps : kWalkSteps;
+    return (int64_t)verify_tile_groups(M, pl.tiles * pl.waves) * ((verify_steps(fp8, K) + chunk - 1) / chunk);
 }
 
 size_t verify_lds_bytes(bool fp8, int tiles, int waves, bool walk) {
@@ -963,9 +971,9 @@ size_t verify_walk_workspace(const VerifyPlan &pl, int64_t chunks) {
 bool verify_plan_finish(bool fp8, int M, int K, VerifyPlan &pl) {
     (void)M;
     if (pl.panel) {
-        if (fp8 || pl.tiles != 1 || pl.waves != kPanelTiles || !pl.walk || pl.groups < 0)
+        if (fp8 || pl.tiles != kPanelWaveTiles || pl.waves != kPanelWaves || !pl.walk || pl.groups < 0)
             return false;
-        pl.chunk = kWalkSteps;
+        pl.chunk = kPanelSteps;
         return true;
     }
     if (!(pl.tiles == 1 || pl.tiles == 2 || pl.tiles == 4) || !(pl.waves == 2 || pl.waves == 4 || pl.waves == 8 ||
@@ -987,10 +995,11 @@ hipError_t launch_verify(const VerifyLaunch &l) {
     if (l.count < 1 || l.count > kGroupPerLaunch)
         return hipErrorInvalidValue;
     if (l.probs[0].plan.panel) {
-        if (l.fp8 || l.tiles != 1 || l.waves != kPanelTiles || !l.probs[0].plan.walk)
+        if (l.fp8 || l.tiles != kPanelWaveTiles || l.waves != kPanelWaves || !l.probs[0].plan.walk)
             return hipErrorInvalidValue;
-        return l.act_dtype == VQ_DTYPE_BF16 ? launch_tw<VQ_DTYPE_BF16, false, 1, kPanelTiles, true>(l)
-                                            : launch_tw<VQ_DTYPE_F16, false, 1, kPanelTiles, true>(l);
+        return l.act_dtype == VQ_DTYPE_BF16
+                   ? launch_tw<VQ_DTYPE_BF16, false, kPanelWaveTiles, kPanelWaves, true>(l)
+                   : launch_tw<VQ_DTYPE_F16, false, kPanelWaveTiles, kPanelWaves, true>(l);
     }
     if (l.act_dtype == VQ_DTYPE_BF16)
         return l.fp8 ? dispatch_t<VQ_DTYPE_BF16, true>(l) : dispatch_t<VQ_DTYPE_BF16, false>(l);

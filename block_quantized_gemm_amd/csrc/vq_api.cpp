@@ -80,12 +80,12 @@ vq::VerifyPlan default_plan(bool fp8, int64_t m, int64_t k, size_t ws_bytes) {
     return fb;
 }
 
-// The plan of a panel-layout Q4_0 problem: always the walk form, one tile per
-// wave and one 128-feature panel per workgroup.
+// The plan of a panel-layout Q4_0 problem: always the walk form, one
+// 256-feature panel per workgroup of 8 waves, 2 tiles per wave.
 vq::VerifyPlan panel_plan(int max_groups) {
     vq::VerifyPlan pl;
-    pl.tiles = 1;
-    pl.waves = vq::kPanelTiles;
+    pl.tiles = vq::kPanelWaveTiles;
+    pl.waves = vq::kPanelWaves;
     pl.walk = true;
     pl.panel = true;
     pl.groups = max_groups;

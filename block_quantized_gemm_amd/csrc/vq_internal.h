@@ -21,16 +21,21 @@ struct VerifyPlan {
     bool walk = false;
     int groups = 0;
     int chunk = 0;
-    bool panel = false;  // Q4_0 weights in the panel layout (walk, 1 tile x 8 waves)
+    bool panel = false;  // Q4_0 weights in the panel layout (walk, 2 tiles x 8 waves)
 };
 
-// Q4_0 panel layout: records of 128 features x 8 steps of 128 k, the codes of
-// the 8 steps (8 tiles x 1 KiB each) and then the tiles' scales (1 KiB each).
-constexpr int kPanelFeatures = 128;
-constexpr int kPanelTiles = 8;
-constexpr int kPanelSteps = 8;
+// Q4_0 panel layout: records of 256 features x 4 steps of 128 k, the codes of
+// the 4 steps (16 tiles x 1 KiB each) and then the tiles' scales (512 bytes
+// each: 16 features x 16 blocks).  A workgroup of 8 waves walks one record
+// per chunk, 2 tiles per wave.
+constexpr int kPanelFeatures = 256;
+constexpr int kPanelTiles = 16;
+constexpr int kPanelWaveTiles = 2;
+constexpr int kPanelWaves = kPanelTiles / kPanelWaveTiles;
+constexpr int kPanelSteps = 4;
 constexpr int kPanelCodeBytes = kPanelSteps * kPanelTiles * 1024;
-constexpr int kPanelRecordBytes = kPanelCodeBytes + kPanelTiles * 1024;
+constexpr int kPanelTileScaleBytes = 16 * 4 * kPanelSteps * 2;
+constexpr int kPanelRecordBytes = kPanelCodeBytes + kPanelTiles * kPanelTileScaleBytes;
 
 // Workspace of a walk launch: arrival counters (one per workgroup and wave,
 // kept at zero between calls) in a fixed region at the start, then two fp32

@@ -83,7 +83,8 @@ extern "C" {
  * buffer: each side writes its fp32 partial sums there and the last to
  * arrive adds them in share order (an arrival counter per boundary and wave).
  * Per call: 64 KiB of counters plus 2 x 4 bytes per tile-group feature per 16
- * rows per workgroup, at most about 16 MiB, see vq_workspace_bytes.
+ * rows per workgroup, at most about 16 MiB (32 MiB on panel weights, whose
+ * tile groups are 256 features wide), see vq_workspace_bytes.
  *  - 16-byte aligned device memory, zero-filled by the caller before its first
  *    use.  Every call leaves it ready for the next one (its counters back at
  *    zero), so it is zeroed once, not per call.
@@ -267,20 +268,23 @@ int vq_gemm_fp8_blk128_grouped(const vq_verify_problem *problems, int count,
  * Q4_0 panel layout -- the weights of vq_gemm_q4_0 (codes and fp16 block
  * scales [P4]), rearranged once so that the verify GEMM reads them in long
  * contiguous runs: every HBM byte is still read once, but each workgroup
- * streams one 72 KiB record at a time instead of 16-row strips of 64 bytes.
- * The arithmetic is that of the row-major walk form with one tile per wave
- * and eight waves: where vq_gemm_q4_0 (or its grouped call) runs that form --
- * M >= 128, K % 256 == 0, a workspace, the same problems and workgroup cap --
- * the panel call returns the same bits.
- *   A panel is 128 consecutive features, a chunk 1024 consecutive k.  With
- *   P = ceil(M/128) panels and C = ceil(K/1024) chunks, record (p, c) starts
+ * streams one 72 KiB record at a time instead of 16-row strips of 64 bytes,
+ * and one staged chunk of activations serves 256 features.  Per output the
+ * arithmetic is that of the row-major walk form (per 32-block: the exact
+ * integer dot, then one FMA with the block scale, blocks in order); where no
+ * tile group is cut between workgroups (one workgroup, say) the panel call
+ * returns the same bits as vq_gemm_q4_0 with one tile per wave and eight
+ * waves.  Where tile groups are cut, the two forms cut them at different k
+ * (1024 k row-major, 512 k here) and may differ in the last bits.
+ *   A panel is 256 consecutive features, a chunk 512 consecutive k.  With
+ *   P = ceil(M/256) panels and C = ceil(K/512) chunks, record (p, c) starts
  *   at byte (p * C + c) * 73728 and holds:
- *    - bytes [0, 65536): for step s = 0..7 (128 k each), tile t = 0..7 (16
+ *    - bytes [0, 65536): for step s = 0..3 (128 k each), tile t = 0..15 (16
  *      features each) and lane l = 0..63 (g = l / 16, j = l % 16), 16 bytes
- *      at 8192 s + 1024 t + 16 l whose dword q (q = 0..3) is dword g (code
- *      bytes 4g..4g+3) of Q4_0 block 32c + 4s + q of feature 128p + 16t + j;
- *    - bytes [65536, 73728): for tile t at 65536 + 1024 t, the fp16 scales of
- *      its 16 features, feature-major, 32 blocks (32c .. 32c + 31) each.
+ *      at 16384 s + 1024 t + 16 l whose dword q (q = 0..3) is dword g (code
+ *      bytes 4g..4g+3) of Q4_0 block 16c + 4s + q of feature 256p + 16t + j;
+ *    - bytes [65536, 73728): for tile t at 65536 + 512 t, the fp16 scales of
+ *      its 16 features, feature-major, 16 blocks (16c .. 16c + 15) each.
  *   Features past M and blocks past K/32 hold zeros.
  *
  * vq_q4_0_panel_bytes -- size of the panel form of an M x K matrix

@@ -186,13 +186,14 @@ def test_grouped_workspace_query():
 
 def test_panel_size_query():
     f = vq.lib().vq_q4_0_panel_bytes
-    # records of 128 features x 1024 k: 64 KiB of codes + 8 KiB of scales
-    assert f(17408, 5120) == 136 * 5 * 73728 == 17408 * 5120 // 2 * 9 // 8
-    assert f(128, 1024) == 73728
-    assert f(129, 1056) == 2 * 2 * 73728     # ragged M and K round up to whole records
+    # records of 256 features x 512 k: 64 KiB of codes + 8 KiB of scales
+    assert f(17408, 5120) == 68 * 10 * 73728 == 17408 * 5120 // 2 * 9 // 8
+    assert f(256, 512) == 73728
+    assert f(128, 1024) == 2 * 73728
+    assert f(257, 544) == 2 * 2 * 73728      # ragged M and K round up to whole records
     assert f(1, 32) == 73728
     assert f(0, 1024) == 0 and f(128, 1000) == 0 and f(128, (1 << 24) + 32) == 0
-    assert vq.q4_0_panel_bytes(5120, 17408) == 40 * 17 * 73728
+    assert vq.q4_0_panel_bytes(5120, 17408) == 20 * 34 * 73728
 
 
 def _pk(c=A, s=B, m=256, k=512, p=C, pb=1 << 20):
@@ -207,7 +208,8 @@ def test_panel_argument_errors():
     assert _pk(c=None) == vq.VQ_ERR_NULL_POINTER
     assert _pk(p=None) == vq.VQ_ERR_NULL_POINTER
     assert _pk(k=500) == vq.VQ_ERR_BAD_SHAPE
-    assert _pk(pb=2 * 73728 - 16) == vq.VQ_ERR_BAD_SHAPE     # (256, 512) needs two records
+    assert _pk(pb=73728 - 16) == vq.VQ_ERR_BAD_SHAPE         # (256, 512) needs one whole record
+    assert _pk(m=257, pb=2 * 73728 - 16) == vq.VQ_ERR_BAD_SHAPE  # (257, 512) needs two
     assert _pk(s=B + 2) == vq.VQ_ERR_MISALIGNED
     assert _pg(w=None) == vq.VQ_ERR_NULL_POINTER
     assert _pg(xd=vq.DTYPE_I8) == vq.VQ_ERR_BAD_DTYPE
@@ -231,17 +233,19 @@ def test_panel_argument_errors():
 
 
 def test_panel_workspace_and_shape_queries():
-    # any K % 32 == 0 walks; one panel of 8 single-tile waves per workgroup
+    # any K % 32 == 0 walks; one 256-feature panel of 8 two-tile waves per
+    # workgroup, chunks of 4 steps (one record)
     for m, k in ((256, 512), (17408, 5120), (1, 32), (129, 1056), (5120, 17408)):
         t, w, walk, used = vq.default_launch_shape("q4_0_panel", m, k)
-        assert (t, w, walk) == (1, 8, 1)
-        assert used == vq.workspace_bytes("q4_0_panel", m, k) == _walk_need(m, k, 1, 8)
-    # where the row-major call walks with the same shape it needs the same workspace
-    assert vq.workspace_bytes("q4_0_panel", 17408, 5120) == vq.workspace_bytes("q4_0", 17408, 5120)
+        assert (t, w, walk) == (2, 8, 1)
+        assert used == vq.workspace_bytes("q4_0_panel", m, k) == _walk_need(m, k, 2, 8, chunk_steps=4)
+    # the same chunk count as the row-major walk (72 KiB chunks), twice the piece size
+    assert vq.workspace_bytes("q4_0_panel", 17408, 5120) - 65536 == 2 * (vq.workspace_bytes("q4_0", 17408, 5120) - 65536)
     f = vq.lib().vq_workspace_bytes_grouped
     layer = [(A, None, C, D, m, k) for m, k in ((8192, 5120), (5120, 8192), (17408, 5120), (17408, 5120),
                                                 (5120, 17408))]
-    assert f(vq.KIND_Q4_0_PANEL, _table(layer), 5) == f(vq.KIND_Q4_0, _table([(A, B) + r[2:] for r in layer]), 5)
+    # 2680 chunks, capped at 1024 workgroups
+    assert f(vq.KIND_Q4_0_PANEL, _table(layer), 5) == 65536 + 1024 * 2 * 16 * 1024
 
 
 def test_greedy_argument_errors_and_workspace_query():
