@@ -36,14 +36,15 @@
 //    are staged the same way.
 //  * With a workspace (the normal case) the walk kernel runs persistent
 //    workgroups, each walking one contiguous share of the launch's chunks
-//    (tile group x 8 steps): the weight pipeline never drains between
+//    (tile group x 8 steps, 4 on panel weights): the weight pipeline never drains between
 //    chunks, the next chunk's activations and scales load into the other of
 //    two LDS buffers, a tile group inside the share is summed in registers
 //    over all of K, and a tile group cut between two shares is finished by
 //    the last of its workgroups to arrive, from fp32 pieces in the workspace
 //    added in share order (the same result on every run).
-//  * Q4_0 weights come row-major or in the panel layout, where each chunk of
-//    a 128-feature tile group is one 72 KiB record read front to back.
+//  * Q4_0 weights come row-major or in the panel layout, where each chunk (4
+//    steps) of a 256-feature tile group is one 72 KiB record read front to
+//    back.
 //  * Without a workspace the one-shot kernel gives each workgroup a whole
 //    tile group over all of K, staged chunk by chunk.
 #include "vq_device.h"
@@ -63,7 +64,7 @@ struct KProblem {
     void *out;            // this row group's [<=16][M] outputs
     int M, K;
     int chunk;            // one-shot kernel: steps per LDS chunk
-    int cpt;              // walk kernel: chunks (of 8 steps) per tile group
+    int cpt;              // walk kernel: chunks (8 steps, 4 on panel weights) per tile group
     int ntg;              // tile groups
     int item0;            // first item of this problem in the launch (a tile group, or a chunk)
 };
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(T >= 4 ?
 
 // ---------------------------------------------------------------------------
 // Walk kernel (workspace): persistent workgroups, each walking one contiguous
-// range of chunks.  A chunk is one tile group x 8 steps; chunks are numbered
+// range of chunks.  A chunk is one tile group x 8 steps (4 on panel weights); chunks are numbered
 // problem by problem, tile group by tile group, along K within a tile group,
 // so a workgroup's range is a run of whole tile groups with at most one
 // partial tile group at each end.  A tile group that lies inside the range is
@@ -452,28 +453,29 @@ struct ChunkRef {
     int pi, tg, c;
 };
 
-// The chunk `it` (a linear search over the launch's problems: once per
-// workgroup; later chunks are reached by next_chunk).
-__device__ __forceinline__ ChunkRef find_chunk(const KGroup &grp, int it) {
+// The problem that holds chunk `it` (a linear search over the launch's
+// problems: once per workgroup; later chunks are reached by next_chunk).
+__device__ __forceinline__ int find_problem(const int (&item0)[kGroupPerLaunch], int count, int it) {
     int pi = 0;
 #pragma unroll
-    for (int q = 1; q < kGroupPerLaunch; ++q)  // independent loads: one wait, not a chain
-        pi += (q < grp.count && it >= grp.item0[q]) ? 1 : 0;
-    const KProblem &a = grp.p[pi];
+    for (int q = 1; q < kGroupPerLaunch; ++q)
+        pi += (q < count && it >= item0[q]) ? 1 : 0;
+    return pi;
+}
+__device__ __forceinline__ ChunkRef chunk_in(const KProblem &a, int pi, int it) {
     const int loc = it - a.item0;
     const int tg = loc / a.cpt;
     return ChunkRef{pi, tg, loc - tg * a.cpt};
 }
 
-// The chunk after r (past the launch's last chunk it stays on the last
-// problem; such chunks are never real).
-__device__ __forceinline__ ChunkRef next_chunk(const KGroup &grp, ChunkRef r) {
-    const KProblem &a = grp.p[r.pi];
+// The chunk after r, a chunk of problem a (past the launch's last chunk it
+// stays on the last problem; such chunks are never real).
+__device__ __forceinline__ ChunkRef next_chunk(int count, const KProblem &a, ChunkRef r) {
     if (++r.c == a.cpt) {
         r.c = 0;
         if (++r.tg == a.ntg) {
             r.tg = 0;
-            r.pi = min(r.pi + 1, grp.count - 1);
+            r.pi = min(r.pi + 1, count - 1);
         }
     }
     return r;
@@ -510,18 +512,23 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                   "one panel record per chunk, one 1 KiB scale load per wave");
 
     const int lane = threadIdx.x & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
+    // The launch constants the first chunk's position needs, loaded as one
+    // batch: at kernel start every scalar load is a memory round trip, and the
+    // compiler would otherwise spread them over several.
     const int G = (int)gridDim.x;
+    const int count = grp.count, share = grp.share, extra = grp.extra, nrows = grp.N;
+    float *const part = grp.part;
+    int item0[kGroupPerLaunch];
+#pragma unroll
+    for (int q = 0; q < kGroupPerLaunch; ++q)
+        item0[q] = grp.item0[q];
+    __builtin_amdgcn_sched_barrier(0);
     // Workgroups go to the 8 XCDs in turn (blockIdx % 8); give each XCD a
     // contiguous run of ranges, so that the workgroups sharing an L2 walk
     // neighbouring tile groups and reuse each other's activation chunks.
-    const int b = [&] {
-        const int nq = G >> 3, nr = G & 7, xcd = (int)blockIdx.x & 7, loc = (int)blockIdx.x >> 3;
-        return xcd < nr ? xcd * (nq + 1) + loc : nr * (nq + 1) + (xcd - nr) * nq + loc;
-    }();
-    const int ib = range_start(grp, b, G), ie = range_start(grp, b + 1, G);
-    if (ib >= ie)
-        return;
-    const int nrows = grp.N;
+    const int b = xcd_run_index((int)blockIdx.x, G);
+    // (ib < ie: the grid never exceeds the launch's chunks)
+    const int ib = b * share + (b * extra) / G, ie = (b + 1) * share + ((b + 1) * extra) / G;
     uint8_t *sc_wave = lds + 2 * kActBuf + wave * 2 * kScBuf;  // this wave's two scale buffers
 
     // ---- weights of a chunk for this wave's T tiles (chunks past the range read zeros)
@@ -530,9 +537,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         int vw, s0, steps, wrow;
         const float *ts[T];
     };
-    auto make_src = [&](const ChunkRef &r, bool real) {
+    auto make_src = [&](const ChunkRef &r, const KProblem &a, bool real) {
         Src src;
-        const KProblem &a = grp.p[r.pi];
         const int M = a.M, K = a.K;
         src.wrow = FP8 ? K : (K >> 1);
         src.steps = steps_of(FP8, K);
@@ -578,21 +584,18 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     };
 
     // ---- a chunk's activations (whole workgroup) and this wave's scales
-    auto act_for = [&](const ChunkRef &r, bool real, int buf) {
-        const KProblem &a = grp.p[r.pi];
+    auto act_for = [&](const ChunkRef &r, const KProblem &a, bool real, int buf) {
         const int steps = steps_of(FP8, a.K);
         const int s0 = r.c * CH;
         const rsrc_t ra = make_rsrc(a.act, real ? (uint32_t)nrows * (uint32_t)a.K * 2u : 0u);
         stage_act_rows<W, CH / 4>(lds + buf * kActBuf, ra, a.K, s0, min(CH, steps - s0), wave, lane);
     };
-    auto scales_for = [&](const ChunkRef &r, bool real, int buf) {
+    auto scales_for = [&](const ChunkRef &r, const KProblem &a, bool real, int buf) {
         if constexpr (PANEL) {  // this wave's 1 KiB of the record's scale rows (its T tiles)
-            const KProblem &a = grp.p[r.pi];
             const rsrc_t rs = make_rsrc(a.w + ((size_t)r.tg * a.cpt + r.c) * kPanelRecordBytes,
                                         real ? (uint32_t)kPanelRecordBytes : 0u);
             bload16_lds(rs, sc_wave + buf * kScBuf, kPanelCodeBytes + wave * 1024 + 16 * lane);
         } else if constexpr (!FP8) {
-            const KProblem &a = grp.p[r.pi];
             const int NB = a.K >> 5, M = a.M;
             const int steps = steps_of(false, a.K);
             const int s0 = r.c * CH;
@@ -605,7 +608,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     };
 
     // ---- outputs and pieces
-    const rsrc_t rp = make_rsrc(grp.part, (uint32_t)G * 2u * TG * 1024u);
+    const rsrc_t rp = make_rsrc(part, (uint32_t)G * 2u * TG * 1024u);
     auto slot_off = [&](int wg, int side, int t) { return ((wg * 2 + side) * TG + wave * T + t) * 1024 + lane * 16; };
     auto store_tiles = [&](const KProblem &a, int tg, const f32x4 (&v)[T]) {
 #pragma unroll
@@ -629,14 +632,19 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // ---- prologue: the first chunk's activations and scales, the first
-    // round of weights
+    // round of weights.  The first chunk's problem record and the next
+    // problem's are read by value, in one round of loads.
     int it = ib;
-    ChunkRef cref = find_chunk(grp, it);
-    ChunkRef nref = next_chunk(grp, cref);
-    Src cur = make_src(cref, true);
-    Src nxt = make_src(nref, it + 1 < ie);
-    act_for(cref, true, 0);
-    scales_for(cref, true, 0);
+    const int pi0 = find_problem(item0, count, it);
+    const KProblem P0 = grp.p[pi0], P1 = grp.p[min(pi0 + 1, count - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    ChunkRef cref = chunk_in(P0, pi0, it);
+    ChunkRef nref = next_chunk(count, P0, cref);
+    const KProblem PN = nref.pi == pi0 ? P0 : P1;
+    Src cur = make_src(cref, P0, true);
+    Src nxt = make_src(nref, PN, it + 1 < ie);
+    act_for(cref, P0, true, 0);
+    scales_for(cref, P0, true, 0);
     static_for<PF>([&](auto U) { issue(U, cur, U.value); });
     wait_vmcnt<kIssueLoads>();  // the first chunk's activations and scales have landed
     lds_barrier();
@@ -649,8 +657,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         // them).  Issued before this chunk's math, after its first round of
         // weights, on every path: the compiler's waits for those weights
         // then never include the staging.
-        act_for(nref, it + 1 < ie, par ^ 1);
-        scales_for(nref, it + 1 < ie, par ^ 1);
+        act_for(nref, grp.p[nref.pi], it + 1 < ie, par ^ 1);
+        scales_for(nref, grp.p[nref.pi], it + 1 < ie, par ^ 1);
         const KProblem &ca = grp.p[cref.pi];
         const uint8_t *abuf = row + par * kActBuf;
         const uint16_t *sc0 = reinterpret_cast<const uint16_t *>(sc_wave + par * kScBuf) + j * scrow;
@@ -698,9 +706,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         lds_barrier();  // every wave is done with buffer `par`, and sees the next chunk's activations
         ++it;
         cref = nref;
-        nref = next_chunk(grp, nref);
+        nref = next_chunk(count, grp.p[nref.pi], nref);
         cur = nxt;
-        nxt = make_src(nref, it + 1 < ie);
+        nxt = make_src(nref, grp.p[nref.pi], it + 1 < ie);
         par ^= 1;
     }
 
@@ -734,14 +742,31 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             continue;
         if (lane == 0)  // every piece has arrived: leave the counter at zero for the next call
             __hip_atomic_store(grp.cnt + b0 * W + wave, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // The pieces' loads go out kSumBatch workgroups at a time (one round
+        // trip for the usual two to four pieces); the adds keep range order.
+        // The explicit wait before the stores matters: without it every
+        // output store waits for the one before it to complete.
+        constexpr int kSumBatch = 4;
         f32x4 sum[T];
-        for (int wg = b0; wg <= b1; ++wg) {
-            const int sd = wg < b1 ? 1 : 0;
+        for (int wg0 = b0; wg0 <= b1; wg0 += kSumBatch) {
+            f32x4 v[kSumBatch][T];
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const f32x4 v = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, slot_off(wg, sd, t), 0, kCoherent));
-                sum[t] = wg == b0 ? v : sum[t] + v;
+            for (int u = 0; u < kSumBatch; ++u) {
+                const int wg = wg0 + u;
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    v[u][t] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   rp, wg <= b1 ? slot_off(wg, wg < b1 ? 1 : 0, t) : kOut, 0, kCoherent));
+            }
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int u = 0; u < kSumBatch; ++u) {
+                if (wg0 + u > b1)
+                    break;
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    sum[t] = wg0 + u == b0 ? v[u][t] : sum[t] + v[u][t];
             }
         }
         store_tiles(a, pend_tg[side], sum);
@@ -873,12 +898,14 @@ hipError_t launch_tw(const VerifyLaunch &l) {
     if (items >= ((int64_t)1 << 31))
         return hipErrorInvalidValue;
     grp.items = (int)items;
-    int grid = (int)items;
+    int grid = (int)items;  // the walk kernel relies on grid <= items: every range holds a chunk
     if (walk) {
         grid = std::min(grid, resident_groups(kern, 64 * W, shm));
         grid = std::min(grid, pl.groups > 0 ? std::min(pl.groups, kMaxWalkGroups) : kMaxWalkGroups);
         grp.cnt = static_cast<uint32_t *>(l.workspace);
         grp.part = reinterpret_cast<float *>(static_cast<char *>(l.workspace) + kWalkCounterBytes);
+        if (grid < 1 || grid > items)  // the kernel does not check for an empty range
+            return hipErrorInvalidValue;
         grp.share = (int)(items / grid);
         grp.extra = (int)(items % grid);  // below grid <= 1024: b * extra stays in 32 bits
     }
