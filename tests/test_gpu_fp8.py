@@ -116,6 +116,16 @@ def test_fp8_walk_shapes(tpw, wpg, groups):
     parity(out_to_f64(q.run(f["act"], **kw)), q.oracle(f["act"]), "bf16")
 
 
+@pytest.mark.parametrize("groups", [4, 5])
+def test_fp8_walk_long_shares(groups):
+    """45 chunks over 4 or 5 workgroups (11.25 and 9 per share): tile groups
+    of 5 chunks cut by range edges at several places."""
+    f = W.fp8(M=272, K=5120, N=16)
+    q = FP8(f["w"], f["tscales"])
+    kw = dict(tiles_per_wave=1, waves_per_group=2, max_groups=groups, workspace=big_workspace())
+    parity(out_to_f64(q.run(f["act"], **kw)), q.oracle(f["act"]), "bf16")
+
+
 @pytest.mark.parametrize("tpw", [1, 2, 4])
 @pytest.mark.parametrize("wpg", [2, 4, 8])
 def test_fp8_one_shot_shapes(tpw, wpg):

@@ -172,10 +172,12 @@ def test_same_bits_as_row_major_walk_when_uncut(M, K):
     assert torch.equal(p.run(a, max_groups=1, workspace=ws), ref)
 
 
-@pytest.mark.parametrize("M,K,groups", [(400, 5120, 3), (17408, 5120, 0), (300, 17408, 40)])
+@pytest.mark.parametrize("M,K,groups", [(400, 5120, 3), (17408, 5120, 0), (300, 17408, 40),
+                                         (1000, 5120, 3), (17408, 5120, 80), (300, 17408, 5)])
 def test_cut_tile_groups_parity(M, K, groups):
     """Workgroups cut tile groups at chunk boundaries (4 steps of 128 k in the
-    panel layout, 8 row-major): both layouts within the bar of the oracle."""
+    panel layout, 8 row-major), with shares from 1.7 to 13.6 chunks: both
+    layouts within the bar of the oracle."""
     g = np.random.Generator(np.random.PCG64(409))
     p = Panel(W.q4_0_codes(M, K, g), W.fp16_scales_lognormal(M, K, g))
     a = W.f32_to_bf16_bits(0.5 * g.standard_t(3, size=(16, K)))

@@ -225,6 +225,28 @@ def test_walk_many_pieces(groups):
         assert np.array_equal(bits_u16(q.run(np.ascontiguousarray(x[n:n + 1]), **kw))[0], bits_u16(y)[n])
 
 
+@pytest.mark.parametrize("groups", [5, 6])
+def test_walk_range_edges_exact(groups):
+    """51 chunks over 5 or 6 workgroups (10.2 and 8.5 per share), so range
+    edges fall inside tile groups at several places.  With integer weights and
+    activations every output is an exact integer, so a step computed twice or
+    dropped at a range edge shows; then real scales against the oracle, and
+    rows bit-identical alone."""
+    g = np.random.Generator(np.random.PCG64(113))
+    M, K, N = 300, 17408, 16
+    codes = W.q4_0_codes(M, K, g)
+    kw = dict(tiles_per_wave=2, waves_per_group=4, max_groups=groups, workspace=big_workspace())
+    qi = Q4(codes, np.full((M, K // 32), 0x3C00, dtype=np.uint16))
+    ai = W.f32_to_bf16_bits(g.integers(-4, 5, size=(N, K)))
+    assert np.array_equal(out_to_f64(qi.run(ai, "bf16", "f32", **kw)), qi.oracle(ai))
+    q = Q4(codes, W.fp16_scales_lognormal(M, K, g))
+    x = W.f32_to_bf16_bits(0.5 * g.standard_t(3, size=(N, K)))
+    y = q.run(x, **kw)
+    parity(out_to_f64(y), q.oracle(x), "bf16")
+    for n in (0, 13):
+        assert np.array_equal(bits_u16(q.run(np.ascontiguousarray(x[n:n + 1]), **kw))[0], bits_u16(y)[n])
+
+
 @pytest.mark.parametrize("tpw", [1, 2, 4])
 @pytest.mark.parametrize("wpg", [2, 4, 8])
 def test_every_one_shot_shape_parity_and_exact_integers(tpw, wpg):
