@@ -486,8 +486,8 @@ __device__ __forceinline__ ChunkRef next_chunk(int count, const KProblem &a, Chu
 // longer ones are spread evenly over the logical ids (so over the XCDs, which
 // take contiguous runs of ids); items = share * G + extra keeps the start in
 // 32 bits.
-__device__ __forceinline__ int range_start(const KGroup &grp, int b, int G) {
-    return b * grp.share + (b * grp.extra) / G;
+__device__ __forceinline__ int range_start(int b, int share, int extra, int G) {
+    return b * share + (b * extra) / G;
 }
 __device__ __forceinline__ int range_owner(const KGroup &grp, int c, int G) {
     return (int)(((int64_t)(c + 1) * G - 1) / grp.items);
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // neighbouring tile groups and reuse each other's activation chunks.
     const int b = xcd_run_index((int)blockIdx.x, G);
     // (ib < ie: the grid never exceeds the launch's chunks)
-    const int ib = b * share + (b * extra) / G, ie = (b + 1) * share + ((b + 1) * extra) / G;
+    const int ib = range_start(b, share, extra, G), ie = range_start(b + 1, share, extra, G);
     uint8_t *sc_wave = lds + 2 * kActBuf + wave * 2 * kScBuf;  // this wave's two scale buffers
 
     // ---- weights of a chunk for this wave's T tiles (chunks past the range read zeros)
