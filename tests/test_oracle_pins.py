@@ -432,6 +432,76 @@ def test_block_quant_without_rotation():
     assert np.array_equal(q8, qr) and np.array_equal(d8, dr)
 
 
+def _rounding_blocks(golden_dir):
+    """The hand-worked blocks of quant_rounding_blocks.txt: (name, qmax,
+    rotate, dtype code, input bits [32], expected d bits, expected q [32])."""
+    from scipy.linalg import hadamard
+    h = hadamard(32).astype(np.float64)
+    out = []
+    with open(os.path.join(golden_dir, "quant_rounding_blocks.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, qmax, rotate, dt, dbits, *ents = line.split()
+            u = np.zeros(32)
+            q = np.zeros(32, dtype=np.int64)
+            for e in ents:
+                i, uv, qv = e.split(":")
+                u[int(i)] = float.fromhex(uv) if "0x" in uv else float(uv)
+                q[int(i)] = int(qv)
+            x = h @ u / 32 if rotate == "1" else u
+            if dt == "f16":
+                bits = W.f32_to_f16_bits(x)
+                back = _np_f16(bits)
+                code = oracle.F16
+            else:
+                bits = W.f32_to_bf16_bits(x)
+                back = _torch_bf16(bits)
+                code = oracle.BF16
+            assert np.array_equal(back, x), name  # the fixture's input is exact in its dtype
+            out.append((name, int(qmax), rotate == "1", code, bits, int(dbits, 16), q))
+    return out
+
+
+def test_quant_rounding_rules_golden(golden_dir):
+    """Hand-worked blocks: ties of u / d go to the even code, the code divides
+    by the stored fp16 scale (not the fp32 quotient), and the clamp to
+    +-qmax acts where the scale rounds down into the fp16 subnormals.  An
+    oracle rounding half away from zero, dividing by fp32(amax / qmax) or
+    leaving out the clamp fails here."""
+    blocks = _rounding_blocks(golden_dir)
+    assert {b[0].rstrip("u") for b in blocks} == {"tie127", "tie7", "stored127", "stored7", "clamp127", "clamp7"}
+    for name, qmax, rotate, code, bits, dbits, qref in blocks:
+        q, d, st = oracle.block_quant(bits.reshape(1, 32), code, 1, 32, qmax, rotate)
+        assert st == 0, name
+        assert int(d[0, 0]) == dbits, (name, hex(int(d[0, 0])))
+        assert np.array_equal(q[0].astype(np.int64), qref), (name, q[0], qref)
+        if rotate:  # the named quantizers are the rotated rule
+            fn = oracle.h32_quant_int8 if qmax == 127 else oracle.h32_quant_int4
+            q2, d2, _ = fn(bits.reshape(1, 32), code, 1, 32)
+            assert np.array_equal(q2, q) and np.array_equal(d2, d), name
+
+
+def test_quant_clamp_binds_only_below_fp16_normals():
+    """The clamp can act only when d = fp16(amax / qmax) rounds down by more
+    than half a code: with a normal fp16 d the relative rounding is at most
+    2^-11, so |u| / d <= qmax (1 + 2^-10) < qmax + 1/2 and rint never leaves
+    the range.  Checked on a sweep of amax over the normal range: every
+    block's largest code is exactly qmax and no code exceeds it."""
+    g = np.random.Generator(np.random.PCG64(91))
+    for qmax in (127, 7):
+        amax = np.exp2(g.uniform(-13.5, 15, size=2000)) * qmax
+        x = np.zeros((2000, 32))
+        x[:, 0] = amax
+        x[:, 1:] = g.uniform(-1, 1, size=(2000, 31)) * amax[:, None]
+        bits = W.f32_to_bf16_bits(x)
+        q, d, st = oracle.block_quant(bits, oracle.BF16, 2000, 32, qmax, False)
+        assert st == 0
+        assert np.all(_np_f16(d) >= 2.0 ** -14)  # every scale is a normal fp16
+        assert np.all(np.abs(q.astype(np.int64)).max(axis=1) == qmax)
+
+
 def test_activation_rounding_error_study():
     """Prompt-processing numerics on the prefill activations (Student-t rows
     with outlier channels): the error that rounding the activations alone adds
