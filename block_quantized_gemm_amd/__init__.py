@@ -32,6 +32,11 @@ KIND_FP8_BLK128 = 1
 KIND_Q4_0_PANEL = 2
 _KINDS = {"q4_0": KIND_Q4_0, "fp8": KIND_FP8_BLK128, "q4_0_panel": KIND_Q4_0_PANEL}
 
+PROBE_BLOCKS = 0
+PROBE_SHARES = 1
+PROBE_WINDOW = 2
+_PROBES = {"blocks": PROBE_BLOCKS, "shares": PROBE_SHARES, "window": PROBE_WINDOW}
+
 DTYPE_F16 = 1
 DTYPE_BF16 = 2
 DTYPE_F32 = 3
@@ -65,6 +70,7 @@ SIGNATURES = {
     "vq_greedy_verify": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "vq_q4_0_rotate_h32": (_I, [_P, _P, _I64, _I64, _P, _P, _P]),
     "vq_greedy_workspace_bytes": (_SZ, [_I64, _I64]),
+    "vq_hbm_read_probe": (_I, [_P, _SZ, _I, _I, _I, _I, _I, _P, _P]),
     "vq_status_string": (ctypes.c_char_p, [_I]),
     "vq_version": (_I, []),
 }
@@ -149,12 +155,18 @@ class Workspace:
     workgroups.
 
     The library leaves the counters at zero after every call, so it is zeroed
-    once.  Calls sharing one workspace must be ordered (one stream)."""
+    once.  The zero fill runs on torch's current stream and is waited for here,
+    so the buffer is ready for a call on any stream.  Calls sharing one
+    workspace must be ordered (one stream, or streams the caller orders)."""
 
     def __init__(self, nbytes: int, device=None):
         torch = _torch()
-        self.tensor = torch.zeros(max(int(nbytes), 16), dtype=torch.uint8,
-                                  device=device if device is not None else "cuda")
+        dev = torch.device(device if device is not None else "cuda")
+        alloc = torch.cuda.current_stream(dev)
+        self.tensor = torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=dev)
+        if not torch.cuda.is_current_stream_capturing():
+            alloc.synchronize()
+        self._streams = {alloc.cuda_stream}
 
     @property
     def nbytes(self) -> int:
@@ -162,6 +174,15 @@ class Workspace:
 
     def ptr(self) -> int:
         return self.tensor.data_ptr()
+
+    def used_on(self, stream_handle: int):
+        """Tell torch's caching allocator that kernels on this stream use the
+        buffer, so that once the Workspace is dropped the memory is not handed
+        out again before that stream's work is done."""
+        if stream_handle not in self._streams:
+            torch = _torch()
+            self.tensor.record_stream(torch.cuda.ExternalStream(stream_handle, device=self.tensor.device))
+            self._streams.add(stream_handle)
 
 
 _auto_ws = {}
@@ -174,6 +195,7 @@ def _workspace_args(workspace, kind: int, m: int, k: int, device, stream_handle:
     if workspace is None:
         return None, 0
     if isinstance(workspace, Workspace):
+        workspace.used_on(stream_handle)
         return workspace.ptr(), workspace.nbytes
     if workspace != "auto":
         raise TypeError("workspace must be a Workspace, None or 'auto'")
@@ -186,6 +208,7 @@ def _workspace_args(workspace, kind: int, m: int, k: int, device, stream_handle:
         if ws is None or ws.nbytes < need:
             ws = Workspace(need, device)
             _auto_ws[key] = ws
+        ws.used_on(stream_handle)
     return ws.ptr(), ws.nbytes
 
 
@@ -399,18 +422,21 @@ class GroupedCall:
 
     def __call__(self, stream=None):
         L = lib()
+        sh = _stream(stream)
+        if self.ws is not None:
+            self.ws.used_on(sh)
         wp, wn = (self.ws.ptr(), self.ws.nbytes) if self.ws is not None else (None, 0)
         if self.kind == KIND_Q4_0:
             st = L.vq_gemm_q4_0_grouped(self.table, self.count, self.act_dtype, self.out_dtype, self.n_rows,
-                                        self.alpha, wp, wn, _stream(stream))
+                                        self.alpha, wp, wn, sh)
             _check(st, "vq_gemm_q4_0_grouped")
         elif self.kind == KIND_Q4_0_PANEL:
             st = L.vq_gemm_q4_0_panel_grouped(self.table, self.count, self.act_dtype, self.out_dtype,
-                                              self.n_rows, self.alpha, wp, wn, _stream(stream))
+                                              self.n_rows, self.alpha, wp, wn, sh)
             _check(st, "vq_gemm_q4_0_panel_grouped")
         else:
             st = L.vq_gemm_fp8_blk128_grouped(self.table, self.count, self.act_dtype, self.out_dtype,
-                                              self.n_rows, wp, wn, _stream(stream))
+                                              self.n_rows, wp, wn, sh)
             _check(st, "vq_gemm_fp8_blk128_grouped")
 
 
@@ -505,6 +531,7 @@ def greedy_verify(logits, draft, tokens_out=None, count_out=None, *, workspace="
                 _auto_ws[key] = ws
     else:
         raise TypeError("workspace must be a Workspace or 'auto'")
+    ws.used_on(sh)
     dptr = _dev_ptr(draft, "draft") if (draft is not None and draft.numel()) else None
     st = lib().vq_greedy_verify(_dev_ptr(logits, "logits"), _dtype_code(logits), n, v, dptr,
                                 _dev_ptr(tokens_out, "tokens_out"), _dev_ptr(count_out, "count_out"),
@@ -524,3 +551,22 @@ def default_launch_shape(kind: str, m: int, k: int, workspace_bytes=None):
                                          ctypes.byref(t), ctypes.byref(w), ctypes.byref(s), ctypes.byref(used)),
            "vq_default_launch_shape")
     return t.value, w.value, s.value, used.value
+
+
+def hbm_read_probe(buf, sink, *, mode: str = "blocks", groups: int = 0, waves_per_group: int = 8, depth: int = 8,
+                   nontemporal: bool = False, stream=None):
+    """One plain read of the device tensor `buf` (its bytes, a multiple of
+    64 KiB up to 2 GiB) by the probe kernel; sink: a device tensor of >= 4
+    bytes.  mode "blocks" (one workgroup per 64 KiB; groups 0), "shares"
+    (`groups` persistent workgroups, contiguous shares) or "window" (`groups`
+    persistent workgroups sweeping 64 KiB blocks); nontemporal: the loads'
+    cache policy."""
+    if mode not in _PROBES:
+        raise ValueError("mode must be one of %s" % sorted(_PROBES))
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold 4 bytes")
+    st = lib().vq_hbm_read_probe(_dev_ptr(buf, "buf"), buf.numel() * buf.element_size(), _PROBES[mode],
+                                 int(groups), int(waves_per_group), int(depth), int(bool(nontemporal)),
+                                 _dev_ptr(sink, "sink"),
+                                 _stream(stream))
+    _check(st, "vq_hbm_read_probe")

@@ -1,0 +1,106 @@
+// hbm_probe.hip -- a plain HBM read probe: the denominator that the verify
+// kernels' streaming rate is compared against on the device at hand.
+//
+// The verify GEMM is a weight stream: its ideal is to read every byte once at
+// the rate HBM delivers to a kernel that does nothing else ("Qwen3.8-27B on the
+// AMD R9700: up to 227 tok/s", TL;DR: plain decode streams the weights at a
+// fraction of the card's bandwidth).  This kernel reads a buffer once with the
+// verify kernels' load instruction (16 bytes per lane, 1 KiB per wave
+// instruction, raw buffer loads) and folds the words into one XOR per thread,
+// stored only if it equals a value the caller never passes, so that no load
+// can be dropped.  Three access patterns:
+//   blocks  -- one workgroup per 64 KiB block (as many workgroups as blocks;
+//              the hardware keeps several per CU);
+//   shares  -- `groups` persistent workgroups, workgroup b reading the b-th of
+//              `groups` equal contiguous shares front to back, its waves
+//              interleaved 1 KiB apart (the walk kernel's pattern);
+//   window  -- `groups` persistent workgroups reading 64 KiB blocks b, b + G,
+//              b + 2G, ... (the whole grid sweeps one contiguous window).
+// Each wave keeps `depth` loads in flight.  The loads use the default cache
+// policy or the non-temporal one (a stream read once: on gfx950 the latter
+// reaches a higher read rate).
+#include "vq_device.h"
+#include "vq_internal.h"
+
+namespace vq {
+
+namespace {
+
+constexpr int kPiece = 1024;       // one wave instruction: 64 lanes x 16 bytes
+constexpr int kBlock = 64 * 1024;  // blocks of the blocks and window patterns
+
+struct ProbeArgs {
+    const uint8_t *buf;
+    uint32_t bytes;
+    int mode;
+    uint32_t share;     // shares: bytes per workgroup (a multiple of kPiece)
+    uint32_t sentinel;  // never equal to a real XOR in practice
+    uint32_t *sink;
+};
+
+template <int W, int D, int AUX>
+__global__ __launch_bounds__(64 * W) void hbm_probe_kernel(const ProbeArgs a) {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int b = (int)blockIdx.x, G = (int)gridDim.x;
+    const rsrc_t r = make_rsrc(a.buf, a.bytes);
+    // byte offset of this wave's j-th piece
+    auto piece = [&](int j) -> uint32_t {
+        if (a.mode == VQ_PROBE_BLOCKS)
+            return (uint32_t)b * kBlock + (uint32_t)(wave + W * j) * kPiece;
+        if (a.mode == VQ_PROBE_SHARES)
+            return (uint32_t)b * a.share + (uint32_t)(wave + W * j) * kPiece;
+        constexpr int per = kBlock / kPiece / W;  // pieces of one block per wave
+        const int blk = j / per, in = j - blk * per;
+        return ((uint32_t)blk * (uint32_t)G + (uint32_t)b) * kBlock + (uint32_t)(wave + W * in) * kPiece;
+    };
+    int n;  // pieces of this wave
+    if (a.mode == VQ_PROBE_BLOCKS)
+        n = kBlock / kPiece / W;
+    else if (a.mode == VQ_PROBE_SHARES)
+        n = (int)(a.share / kPiece) / W;
+    else
+        n = (int)((a.bytes / kBlock + G - 1 - b) / G) * (kBlock / kPiece / W);
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    u32x4 st[D];
+    pipeline<D>(
+        n, [&](auto U, int j) { st[U.value] = bload16<AUX>(r, (int)(piece(j) + 16u * lane), 0); },
+        [&](auto U, int, bool) { acc ^= st[U.value]; });
+    const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (x == a.sentinel)
+        a.sink[0] = x;
+}
+
+template <int W, int AUX>
+hipError_t launch_w(const ProbeArgs &a, int grid, int depth, hipStream_t s) {
+    switch (depth) {
+    case 4: hipLaunchKernelGGL((hbm_probe_kernel<W, 4, AUX>), dim3(grid), dim3(64 * W), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((hbm_probe_kernel<W, 8, AUX>), dim3(grid), dim3(64 * W), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((hbm_probe_kernel<W, 16, AUX>), dim3(grid), dim3(64 * W), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int AUX>
+hipError_t launch_aux(const ProbeArgs &a, int grid, int waves, int depth, hipStream_t s) {
+    switch (waves) {
+    case 4: return launch_w<4, AUX>(a, grid, depth, s);
+    case 8: return launch_w<8, AUX>(a, grid, depth, s);
+    case 16: return launch_w<16, AUX>(a, grid, depth, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_hbm_probe(const void *buf, size_t bytes, int mode, int groups, int waves, int depth,
+                            bool nontemporal, uint32_t *sink, hipStream_t stream) {
+    ProbeArgs a{static_cast<const uint8_t *>(buf), (uint32_t)bytes, mode, 0u, 0x9E3779B9u, sink};
+    if (mode == VQ_PROBE_SHARES)
+        a.share = (uint32_t)(bytes / (size_t)groups);
+    const int grid = mode == VQ_PROBE_BLOCKS ? (int)(bytes / kBlock) : groups;
+    return nontemporal ? launch_aux<kAuxStream>(a, grid, waves, depth, stream)
+                       : launch_aux<kAuxCached>(a, grid, waves, depth, stream);
+}
+
+}  // namespace vq

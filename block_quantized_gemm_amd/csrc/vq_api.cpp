@@ -522,6 +522,34 @@ int vq_greedy_verify(const void *logits, int logits_dtype, int64_t n_rows, int64
                : VQ_ERR_LAUNCH;
 }
 
+int vq_hbm_read_probe(const void *buf, size_t bytes, int mode, int groups, int waves_per_group, int depth,
+                      int nontemporal, uint32_t *sink, void *stream) {
+    if (!buf || !sink)
+        return VQ_ERR_NULL_POINTER;
+    if (!aligned16(buf) || !aligned16(sink))
+        return VQ_ERR_MISALIGNED;
+    if (bytes < 65536 || bytes > ((size_t)1 << 31) || bytes % 65536 != 0)
+        return VQ_ERR_BAD_SHAPE;
+    if (mode != VQ_PROBE_BLOCKS && mode != VQ_PROBE_SHARES && mode != VQ_PROBE_WINDOW)
+        return VQ_ERR_BAD_CONFIG;
+    if ((waves_per_group != 4 && waves_per_group != 8 && waves_per_group != 16) ||
+        (depth != 4 && depth != 8 && depth != 16))
+        return VQ_ERR_BAD_CONFIG;
+    if (mode == VQ_PROBE_BLOCKS ? groups != 0 : (groups < 1 || groups > 65535))
+        return VQ_ERR_BAD_CONFIG;
+    if (nontemporal != 0 && nontemporal != 1)
+        return VQ_ERR_BAD_CONFIG;
+    if (mode == VQ_PROBE_SHARES && bytes % ((size_t)groups * (size_t)waves_per_group * 1024) != 0)
+        return VQ_ERR_BAD_SHAPE;
+    const int dev = check_device();
+    if (dev != VQ_OK)
+        return dev;
+    return vq::launch_hbm_probe(buf, bytes, mode, groups, waves_per_group, depth, nontemporal != 0, sink,
+                                static_cast<hipStream_t>(stream)) == hipSuccess
+               ? VQ_OK
+               : VQ_ERR_LAUNCH;
+}
+
 const char *vq_status_string(int status) {
     switch (status) {
     case VQ_OK: return "ok";

@@ -121,4 +121,8 @@ hipError_t launch_h32_quant(const void *x, int x_dtype, int8_t *q, void *d, int 
 hipError_t launch_q4_rotate_h32(const void *codes, const void *scales, int M, int K, void *codes_out,
                                 void *scales_out, hipStream_t stream);
 
+// The HBM read probe (one kernel; arguments checked by the caller).
+hipError_t launch_hbm_probe(const void *buf, size_t bytes, int mode, int groups, int waves, int depth,
+                            bool nontemporal, uint32_t *sink, hipStream_t stream);
+
 }  // namespace vq

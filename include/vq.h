@@ -392,6 +392,33 @@ int vq_greedy_verify(const void *logits, int logits_dtype, int64_t n_rows, int64
                      void *workspace, size_t workspace_bytes, void *stream);
 size_t vq_greedy_workspace_bytes(int64_t n_rows, int64_t vocab);
 
+/*
+ * vq_hbm_read_probe -- a plain read of `bytes` of device memory at `buf`,
+ * the bandwidth the verify GEMM's weight stream is measured against ([P1]
+ * TL;DR: decode streams the weights at a fraction of the card's bandwidth,
+ * so the ceiling on the device at hand is worth knowing).  Every 16-byte
+ * piece is loaded once with the verify kernels' load instruction (raw buffer
+ * loads, 1 KiB per wave instruction) and folded into an XOR; nothing is
+ * written except, in the unlikely case that some thread's XOR equals a fixed
+ * 32-bit constant, that value to sink[0].  Patterns (`mode`):
+ *   VQ_PROBE_BLOCKS  one workgroup per 64 KiB block (groups must be 0);
+ *   VQ_PROBE_SHARES  `groups` workgroups, each reading one of `groups` equal
+ *                    contiguous shares front to back (the walk kernel's
+ *                    pattern); bytes % (groups * waves_per_group * 1024) == 0;
+ *   VQ_PROBE_WINDOW  `groups` workgroups reading 64 KiB blocks b, b + groups,
+ *                    b + 2 groups, ...
+ * waves_per_group 4, 8 or 16; depth (loads in flight per wave) 4, 8 or 16;
+ * nontemporal 0 (default cache policy) or 1 (non-temporal loads, the policy
+ * of a stream read once); 65536 <= bytes <= 2^31, bytes % 65536 == 0;
+ * 1 <= groups <= 65535 for the persistent patterns.  sink: 4 bytes of device
+ * memory.  One kernel on `stream`; time it with events on that stream.
+ */
+#define VQ_PROBE_BLOCKS 0
+#define VQ_PROBE_SHARES 1
+#define VQ_PROBE_WINDOW 2
+int vq_hbm_read_probe(const void *buf, size_t bytes, int mode, int groups, int waves_per_group, int depth,
+                      int nontemporal, uint32_t *sink, void *stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *vq_status_string(int status);
 

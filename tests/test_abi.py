@@ -292,3 +292,27 @@ def test_fp8_prefill_argument_errors():
     assert f(A, B, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 512, 256, 480, None) == vq.VQ_ERR_BAD_SHAPE
     assert f(A, B, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 0, 256, 512, None) == vq.VQ_ERR_BAD_SHAPE
     assert f(A, B, C + 2, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 512, 256, 512, None) == vq.VQ_ERR_MISALIGNED
+
+
+def test_hbm_probe_argument_errors():
+    L = vq.lib()
+
+    def probe(buf=A, nbytes=1 << 20, mode=vq.PROBE_BLOCKS, groups=0, waves=8, depth=8, nt=0, sink=B):
+        return L.vq_hbm_read_probe(buf, nbytes, mode, groups, waves, depth, nt, sink, None)
+    assert probe(buf=None) == vq.VQ_ERR_NULL_POINTER
+    assert probe(sink=None) == vq.VQ_ERR_NULL_POINTER
+    assert probe(buf=A + 8) == vq.VQ_ERR_MISALIGNED
+    assert probe(nbytes=65536 + 1024) == vq.VQ_ERR_BAD_SHAPE
+    assert probe(nbytes=0) == vq.VQ_ERR_BAD_SHAPE
+    assert probe(nbytes=(1 << 31) + 65536) == vq.VQ_ERR_BAD_SHAPE
+    assert probe(mode=3) == vq.VQ_ERR_BAD_CONFIG
+    assert probe(waves=2) == vq.VQ_ERR_BAD_CONFIG
+    assert probe(depth=5) == vq.VQ_ERR_BAD_CONFIG
+    assert probe(nt=2) == vq.VQ_ERR_BAD_CONFIG
+    assert probe(groups=4) == vq.VQ_ERR_BAD_CONFIG                     # blocks: no group count
+    assert probe(mode=vq.PROBE_SHARES, groups=0) == vq.VQ_ERR_BAD_CONFIG
+    assert probe(mode=vq.PROBE_SHARES, groups=3) == vq.VQ_ERR_BAD_SHAPE  # shares must divide evenly
+    assert probe(mode=vq.PROBE_WINDOW, groups=70000) == vq.VQ_ERR_BAD_CONFIG
+    # valid arguments get as far as the device check (no GPU here)
+    if not torch.cuda.is_available():
+        assert probe(mode=vq.PROBE_SHARES, groups=16) == vq.VQ_ERR_DEVICE

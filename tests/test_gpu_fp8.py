@@ -76,15 +76,28 @@ def test_fp8_tile_scale_index_exact():
     assert np.array_equal(out_to_f64(q.run(a, "bf16", "f32")), q.oracle(a))
 
 
-def test_fp8_rows_bit_identical_across_widths():
-    f = W.fp8(M=5120, K=5120, N=16)
+@pytest.mark.parametrize("M", [5120, 17408])
+def test_fp8_rows_bit_identical_across_widths(M):
+    """Both FP8 workload shapes: every row at N = 1, the 4-row and 8-row
+    blocks, a permuted block and junk neighbours give the 16-row call's bits."""
+    f = W.fp8(M=M, K=5120, N=16)
     q = FP8(f["w"], f["tscales"])
     x = f["act"]
     full = bits_u16(q.run(x))
     for n in range(16):
         assert np.array_equal(bits_u16(q.run(np.ascontiguousarray(x[n:n + 1])))[0], full[n]), n
     assert np.array_equal(bits_u16(q.run(np.ascontiguousarray(x[4:8]))), full[4:8])
+    for h in (0, 8):
+        assert np.array_equal(bits_u16(q.run(np.ascontiguousarray(x[h:h + 8]))), full[h:h + 8])
+    perm = np.random.Generator(np.random.PCG64(M)).permutation(16)
+    assert np.array_equal(bits_u16(q.run(np.ascontiguousarray(x[perm]))), full[perm])
+    junk = W.f32_to_bf16_bits(np.random.Generator(np.random.PCG64(M + 1)).standard_normal((16, 5120)) * 30)
+    junk[11] = x[2]
+    assert np.array_equal(bits_u16(q.run(junk))[11], full[2])
     assert np.array_equal(bits_u16(q.run(x)), full)
+    if M == 17408:
+        cols = np.unique(np.concatenate([[0, M - 1], np.random.Generator(np.random.PCG64(3)).choice(M, 300)]))
+        parity(out_to_f64(q.run(x))[:, cols], q.oracle(x, cols=cols), "bf16")
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 1), (300, 384, 5), (130, 1280, 33)])

@@ -257,6 +257,52 @@ def test_grouped_layer_parity_and_rows_invariant():
         assert torch.equal(o[0], yp[6])
 
 
+def _grouped(kind, mats, xs, ws):
+    """One grouped call over the layer's matrices with activations xs[i]."""
+    outs = [torch.empty((x.shape[0], p.M), dtype=torch.bfloat16, device="cuda") for (p, _, _), x in zip(mats, xs)]
+    if kind == "q4_0_panel":
+        probs = [(p.panel, p.M, x, o) for (p, _, _), x, o in zip(mats, xs, outs)]
+    else:
+        probs = [(p.codes, p.scales, x, o) for (p, _, _), x, o in zip(mats, xs, outs)]
+    vq.GroupedCall(kind, probs, workspace=ws)()
+    torch.cuda.synchronize()
+    return [bits_u16(o) for o in outs]
+
+
+@pytest.mark.parametrize("kind", ["q4_0_panel", "q4_0"])
+def test_grouped_layer_rows_bit_identical_at_every_width(kind):
+    """The benchmarked form (one grouped call over a layer's five stream
+    matrices) at every width: each row at N = 1, both 8-row halves, a permuted
+    block and blocks whose other rows are junk return the bits of the 16-row
+    call, for all five matrices."""
+    g = np.random.Generator(np.random.PCG64(414))
+    mats = _layer(g)
+    ws = vq.Workspace(64 << 20)
+    full = _grouped(kind, mats, [x for _, _, x in mats], ws)
+    for r in range(16):
+        one = _grouped(kind, mats, [x[r:r + 1].contiguous() for _, _, x in mats], ws)
+        for i, (o, f) in enumerate(zip(one, full)):
+            assert np.array_equal(o[0], f[r]), (kind, i, r)
+    for h in (0, 8):
+        half = _grouped(kind, mats, [x[h:h + 8].contiguous() for _, _, x in mats], ws)
+        for i, (o, f) in enumerate(zip(half, full)):
+            assert np.array_equal(o, f[h:h + 8]), (kind, i, h)
+    perm = g.permutation(16)
+    pt = torch.from_numpy(perm).cuda()
+    per = _grouped(kind, mats, [x[pt].contiguous() for _, _, x in mats], ws)
+    for i, (o, f) in enumerate(zip(per, full)):
+        assert np.array_equal(o, f[perm]), (kind, i)
+    for tgt, pos in ((0, 15), (9, 4)):
+        xs = []
+        for _, bits, x in mats:
+            j = to_dev(W.f32_to_bf16_bits(40 * g.standard_normal((16, x.shape[1]))), torch.bfloat16)
+            j[pos] = x[tgt]
+            xs.append(j)
+        jk = _grouped(kind, mats, xs, ws)
+        for i, (o, f) in enumerate(zip(jk, full)):
+            assert np.array_equal(o[pos], f[tgt]), (kind, i, tgt)
+
+
 def test_grouped_graph_replays_match_eager():
     g = np.random.Generator(np.random.PCG64(413))
     mats = []

@@ -74,6 +74,42 @@ def test_ffn_config_parity_sampled(ffn, n_rows):
     print("ffn N=%d: relF %.3e worst %.3e max %.2f ulp" % (n_rows, fro, worst, ulps))
 
 
+def test_ffn_f16_outlier_rows_f32_out():
+    """fp16 activations with the FFN rows' heavy tails and x50 outlier channels,
+    fp32 outputs.  The block MFMA adds sum x (1024 + q) and -1032 sum x, two
+    terms about 130 times the block dot that mostly cancel, so fp32 rounding
+    is amplified by about that factor for fp16 rows (17 for bf16, whose codes
+    are 128 + q); the 1 ulp + 1e-4 rms per-element check measures it."""
+    t = W.ffn(N=16)
+    q = Q4(t["codes"], t["scales"])
+    g = W.rng(W.CFG_FFN, 0, W.T_ACT)
+    a = W.act_student_outliers(16, q.K, g, W.rng(W.CFG_FFN, 0, W.T_OUTLIER), dtype="f16")
+    y = out_to_f64(q.run(a, "f16", "f32"))
+    cols = _sample_cols(q.M, 512, 17)
+    fro, worst, ulps = parity(y[:, cols], q.oracle(a, "f16", cols=cols), "f32")
+    print("ffn f16 rows, f32 out: relF %.3e worst %.3e max %.2f ulp" % (fro, worst, ulps))
+
+
+def test_auto_workspace_on_a_fresh_side_stream():
+    """workspace="auto" on a stream other than torch's current one, from an
+    empty cache, then grown by a larger shape on the same stream: the zero fill
+    is complete before the first call, and results match the oracle."""
+    g = np.random.Generator(np.random.PCG64(118))
+    vq._auto_ws.clear()
+    s = torch.cuda.Stream()
+    for M, K in ((520, 2048), (4100, 5120)):
+        q = Q4(W.q4_0_codes(M, K, g), W.fp16_scales_uniform(M, K, g))
+        a = W.f32_to_bf16_bits(g.standard_normal((16, K)))
+        x = to_dev(a, torch.bfloat16)
+        out = torch.empty((16, M), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        vq.gemm_q4_0(q.codes, q.scales, x, out, stream=s)
+        s.synchronize()
+        parity(out_to_f64(out), q.oracle(a), "bf16")
+    key = [k for k in vq._auto_ws if k[1] == s.cuda_stream]
+    assert key and not vq._auto_ws[key[0]].tensor[:65536].cpu().numpy().any()
+
+
 @pytest.mark.parametrize("act_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f16", "f32"])
 def test_dtype_combinations_parity(act_dtype, out_dtype):

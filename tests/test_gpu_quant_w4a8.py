@@ -34,6 +34,23 @@ def test_quantizer_bit_exact_prefill_rows(x_dtype):
     assert np.array_equal(q, qo)
 
 
+def test_quantizer_rounding_blocks_golden(golden_dir):
+    """The hand-worked blocks of tests/golden/quant_rounding_blocks.txt
+    (exact ties, division by the stored fp16 scale, the clamp at subnormal
+    scales) through both GPU quantizers: codes and scales as worked by hand."""
+    from test_oracle_pins import _rounding_blocks
+    for name, qmax, rotate, code, bits, dbits, qref in _rounding_blocks(golden_dir):
+        if not rotate:
+            continue
+        x = to_dev(bits.reshape(1, 32), torch.bfloat16 if code == oracle.BF16 else torch.float16)
+        q = torch.empty((1, 32), dtype=torch.int8, device="cuda")
+        d = torch.empty((1, 1), dtype=torch.float16, device="cuda")
+        (vq.hadamard32_quant_int8 if qmax == 127 else vq.hadamard32_quant_int4)(x, q, d)
+        torch.cuda.synchronize()
+        assert int(bits_u16(d)[0, 0]) == dbits, name
+        assert np.array_equal(q.cpu().numpy()[0].astype(np.int64), qref), name
+
+
 @pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (7, 4128)])
 def test_quantizer_bit_exact_ragged(N, K):
     g = np.random.Generator(np.random.PCG64(N * K))
