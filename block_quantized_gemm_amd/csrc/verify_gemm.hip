@@ -629,6 +629,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
     };
     int pend_pi[2] = {-1, -1}, pend_tg[2] = {0, 0};  // this workgroup's pieces, by side
+    // Side 0 (a tile group that ends in this range, begun in an earlier one)
+    // is counted in at the chunk boundary after its piece was stored, so the
+    // end of the range does not wait for that round trip: 0 nothing to count,
+    // 1 piece stored, 2 counted in (old0: the count before this arrival).
+    int s0_state = 0;
+    uint32_t old0 = 0u;
 
     f32x4 acc[T];
 #pragma unroll
@@ -666,6 +672,20 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         const KProblem &ca = grp.p[cref.pi];
         const uint8_t *abuf = row + par * kActBuf;
         const uint16_t *sc0 = reinterpret_cast<const uint16_t *>(sc_wave + par * kScBuf) + j * scrow;
+        // The range's last chunk begins a tile group that the next range
+        // finishes at its own start, so that range's count is normally in by
+        // now: read the counter while this chunk streams, and if the other
+        // part has arrived, load it and finish the tile group here, without
+        // storing this part, counting in and reading it back.
+        bool want1 = false, early1 = false;
+        uint32_t cnt1 = 0u;
+        f32x4 p1[T];
+        if (it + 1 >= ie) {
+            const int first = ca.item0 + cref.tg * ca.cpt;
+            want1 = first >= ib && first + ca.cpt > ie && range_owner(grp, first + ca.cpt - 1, G) == b + 1;
+            if (want1 && lane == 0)
+                cnt1 = __hip_atomic_load(grp.cnt + b * W + wave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
 #pragma unroll
         for (int rd = 0; rd < CH / PF; ++rd) {
             // this round's loads fetch the next round of this chunk, or the
@@ -679,6 +699,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                                                   tsb[U.value], acc);
                 __builtin_amdgcn_sched_barrier(0);
                 issue(U, src, st0 + U.value);
+                if (rd == 0 && U.value == PF / 2 - 1 && want1) {
+                    // the count, two steps after it was requested; the other
+                    // part is read only after its arrival was seen
+                    early1 = __builtin_amdgcn_readfirstlane(cnt1) == 1u;
+                    if (early1) {
+#pragma unroll
+                        for (int t = 0; t < T; ++t)
+                            p1[t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                  rp, slot_off(b + 1, 0, t), 0, kCoherent));
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
@@ -688,10 +719,28 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         // wave's scales for it have landed.
         wait_vmcnt<kIssueLoads>();
         const bool last = it + 1 >= ie;
+        if (s0_state == 1) {
+            // the side-0 piece, stored at an earlier boundary, is complete
+            // (older than the newest round): count in now
+            const KProblem &a0 = grp.p[pend_pi[0]];
+            const int b0 = range_owner(grp, a0.item0 + pend_tg[0] * a0.cpt, G);
+            if (lane == 0)
+                old0 = __hip_atomic_fetch_add(grp.cnt + b0 * W + wave, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s0_state = 2;
+        }
         if (cref.c == ca.cpt - 1 || last) {  // this workgroup's part of the tile group is done
             const int first = ca.item0 + cref.tg * ca.cpt;
             if (first >= ib && first + ca.cpt <= ie) {
                 store_tiles(ca, cref.tg, acc);
+            } else if (early1) {
+                // both parts in registers: added in range order (this part
+                // first), as the last arrival would; the counter is left at zero
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    p1[t] = acc[t] + p1[t];
+                store_tiles(ca, cref.tg, p1);
+                if (lane == 0)
+                    __hip_atomic_store(grp.cnt + b * W + wave, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             } else {
                 const int side = first + ca.cpt > ie ? 1 : 0;  // 1: the tile group goes on past this range
 #pragma unroll
@@ -700,6 +749,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                                                            slot_off(b, side, t), 0, kCoherent);
                 pend_pi[side] = cref.pi;
                 pend_tg[side] = cref.tg;
+                if (side == 0)
+                    s0_state = 1;
             }
 #pragma unroll
             for (int t = 0; t < T; ++t)
@@ -732,7 +783,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int first = a.item0 + pend_tg[side] * a.cpt;
         b0s[side] = range_owner(grp, first, G);
         b1s[side] = range_owner(grp, first + a.cpt - 1, G);
-        if (lane == 0)
+        if (side == 0 && s0_state == 2)
+            old[0] = old0;  // counted in during the walk
+        else if (lane == 0)
             old[side] = __hip_atomic_fetch_add(grp.cnt + b0s[side] * W + wave, 1u, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
     }
