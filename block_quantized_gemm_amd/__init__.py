@@ -26,6 +26,7 @@ VQ_ERR_DEVICE = -5
 VQ_ERR_LAUNCH = -6
 VQ_ERR_BAD_CONFIG = -7
 VQ_ERR_WORKSPACE = -8
+VQ_ERR_SCRATCH = -9
 
 KIND_Q4_0 = 0
 KIND_FP8_BLK128 = 1
@@ -50,6 +51,7 @@ _F = ctypes.c_float
 _SZ = ctypes.c_size_t
 SIGNATURES = {
     "vq_gemm_q4_0": (_I, [_P, _P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _F, _P, _SZ, _P]),
+    "vq_gemm_q4_0_noalloc": (_I, [_P, _P, _P, _I, _P, _P, _I, _I64, _I64, _I64, _F, _P]),
     "vq_gemm_fp8_blk128": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
     "vq_hadamard32_quant_int8": (_I, [_P, _I, _P, _P, _I64, _I64, _P]),
     "vq_hadamard32_quant_int4": (_I, [_P, _I, _P, _P, _I64, _I64, _P]),
@@ -265,6 +267,30 @@ def gemm_q4_0(codes, scales, x, out, *, x_scales=None, alpha: float = 1.0, works
                             act_dtype, None, _dev_ptr(out, "out"), _dtype_code(out), N, M, K,
                             float(alpha), wp, wn, sh)
         _check(st, "vq_gemm_q4_0")
+    return out
+
+
+def gemm_q4_0_noalloc(codes, scales, x, out, *, x_scales=None, alpha: float = 1.0, stream=None):
+    """gemm_q4_0 through the allocation-free entry point: no workspace, the
+    library's fixed per-GPU scratch array instead (calls on one GPU must not
+    overlap in time).  Same arguments and results as gemm_q4_0."""
+    N, K = x.shape
+    M = codes.shape[0]
+    _check_2d(codes, "codes", (M, K // 2))
+    _check_2d(scales, "scales", (M, K // 32))
+    _check_2d(out, "out", (N, M))
+    xs = None
+    if _dtype_code(x) == DTYPE_I8:
+        if x_scales is None:
+            raise ValueError("int8 activations need x_scales")
+        _check_2d(x_scales, "x_scales", (N, K // 32))
+        xs = _dev_ptr(x_scales, "x_scales")
+    elif x_scales is not None:
+        raise ValueError("x_scales only go with int8 activations")
+    st = lib().vq_gemm_q4_0_noalloc(_dev_ptr(codes, "codes"), _dev_ptr(scales, "scales"), _dev_ptr(x, "x"),
+                                    _dtype_code(x), xs, _dev_ptr(out, "out"), _dtype_code(out), N, M, K,
+                                    float(alpha), _stream(stream))
+    _check(st, "vq_gemm_q4_0_noalloc")
     return out
 
 

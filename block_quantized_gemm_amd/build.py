@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libvq.so")
 
 SOURCES = ["verify_gemm.hip", "w4a8_gemm.hip", "fp8_prefill.hip", "h32_quant.hip", "greedy_verify.hip",
-           "hbm_probe.hip", "vq_api.cpp"]
+           "hbm_probe.hip", "verify_noalloc.hip", "vq_api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

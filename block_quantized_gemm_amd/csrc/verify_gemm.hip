@@ -966,6 +966,10 @@ hipError_t launch_tw(const VerifyLaunch &l) {
         grp.share = (int)(items / grid);
         grp.extra = (int)(items % grid);  // below grid <= 1024: b * extra stays in 32 bits
     }
+    if (l.used) {
+        *l.used = walk ? kWalkCounterBytes + (size_t)grid * 2 * TG * 1024 : 0;
+        return hipSuccess;
+    }
     for (int i = 0; i < l.count; ++i)
         grp.item0[i] = grp.p[i].item0;
     // Row groups of 16 run one after another: they share the workspace and

@@ -289,6 +289,44 @@ int vq_gemm_q4_0(const void *w_codes, const void *w_scales, const void *act, int
     return vq::launch_w4a8(p) == hipSuccess ? VQ_OK : VQ_ERR_LAUNCH;
 }
 
+int vq_gemm_q4_0_noalloc(const void *w_codes, const void *w_scales, const void *act, int act_dtype,
+                         const void *act_scales, void *out, int out_dtype, int64_t n_rows, int64_t m, int64_t k,
+                         float alpha, void *stream) {
+    if (act_dtype == VQ_DTYPE_I8)  // the W4A8 kernel uses no scratch memory
+        return vq_gemm_q4_0(w_codes, w_scales, act, act_dtype, act_scales, out, out_dtype, n_rows, m, k, alpha,
+                            nullptr, 0, stream);
+    if (act_scales != nullptr)
+        return VQ_ERR_BAD_DTYPE;
+    const int st = check_problem(false, w_codes, w_scales, act, out, m, k);
+    if (st != VQ_OK)
+        return st;
+    if (!float_act(act_dtype) || !out_ok(out_dtype))
+        return VQ_ERR_BAD_DTYPE;
+    if (!dim_ok(n_rows))
+        return VQ_ERR_BAD_SHAPE;
+    // the launch vq_gemm_q4_0 makes with an ample workspace, so the results
+    // are the same bits
+    const vq::VerifyPlan pl = default_plan(false, m, k, SIZE_MAX);
+    const int dev = check_device();
+    if (dev != VQ_OK)
+        return dev;
+    const vq::VerifyProblem prob{w_codes, w_scales, act, out, (int)m, (int)k, pl};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    void *scratch = nullptr;
+    if (pl.walk) {
+        size_t used = 0;
+        vq::VerifyLaunch l{false, act_dtype, out_dtype, (int)n_rows, alpha, pl.tiles, pl.waves, &prob, 1,
+                           nullptr, s, &used};
+        if (vq::launch_verify(l) != hipSuccess)
+            return VQ_ERR_LAUNCH;
+        if (used > vq::kNoallocScratchBytes)
+            return VQ_ERR_SCRATCH;
+        if (vq::noalloc_scratch(s, &scratch) != hipSuccess)
+            return VQ_ERR_LAUNCH;
+    }
+    return launch_problems(false, &prob, 1, act_dtype, out_dtype, (int)n_rows, alpha, scratch, s, nullptr);
+}
+
 int vq_gemm_q4_0_ex(const void *w_codes, const void *w_scales, const void *act, int act_dtype,
                     void *out, int out_dtype, int64_t n_rows, int64_t m, int64_t k, float alpha,
                     int tiles_per_wave, int waves_per_group, int max_groups, void *workspace,
@@ -561,6 +599,7 @@ const char *vq_status_string(int status) {
     case VQ_ERR_LAUNCH: return "HIP kernel launch failed";
     case VQ_ERR_BAD_CONFIG: return "unsupported explicit launch shape";
     case VQ_ERR_WORKSPACE: return "workspace too small for the explicit launch shape";
+    case VQ_ERR_SCRATCH: return "the launch needs more scratch memory than the fixed array holds";
     default: return "unknown status";
     }
 }

@@ -42,6 +42,10 @@ constexpr int kPanelRecordBytes = kPanelCodeBytes + kPanelTiles * kPanelTileScal
 // piece slots of TG tiles per workgroup.  At most kMaxWalkGroups workgroups.
 constexpr int kMaxWalkGroups = 1024;
 constexpr size_t kWalkCounterBytes = 64 * 1024;
+// The allocation-free entry point's fixed scratch: the counters and 8 MiB of
+// pieces (the default row-major shape cuts 16 KiB per workgroup: 512
+// workgroups, twice the MI355X's resident count).
+constexpr size_t kNoallocScratchBytes = kWalkCounterBytes + ((size_t)8 << 20);
 
 // One verify GEMM of a launch, already validated.
 struct VerifyProblem {
@@ -66,6 +70,10 @@ struct VerifyLaunch {
     int count;        // 1 .. kGroupPerLaunch
     void *workspace;  // walk launches: counters and pieces
     hipStream_t stream;
+    // When set, nothing is launched: the bytes of workspace the launch would
+    // use (counters and the pieces of the workgroups it would run) are
+    // written here instead.
+    size_t *used = nullptr;
 };
 
 // Largest dynamic LDS a workgroup may use on gfx950 (160 KiB per CU).
@@ -122,6 +130,10 @@ hipError_t launch_q4_rotate_h32(const void *codes, const void *scales, int M, in
                                 void *scales_out, hipStream_t stream);
 
 // The HBM read probe (one kernel; arguments checked by the caller).
+// The fixed scratch of the current device (set up on first use: its address
+// looked up, its counters cleared by a kernel on `stream`).
+hipError_t noalloc_scratch(hipStream_t stream, void **ptr);
+
 hipError_t launch_hbm_probe(const void *buf, size_t bytes, int mode, int groups, int waves, int depth,
                             bool nontemporal, uint32_t *sink, hipStream_t stream);
 

@@ -59,6 +59,7 @@ extern "C" {
 #define VQ_ERR_LAUNCH (-6)         /* the HIP launch itself reported an error */
 #define VQ_ERR_BAD_CONFIG (-7)     /* explicit launch shape not supported */
 #define VQ_ERR_WORKSPACE (-8)      /* explicit launch shape needs a larger workspace */
+#define VQ_ERR_SCRATCH (-9)        /* the launch needs more than the fixed scratch array */
 
 /* Element type codes. */
 #define VQ_DTYPE_F16 1             /* IEEE binary16 */
@@ -134,6 +135,28 @@ int vq_gemm_q4_0(const void *w_codes, const void *w_scales,
                  int64_t n_rows, int64_t m, int64_t k,
                  float alpha, void *workspace, size_t workspace_bytes,
                  void *stream);
+
+/*
+ * vq_gemm_q4_0_noalloc -- vq_gemm_q4_0 for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, layouts, sizes and results as
+ * vq_gemm_q4_0 with an ample workspace (the same launch, so the same bits),
+ * but no workspace argument: the walk form's arrival counters and partial
+ * sums live in a fixed device array inside the library, 64 KiB + 8 MiB per
+ * GPU, held until the process ends and set up on the first call on each
+ * device (its counters cleared by a kernel on `stream`).  The call allocates
+ * and frees nothing.  Every call on one GPU shares that GPU's array, and
+ * every call leaves its counters at zero: calls that overlap in time on one
+ * GPU (on unordered streams or from several host threads) race and must not
+ * be made.  VQ_ERR_SCRATCH if the launch would need more than the array
+ * holds (more than 512 resident workgroups of the default shape; none on an
+ * MI355X).  act_dtype I8 takes the W4A8 kernel, which needs no scratch.
+ */
+int vq_gemm_q4_0_noalloc(const void *w_codes, const void *w_scales,
+                         const void *act, int act_dtype, const void *act_scales,
+                         void *out, int out_dtype,
+                         int64_t n_rows, int64_t m, int64_t k,
+                         float alpha, void *stream);
 
 /*
  * vq_gemm_fp8_blk128 -- out[n][m] = sum_k x[n][k] * w[m][k], FP8 weights with

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert vq.lib().vq_version() == 310
-    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert vq.status_string(st) and vq.status_string(st) != "unknown status"
     assert vq.status_string(-99) == "unknown status"
 
@@ -316,3 +316,21 @@ def test_hbm_probe_argument_errors():
     # valid arguments get as far as the device check (no GPU here)
     if not torch.cuda.is_available():
         assert probe(mode=vq.PROBE_SHARES, groups=16) == vq.VQ_ERR_DEVICE
+
+
+def test_noalloc_argument_errors():
+    L = vq.lib()
+
+    def na(w=A, s=B, x=C, xd=vq.DTYPE_BF16, xs=None, o=D, od=vq.DTYPE_BF16, n=16, m=256, k=512):
+        return L.vq_gemm_q4_0_noalloc(w, s, x, xd, xs, o, od, n, m, k, 1.0, None)
+    assert na(w=None) == vq.VQ_ERR_NULL_POINTER
+    assert na(o=None) == vq.VQ_ERR_NULL_POINTER
+    assert na(xd=vq.DTYPE_F32) == vq.VQ_ERR_BAD_DTYPE
+    assert na(xs=E) == vq.VQ_ERR_BAD_DTYPE
+    assert na(od=vq.DTYPE_I8) == vq.VQ_ERR_BAD_DTYPE
+    assert na(k=500) == vq.VQ_ERR_BAD_SHAPE
+    assert na(n=0) == vq.VQ_ERR_BAD_SHAPE
+    assert na(x=C + 8) == vq.VQ_ERR_MISALIGNED
+    assert na(xd=vq.DTYPE_I8, xs=None) == vq.VQ_ERR_NULL_POINTER
+    if not torch.cuda.is_available():
+        assert na() == vq.VQ_ERR_DEVICE
