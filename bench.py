@@ -62,7 +62,7 @@ KERNEL_SOURCES = ("block_quantized_gemm_amd/csrc/verify_gemm.hip", "block_quanti
                   "block_quantized_gemm_amd/csrc/vq_internal.h", "block_quantized_gemm_amd/csrc/vq_api.cpp")
 COPY_BYTES = 512 << 20  # calibration copy for the traffic counters
 COPIES_BYTES = 2100 << 20  # weight copies per single-matrix measurement (> 8x the Infinity Cache)
-PARTS = ("stream", "tiny", "ffn", "fp8", "prefill", "greedy", "probe")
+PARTS = ("stream", "tiny", "ffn", "fp8", "fp8stream", "prefill", "greedy", "probe")
 
 
 def kernel_source_hash() -> str:
@@ -621,6 +621,59 @@ def prefill_part(args, dev, stream):
     return res
 
 
+def fp8_stream_part(args, dev, stream):
+    """The per-token stream's shapes in FP8 E4M3 with 128 x 128 fp32 tile
+    scales (E4M3 of N(0,1), scales U[1e-3, 1e-2], drawn on the device): 64
+    layers x 5 matrices, 16 bf16 rows per layer, each layer's five GEMMs one
+    grouped call, the step's launches replayed as one HIP graph; also at 1 row
+    and as whole-stack grouped calls."""
+    import torch
+    import block_quantized_gemm_amd as vq
+    import workloads as W
+    layers = args.layers
+    mats = []
+    for layer in range(layers):
+        for idx, (m, k) in enumerate(SHAPES):
+            g = torch.Generator(device=dev)
+            g.manual_seed(W.seed_of(W.CFG_FP8, layer, 10 * idx))
+            w = torch.randn((m, k), generator=g, device=dev).to(torch.float8_e4m3fn).view(torch.uint8)
+            ts = torch.empty(((m + 127) // 128, k // 128), dtype=torch.float32, device=dev).uniform_(1e-3, 1e-2,
+                                                                                                      generator=g)
+            mats.append((layer, m, k, w, ts))
+    acts = {(l, k): W.act_device(16, k, W.seed_of(W.CFG_FP8, l, 1000 + k), dev)
+            for l in range(layers) for k in sorted({k for _, k in SHAPES})}
+    outs = {m: torch.empty((16, m), dtype=torch.bfloat16, device=dev) for m in {m for m, _ in SHAPES}}
+    torch.cuda.synchronize()
+    wbytes = sum(m * k + 4 * ((m + 127) // 128) * (k // 128) for _, m, k, _, _ in mats)
+    res = {"workload": "FP8 E4M3 per-token stream: %d layers x (8192x5120, 5120x8192, 17408x5120 x2, 5120x17408), "
+                       "128 x 128 fp32 tile scales, 16-row bf16 block per layer; each layer's 5 GEMMs one grouped "
+                       "call, the step's launches one HIP graph" % layers, "weight_bytes": wbytes}
+    ws = None
+    times = {}
+    for n in (16, 1):
+        def problems(sel):
+            return [(w, ts, acts[(l, k)][:n], outs[m][:n]) for l, m, k, w, ts in mats if sel(l)]
+        calls = [vq.GroupedCall("fp8", problems(lambda l, L=L: l == L), workspace="auto") for L in range(layers)]
+        ws = max((c.ws for c in calls if c.ws is not None), key=lambda w: w.nbytes, default=None)
+        for c in calls:
+            c.ws = ws
+        t = timed(lambda st: [c(st) for c in calls], stream, max(8, args.steps // 2), args.warmup)
+        alg = wbytes + sum(n * k * 2 + n * m * 2 for _, m, k, _, _ in mats)
+        times[n] = t
+        res["gbs_%d_rows" % n] = rate(t, alg, 1e9)
+        if n == 16:
+            whole = [vq.GroupedCall("fp8", problems(lambda l, L=L: L <= l < L + 6), workspace=ws)
+                     for L in range(0, layers, 6)]
+            tw = timed(lambda st: [c(st) for c in whole], stream, max(8, args.steps // 2), args.warmup)
+            res["gbs_16_rows_whole_stack"] = rate(tw, alg, 1e9)
+            res["roofline"] = {"bound": "hbm", "achieved": res["gbs_16_rows"]["median"], "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(res["gbs_16_rows"]["median"] / HBM_PEAK_GBS, 4)}
+    res["t16_over_t1"] = round(times[16]["median_ms"] / times[1]["median_ms"], 4)
+    del mats, acts, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 GREEDY_VOCAB = 151936  # a synthetic vocabulary of 151,936 entries
 
 
@@ -749,8 +802,8 @@ def main():
     vq.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream()
-    parts = {"tiny": tiny_part, "ffn": ffn_part, "fp8": fp8_part, "prefill": prefill_part,
-             "greedy": greedy_part, "probe": probe_part}
+    parts = {"tiny": tiny_part, "ffn": ffn_part, "fp8": fp8_part, "fp8stream": fp8_stream_part,
+             "prefill": prefill_part, "greedy": greedy_part, "probe": probe_part}
     if args.only and args.only != "stream":
         print(json.dumps({args.only: parts[args.only](args, dev, stream)}))
         return
@@ -763,7 +816,7 @@ def main():
         return
     print("stream timed: %.1f GB/s" % head["gbs_by_rows"]["16"], file=sys.stderr, flush=True)
     configs = {}
-    for name in ("tiny", "ffn", "fp8", "prefill", "greedy", "probe"):
+    for name in ("tiny", "ffn", "fp8", "fp8stream", "prefill", "greedy", "probe"):
         configs[name] = parts[name](args, dev, stream)
         print("%s timed" % name, file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
