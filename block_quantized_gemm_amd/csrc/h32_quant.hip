@@ -13,8 +13,8 @@
 // with single IEEE fp32 adds, in the fixed order h = 1, 2, 4, 8, 16.  Then
 // amax over the block, d = fp16_rne(amax / QMAX) with a correctly rounded
 // division, q = clamp(rint(u / d), -QMAX, QMAX): QMAX = 127 for int8 codes,
-// 7 for the 4-bit codes of the same section (only the activations are
-// rounded to 4 bits; stored one per byte, so the same GEMM reads them).  Every operation is one IEEE
+// 7 for the 4-bit activation codes of the same section (stored one per byte,
+// so the same GEMM reads them).  Every operation is one IEEE
 // rounding (no FMA contraction is possible: there are no multiplies), so the
 // codes and scales are reproducible bit for bit on any IEEE implementation.
 #include "vq_device.h"

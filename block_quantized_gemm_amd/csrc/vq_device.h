@@ -28,7 +28,15 @@ constexpr int kWave = 64;
 // MAGIC + q by placing the nibble in the low mantissa bits under a fixed
 // exponent byte: bf16 0x43nn = 128 + q, fp16 0x64nn = 1024 + q.  The offset
 // (MAGIC + 8) is removed through the MFMA accumulator input (see the verify
-// kernel), so every product and the per-block dot are exact.
+// kernel).  Every product x * (MAGIC + q) is exact in fp32, but the block
+// MFMA adds 32 terms of size about (MAGIC + 8) |x| onto -(MAGIC + 8) * sum x,
+// and these mostly cancel: the fp32 rounding of that sum is up to about
+// (MAGIC + 8) / 8 times that of a direct sum of (q - 8) x, i.e. about 17x for
+// bf16 activations (136 / 8) and about 130x for fp16 (1032 / 8).  The block
+// dot is exact where the partial sums are (integer-valued activations of
+// modest size); otherwise it carries that amplified fp32 rounding, which the
+// parity tolerance covers (fp16 heavy-tailed rows with outlier channels are
+// among the parity cases).
 // ---------------------------------------------------------------------------
 template <int ACT>
 struct Act16;

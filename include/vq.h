@@ -95,11 +95,17 @@ extern "C" {
  *    one-shot form (one workgroup per feature-tile group over all of K), which
  *    is correct but slower.  Q4_0 shapes with K not a multiple of 256 always
  *    run one-shot.
- *  - Where a tile group is cut depends on the launch (its problems and the
- *    number of workgroups the device holds), never on N: for a fixed call
- *    every output bit is the same for any number of rows and from run to run.
- *    The same problem in another call (alone, or grouped with others) may
- *    round differently in the last bits.
+ *  - Output bits are a function of the call, not only of the problem.  Where
+ *    a tile group is cut depends on the launch: the problems it holds (their
+ *    order and shapes) and its workgroup count, which by default is what the
+ *    device holds at once and so follows its CU count (256 on an MI355X).
+ *    It never depends on N or on the activation values: for a fixed call on a
+ *    fixed device every output bit is the same for any number of rows, any
+ *    neighbouring rows and from run to run.  The same problem in another call
+ *    (alone, or grouped with others), or on a device with another CU count,
+ *    may round differently in the last bits (all within the parity bound);
+ *    the _ex calls' workgroup cap, set at or below what every device in use
+ *    holds at once, fixes the count across devices.
  */
 
 /*
@@ -214,8 +220,8 @@ int vq_hadamard32_quant_int8(const void *x, int x_dtype,
 
 /*
  * vq_hadamard32_quant_int4 -- the 4-bit activation quantizer of the same
- * section [P4] ("only the activations are rounded to 4 bits", after the same
- * H32 rotation): identical to vq_hadamard32_quant_int8 with 7 in place of
+ * section [P4] (there the activations alone go to 4-bit codes, after the
+ * same H32 rotation; the weights keep their Q4_0 form): identical to vq_hadamard32_quant_int8 with 7 in place of
  * 127 (the library's reading: the symmetric 4-bit range),
  *   d   = fp16_rne(fp32(max_j |u_j|) / 7)          -> scales_out [N][K/32] f16
  *   q_j = clamp(rint_half_even(u_j / d), -7, 7)     -> q_out [N][K] int8
@@ -230,8 +236,9 @@ int vq_hadamard32_quant_int4(const void *x, int x_dtype,
 
 /*
  * vq_q4_0_rotate_h32 -- the offline weight rotation of the W4A8 path [P4]
- * ("we rotate the weights the same way once, offline, so the product is
- * unchanged"; the pages' tool turns a plain Q4_0 file into the rotated one).
+ * (the weights get the same H32 rotation once, ahead of time, which leaves
+ * the product of rotated weights and rotated activations as it was; the
+ * pages' tool turns a plain Q4_0 file into the rotated one).
  * For every row and 32-block of the Q4_0 matrix (w_codes, w_scales), in the
  * layout of vq_gemm_q4_0:
  *   x = d * (q - 8) exactly in fp32, then u = H32 x by the butterflies of

@@ -40,9 +40,9 @@
  *    q = clamp(rint_half_even(u / d), -127, 127), amax == 0 gives d = 0, q = 0.
  *    The 4-bit quantizer of the same section is the same rule with 7 in place
  *    of 127 (symmetric 4-bit codes, stored one per byte).
- *  - H32 rotation of Q4_0 weights ([P4]: "we rotate the weights the same way
- *    once, offline"; the pages' tool makes a rotated Q4_0 file from a plain
- *    one): per 32-block, dequantize exactly in fp32, H32 by the butterflies
+ *  - H32 rotation of Q4_0 weights ([P4]: the weights take the same rotation
+ *    once, ahead of time; the pages' tool makes a rotated Q4_0 file from a
+ *    plain one): per 32-block, dequantize exactly in fp32, H32 by the butterflies
  *    above, requantize to Q4_0 by the rule of the GGUF Q4_0 format the pages'
  *    files use: m = the block's value of largest magnitude (the first one on
  *    ties), d = m / -8, id = d != 0 ? 1 / d : 0, q = min(15, trunc(x * id +
@@ -335,8 +335,8 @@ void vqo_h32_matrix(int8_t *h)
 /* Per (row, 32-block): u = H32 x in fp32 (or u = x when rotate == 0),
  * amax = max |u|, d = fp16_rne(amax / qmax), q = clamp(rint(u / d), -qmax,
  * qmax).  qmax = 127 is the int8 quantizer, qmax = 7 the 4-bit one ([P4]
- * "Prompt processing": only the activations are rounded to 4 bits; read here
- * as the int8 rule with the symmetric 4-bit range, codes one per byte).
+ * "Prompt processing": there the activations alone become 4-bit codes; read
+ * here as the int8 rule with the symmetric 4-bit range, codes one per byte).
  * Returns 0, or -1 if some d overflows fp16 (then outputs are partial). */
 int vqo_block_quant(const uint16_t *x, int x_dtype, int64_t N, int64_t K, int qmax, int rotate,
                     int8_t *q, uint16_t *d)
