@@ -629,6 +629,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
     };
     int pend_pi[2] = {-1, -1}, pend_tg[2] = {0, 0};  // this workgroup's pieces, by side
+    // the first and last chunk of each piece's tile group (kept from when the
+    // piece was stored, so that counting in needs no load of the problem)
+    int pend_first[2] = {0, 0}, pend_end[2] = {0, 0};
     // Side 0 (a tile group that ends in this range, begun in an earlier one)
     // is counted in at the chunk boundary after its piece was stored, so the
     // end of the range does not wait for that round trip: 0 nothing to count,
@@ -661,6 +664,18 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 
     int par = 0;
     const uint8_t *row = lds + j * kActPitch;
+    // The range's last chunk may begin a tile group that the next range
+    // finishes at its own start; that range's count is normally in before
+    // this one ends.  The counter is read during the second-to-last chunk
+    // and looked at after that chunk's boundary wait (which already covers
+    // it); if the other part has arrived it is loaded then, lands during the
+    // last chunk, and the tile group is finished here, without storing this
+    // part, counting in and reading it back.  (Reading the counter within
+    // the chunk that uses it made the compiler wait for every older load at
+    // that point in every chunk: the register it lands in was reused.)
+    bool want1 = false, early1 = false;
+    uint32_t cnt1 = 0u;
+    f32x4 p1[T];
     for (;;) {
         // The next chunk's activations and scales go into the other buffers
         // (free: every wave passed the barrier after the chunk that used
@@ -672,17 +687,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         const KProblem &ca = grp.p[cref.pi];
         const uint8_t *abuf = row + par * kActBuf;
         const uint16_t *sc0 = reinterpret_cast<const uint16_t *>(sc_wave + par * kScBuf) + j * scrow;
-        // The range's last chunk begins a tile group that the next range
-        // finishes at its own start, so that range's count is normally in by
-        // now: read the counter while this chunk streams, and if the other
-        // part has arrived, load it and finish the tile group here, without
-        // storing this part, counting in and reading it back.
-        bool want1 = false, early1 = false;
-        uint32_t cnt1 = 0u;
-        f32x4 p1[T];
-        if (it + 1 >= ie) {
-            const int first = ca.item0 + cref.tg * ca.cpt;
-            want1 = first >= ib && first + ca.cpt > ie && range_owner(grp, first + ca.cpt - 1, G) == b + 1;
+        if (it + 2 == ie) {  // the last chunk is nref
+            const KProblem &na = grp.p[nref.pi];
+            const int first = na.item0 + nref.tg * na.cpt;
+            want1 = first >= ib && first + na.cpt > ie && range_owner(grp, first + na.cpt - 1, G) == b + 1;
             if (want1 && lane == 0)
                 cnt1 = __hip_atomic_load(grp.cnt + b * W + wave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -699,17 +707,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                                                   tsb[U.value], acc);
                 __builtin_amdgcn_sched_barrier(0);
                 issue(U, src, st0 + U.value);
-                if (rd == 0 && U.value == PF / 2 - 1 && want1) {
-                    // the count, two steps after it was requested; the other
-                    // part is read only after its arrival was seen
-                    early1 = __builtin_amdgcn_readfirstlane(cnt1) == 1u;
-                    if (early1) {
-#pragma unroll
-                        for (int t = 0; t < T; ++t)
-                            p1[t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                  rp, slot_off(b + 1, 0, t), 0, kCoherent));
-                    }
-                }
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
@@ -722,8 +719,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         if (s0_state == 1) {
             // the side-0 piece, stored at an earlier boundary, is complete
             // (older than the newest round): count in now
-            const KProblem &a0 = grp.p[pend_pi[0]];
-            const int b0 = range_owner(grp, a0.item0 + pend_tg[0] * a0.cpt, G);
+            const int b0 = range_owner(grp, pend_first[0], G);
             if (lane == 0)
                 old0 = __hip_atomic_fetch_add(grp.cnt + b0 * W + wave, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             s0_state = 2;
@@ -749,6 +745,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                                                            slot_off(b, side, t), 0, kCoherent);
                 pend_pi[side] = cref.pi;
                 pend_tg[side] = cref.tg;
+                pend_first[side] = first;
+                pend_end[side] = first + ca.cpt - 1;
                 if (side == 0)
                     s0_state = 1;
             }
@@ -758,6 +756,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
         if (last)
             break;
+        if (want1 && it + 2 == ie) {
+            // the count (complete after the boundary wait); the other part is
+            // read only after its arrival was seen
+            early1 = __builtin_amdgcn_readfirstlane(cnt1) == 1u;
+            if (early1) {
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    p1[t] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, slot_off(b + 1, 0, t), 0, kCoherent));
+            }
+        }
         lds_barrier();  // every wave is done with buffer `par`, and sees the next chunk's activations
         ++it;
         cref = nref;
@@ -779,10 +788,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int side = 0; side < 2; ++side) {
         if (pend_pi[side] < 0)
             continue;
-        const KProblem &a = grp.p[pend_pi[side]];
-        const int first = a.item0 + pend_tg[side] * a.cpt;
-        b0s[side] = range_owner(grp, first, G);
-        b1s[side] = range_owner(grp, first + a.cpt - 1, G);
+        b0s[side] = range_owner(grp, pend_first[side], G);
+        b1s[side] = range_owner(grp, pend_end[side], G);
         if (side == 0 && s0_state == 2)
             old[0] = old0;  // counted in during the walk
         else if (lane == 0)
