@@ -714,7 +714,9 @@ def greedy_part(args, dev, stream):
 def probe_part(args, dev, stream):
     """The library's HBM read probe over 2 GiB: one workgroup per 64 KiB, and
     one persistent workgroup per CU in contiguous shares and as a sweeping
-    window, with the default and the non-temporal cache policy."""
+    window, with the default and the non-temporal cache policy; then the
+    rate of L2 hits (each workgroup re-reading its 64 KiB), kept out of
+    best_gbs."""
     import torch
     import block_quantized_gemm_amd as vq
     nbytes = 1 << 31
@@ -728,9 +730,16 @@ def probe_part(args, dev, stream):
                                                  ("shares_%d_w8_d8_nt" % cus, "shares", cus, 8, 8, True),
                                                  ("window_%d_w8_d8_nt" % cus, "window", cus, 8, 8, True)):
         t = timed(lambda s: vq.hbm_read_probe(buf, sink, mode=mode, groups=groups, waves_per_group=waves,
-                                              depth=depth, nontemporal=nt, stream=s), stream, args.reps, args.warmup)
+                                              depth=depth, nontemporal=nt, stream=s), stream, args.reps, args.warmup,
+                  inner=4)
         res[name] = rate(t, nbytes, 1e9)
     res["best_gbs"] = max(v["median"] for k, v in res.items() if isinstance(v, dict))
+    # the rate of L2 hits: 64 KiB per workgroup (2 MiB per XCD), read 16 times over in one launch
+    small = buf[: cus * (64 << 10)]
+    t = timed(lambda s: vq.hbm_read_probe(small, sink, mode="reread", groups=cus, waves_per_group=8, depth=8,
+                                          stream=s), stream, args.reps, args.warmup, inner=32)
+    res["reread_l2_%d_w8_d8" % cus] = rate(t, small.numel() * vq.PROBE_REREAD_PASSES, 1e9)
+    res["reread_l2_gbs_per_cu"] = round(res["reread_l2_%d_w8_d8" % cus]["median"] / cus, 1)
     del buf
     return res
 

@@ -36,7 +36,9 @@ _KINDS = {"q4_0": KIND_Q4_0, "fp8": KIND_FP8_BLK128, "q4_0_panel": KIND_Q4_0_PAN
 PROBE_BLOCKS = 0
 PROBE_SHARES = 1
 PROBE_WINDOW = 2
-_PROBES = {"blocks": PROBE_BLOCKS, "shares": PROBE_SHARES, "window": PROBE_WINDOW}
+PROBE_REREAD = 3
+PROBE_REREAD_PASSES = 16
+_PROBES = {"blocks": PROBE_BLOCKS, "shares": PROBE_SHARES, "window": PROBE_WINDOW, "reread": PROBE_REREAD}
 
 DTYPE_F16 = 1
 DTYPE_BF16 = 2
@@ -584,9 +586,10 @@ def hbm_read_probe(buf, sink, *, mode: str = "blocks", groups: int = 0, waves_pe
     """One plain read of the device tensor `buf` (its bytes, a multiple of
     64 KiB up to 2 GiB) by the probe kernel; sink: a device tensor of >= 4
     bytes.  mode "blocks" (one workgroup per 64 KiB; groups 0), "shares"
-    (`groups` persistent workgroups, contiguous shares) or "window" (`groups`
-    persistent workgroups sweeping 64 KiB blocks); nontemporal: the loads'
-    cache policy."""
+    (`groups` persistent workgroups, contiguous shares), "window" (`groups`
+    persistent workgroups sweeping 64 KiB blocks) or "reread" (as "shares",
+    each share read PROBE_REREAD_PASSES times within the launch: the rate of
+    L2 hits once a share fits in L2); nontemporal: the loads' cache policy."""
     if mode not in _PROBES:
         raise ValueError("mode must be one of %s" % sorted(_PROBES))
     if sink.numel() * sink.element_size() < 4:

@@ -15,7 +15,9 @@
 //              `groups` equal contiguous shares front to back, its waves
 //              interleaved 1 KiB apart (the walk kernel's pattern);
 //   window  -- `groups` persistent workgroups reading 64 KiB blocks b, b + G,
-//              b + 2G, ... (the whole grid sweeps one contiguous window).
+//              b + 2G, ... (the whole grid sweeps one contiguous window);
+//   reread  -- as shares, each share read VQ_PROBE_REREAD_PASSES times over
+//              in the launch (after the first pass, from L2 if it fits).
 // Each wave keeps `depth` loads in flight.  The loads use the default cache
 // policy or the non-temporal one (a stream read once: on gfx950 the latter
 // reaches a higher read rate).
@@ -38,26 +40,36 @@ struct ProbeArgs {
     uint32_t *sink;
 };
 
-template <int W, int D, int AUX>
+// RR: the reread pattern, in an instantiation of its own (its offsets wrap
+// with a mask, and no other pattern's branches sit in its loop: it measures
+// L2 hits, where the cost of issuing a load shows).
+template <int W, int D, int AUX, bool RR>
 __global__ __launch_bounds__(64 * W) void hbm_probe_kernel(const ProbeArgs a) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int b = (int)blockIdx.x, G = (int)gridDim.x;
     const rsrc_t r = make_rsrc(a.buf, a.bytes);
+    const int per = (int)(a.share / kPiece) / W;  // shares: pieces of one share (one pass) per wave
     // byte offset of this wave's j-th piece
     auto piece = [&](int j) -> uint32_t {
-        if (a.mode == VQ_PROBE_BLOCKS)
-            return (uint32_t)b * kBlock + (uint32_t)(wave + W * j) * kPiece;
-        if (a.mode == VQ_PROBE_SHARES)
-            return (uint32_t)b * a.share + (uint32_t)(wave + W * j) * kPiece;
-        constexpr int per = kBlock / kPiece / W;  // pieces of one block per wave
-        const int blk = j / per, in = j - blk * per;
-        return ((uint32_t)blk * (uint32_t)G + (uint32_t)b) * kBlock + (uint32_t)(wave + W * in) * kPiece;
+        if constexpr (RR) {
+            return (uint32_t)b * a.share + (uint32_t)(wave + W * (j & (per - 1))) * kPiece;
+        } else {
+            if (a.mode == VQ_PROBE_BLOCKS)
+                return (uint32_t)b * kBlock + (uint32_t)(wave + W * j) * kPiece;
+            if (a.mode == VQ_PROBE_SHARES)
+                return (uint32_t)b * a.share + (uint32_t)(wave + W * j) * kPiece;
+            constexpr int pb = kBlock / kPiece / W;  // pieces of one block per wave
+            const int blk = j / pb, in = j - blk * pb;
+            return ((uint32_t)blk * (uint32_t)G + (uint32_t)b) * kBlock + (uint32_t)(wave + W * in) * kPiece;
+        }
     };
     int n;  // pieces of this wave
-    if (a.mode == VQ_PROBE_BLOCKS)
+    if (RR)
+        n = per * VQ_PROBE_REREAD_PASSES;
+    else if (a.mode == VQ_PROBE_BLOCKS)
         n = kBlock / kPiece / W;
     else if (a.mode == VQ_PROBE_SHARES)
-        n = (int)(a.share / kPiece) / W;
+        n = per;
     else
         n = (int)((a.bytes / kBlock + G - 1 - b) / G) * (kBlock / kPiece / W);
     u32x4 acc = {0u, 0u, 0u, 0u};
@@ -70,15 +82,21 @@ __global__ __launch_bounds__(64 * W) void hbm_probe_kernel(const ProbeArgs a) {
         a.sink[0] = x;
 }
 
-template <int W, int AUX>
-hipError_t launch_w(const ProbeArgs &a, int grid, int depth, hipStream_t s) {
+template <int W, int AUX, bool RR>
+hipError_t launch_rr(const ProbeArgs &a, int grid, int depth, hipStream_t s) {
     switch (depth) {
-    case 4: hipLaunchKernelGGL((hbm_probe_kernel<W, 4, AUX>), dim3(grid), dim3(64 * W), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((hbm_probe_kernel<W, 8, AUX>), dim3(grid), dim3(64 * W), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((hbm_probe_kernel<W, 16, AUX>), dim3(grid), dim3(64 * W), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((hbm_probe_kernel<W, 4, AUX, RR>), dim3(grid), dim3(64 * W), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((hbm_probe_kernel<W, 8, AUX, RR>), dim3(grid), dim3(64 * W), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((hbm_probe_kernel<W, 16, AUX, RR>), dim3(grid), dim3(64 * W), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <int W, int AUX>
+hipError_t launch_w(const ProbeArgs &a, int grid, int depth, hipStream_t s) {
+    return a.mode == VQ_PROBE_REREAD ? launch_rr<W, AUX, true>(a, grid, depth, s)
+                                     : launch_rr<W, AUX, false>(a, grid, depth, s);
 }
 
 template <int AUX>
@@ -96,7 +114,7 @@ hipError_t launch_aux(const ProbeArgs &a, int grid, int waves, int depth, hipStr
 hipError_t launch_hbm_probe(const void *buf, size_t bytes, int mode, int groups, int waves, int depth,
                             bool nontemporal, uint32_t *sink, hipStream_t stream) {
     ProbeArgs a{static_cast<const uint8_t *>(buf), (uint32_t)bytes, mode, 0u, 0x9E3779B9u, sink};
-    if (mode == VQ_PROBE_SHARES)
+    if (mode == VQ_PROBE_SHARES || mode == VQ_PROBE_REREAD)
         a.share = (uint32_t)(bytes / (size_t)groups);
     const int grid = mode == VQ_PROBE_BLOCKS ? (int)(bytes / kBlock) : groups;
     return nontemporal ? launch_aux<kAuxStream>(a, grid, waves, depth, stream)

@@ -437,6 +437,13 @@ size_t vq_greedy_workspace_bytes(int64_t n_rows, int64_t vocab);
  *                    pattern); bytes % (groups * waves_per_group * 1024) == 0;
  *   VQ_PROBE_WINDOW  `groups` workgroups reading 64 KiB blocks b, b + groups,
  *                    b + 2 groups, ...
+ *   VQ_PROBE_REREAD  as VQ_PROBE_SHARES, but each workgroup reads its share
+ *                    VQ_PROBE_REREAD_PASSES times over within the launch, so
+ *                    that after the first pass a share small enough for L2
+ *                    is read from L2: the launch reads that many times
+ *                    `bytes` (the rate of L2 hits per CU, not of HBM);
+ *                    bytes / (groups * waves_per_group * 1024) must be a
+ *                    power of two;
  * waves_per_group 4, 8 or 16; depth (loads in flight per wave) 4, 8 or 16;
  * nontemporal 0 (default cache policy) or 1 (non-temporal loads, the policy
  * of a stream read once); 65536 <= bytes <= 2^31, bytes % 65536 == 0;
@@ -446,6 +453,8 @@ size_t vq_greedy_workspace_bytes(int64_t n_rows, int64_t vocab);
 #define VQ_PROBE_BLOCKS 0
 #define VQ_PROBE_SHARES 1
 #define VQ_PROBE_WINDOW 2
+#define VQ_PROBE_REREAD 3
+#define VQ_PROBE_REREAD_PASSES 16
 int vq_hbm_read_probe(const void *buf, size_t bytes, int mode, int groups, int waves_per_group, int depth,
                       int nontemporal, uint32_t *sink, void *stream);
 

@@ -8,7 +8,8 @@ import block_quantized_gemm_amd as vq
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("mode,groups", [("blocks", 0), ("shares", 16), ("window", 7), ("window", 300)])
+@pytest.mark.parametrize("mode,groups", [("blocks", 0), ("shares", 16), ("window", 7), ("window", 300),
+                                         ("reread", 16), ("reread", 256)])
 @pytest.mark.parametrize("waves,depth", [(4, 16), (8, 8), (16, 4)])
 @pytest.mark.parametrize("nt", [False, True])
 def test_probe_patterns_run_and_write_nothing(mode, groups, waves, depth, nt):
