@@ -39,12 +39,14 @@
 //    (tile group x 8 steps, 4 on panel weights): the weight pipeline never drains between
 //    chunks, the next chunk's activations and scales load into the other of
 //    two LDS buffers, a tile group inside the share is summed in registers
-//    over all of K, and a tile group cut between two shares is finished by
-//    the last of its workgroups to arrive, from fp32 pieces in the workspace
-//    added in share order (the same result on every run).
+//    over all of K, and a tile group cut between two shares is finished from
+//    its fp32 parts added in share order (the same result on every run):
+//    by the last of its workgroups to arrive, from pieces in the workspace,
+//    or, when the next share's part is in before a share's last chunk, by
+//    the share's own workgroup, from registers.
 //  * Q4_0 weights come row-major or in the panel layout, where each chunk (4
 //    steps) of a 256-feature tile group is one 72 KiB record read front to
-//    back.
+//    back with non-temporal loads.
 //  * Without a workspace the one-shot kernel gives each workgroup a whole
 //    tile group over all of K, staged chunk by chunk.
 #include "vq_device.h"

@@ -112,9 +112,11 @@ __device__ __forceinline__ u32x4 q4_operand(uint32_t v) {
 // Raw buffer loads.  A buffer resource carries a byte size; the hardware
 // returns zeros for any lane whose offset falls outside it, which is how rows
 // past M or N are masked without divergent branches.  Offsets: a per-lane
-// VGPR part and a wave-uniform SGPR part.  The verify kernels read weights
-// with the default policy: non-temporal (aux = 2) and sc1 loads measured
-// slower on the weight stream.
+// VGPR part and a wave-uniform SGPR part.  Cache policy (aux): non-temporal
+// (2) for a stream read once front to back in whole lines (panel records),
+// the default (0) where a load takes half of each 128-byte line and the
+// next step takes the other half (row-major Q4_0 and FP8 rows), which L2
+// must keep.
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kAuxStream = 2;  // nt
