@@ -31,7 +31,8 @@ VQ_ERR_SCRATCH = -9
 KIND_Q4_0 = 0
 KIND_FP8_BLK128 = 1
 KIND_Q4_0_PANEL = 2
-_KINDS = {"q4_0": KIND_Q4_0, "fp8": KIND_FP8_BLK128, "q4_0_panel": KIND_Q4_0_PANEL}
+KIND_FP8_PANEL = 3
+_KINDS = {"q4_0": KIND_Q4_0, "fp8": KIND_FP8_BLK128, "q4_0_panel": KIND_Q4_0_PANEL, "fp8_panel": KIND_FP8_PANEL}
 
 PROBE_BLOCKS = 0
 PROBE_SHARES = 1
@@ -71,6 +72,11 @@ SIGNATURES = {
     "vq_gemm_q4_0_panel": (_I, [_P, _P, _I, _P, _I, _I64, _I64, _I64, _F, _P, _SZ, _P]),
     "vq_gemm_q4_0_panel_ex": (_I, [_P, _P, _I, _P, _I, _I64, _I64, _I64, _F, _I, _P, _SZ, _P]),
     "vq_gemm_q4_0_panel_grouped": (_I, [_P, _I, _I, _I, _I64, _F, _P, _SZ, _P]),
+    "vq_fp8_panel_bytes": (_SZ, [_I64, _I64]),
+    "vq_fp8_to_panel": (_I, [_P, _I64, _I64, _P, _SZ, _P]),
+    "vq_gemm_fp8_blk128_panel": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _P, _SZ, _P]),
+    "vq_gemm_fp8_blk128_panel_ex": (_I, [_P, _P, _P, _I, _P, _I, _I64, _I64, _I64, _I, _P, _SZ, _P]),
+    "vq_gemm_fp8_blk128_panel_grouped": (_I, [_P, _I, _I, _I, _I64, _P, _SZ, _P]),
     "vq_greedy_verify": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "vq_q4_0_rotate_h32": (_I, [_P, _P, _I64, _I64, _P, _P, _P]),
     "vq_greedy_workspace_bytes": (_SZ, [_I64, _I64]),
@@ -224,7 +230,7 @@ def _kind(kind: str) -> int:
 
 def workspace_bytes(kind: str, m: int, k: int) -> int:
     """Workspace bytes the default launch shape of an (M, K) verify GEMM uses
-    (kind "q4_0", "fp8" or "q4_0_panel")."""
+    (kind "q4_0", "fp8", "q4_0_panel" or "fp8_panel")."""
     return int(lib().vq_workspace_bytes(_kind(kind), m, k))
 
 
@@ -374,6 +380,58 @@ def gemm_q4_0_panel(panel, m: int, k: int, x, out, *, alpha: float = 1.0, worksp
     return out
 
 
+def fp8_panel_bytes(m: int, k: int) -> int:
+    """Bytes of the panel form of an M x K E4M3 matrix (0 for invalid sizes)."""
+    return int(lib().vq_fp8_panel_bytes(m, k))
+
+
+def fp8_to_panel(w, panel=None, *, stream=None):
+    """The panel form of E4M3 weights (w uint8 [M][K]) as a uint8 device
+    tensor of fp8_panel_bytes(M, K) bytes (written into `panel` when given).
+    The tile scales are used as they are."""
+    torch = _torch()
+    M, K = w.shape
+    _check_2d(w, "w", (M, K))
+    nbytes = fp8_panel_bytes(M, K)
+    if nbytes == 0:
+        raise ValueError("invalid FP8 shape %s" % ((M, K),))
+    if panel is None:
+        panel = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    if panel.dtype != torch.uint8 or panel.numel() < nbytes:
+        raise ValueError("panel must be a uint8 tensor of at least %d bytes" % nbytes)
+    st = lib().vq_fp8_to_panel(_dev_ptr(w, "w"), M, K, _dev_ptr(panel, "panel"), panel.numel(), _stream(stream))
+    _check(st, "vq_fp8_to_panel")
+    return panel
+
+
+def gemm_fp8_blk128_panel(panel, tile_scales, x, out, *, workspace="auto", stream=None, max_groups: int = 0):
+    """gemm_fp8_blk128 on panel weights (fp8_to_panel): tile_scales float32
+    [ceil(M/128)][K/128], x float16 / bfloat16 [N][K], out [N][M]; the walk
+    form always (workspace "auto" or a Workspace)."""
+    N, K = x.shape
+    M = out.shape[1]
+    _check_2d(out, "out", (N, M))
+    _check_2d(tile_scales, "tile_scales", ((M + 127) // 128, K // 128))
+    if panel.numel() < fp8_panel_bytes(M, K):
+        raise ValueError("panel tensor is smaller than the panel form of (%d, %d)" % (M, K))
+    if workspace is None:
+        raise ValueError("panel weights need a workspace")
+    L = lib()
+    sh = _stream(stream)
+    wp, wn = _workspace_args(workspace, KIND_FP8_PANEL, M, K, x.device, sh)
+    if max_groups:
+        st = L.vq_gemm_fp8_blk128_panel_ex(_dev_ptr(panel, "panel"), _dev_ptr(tile_scales, "tile_scales"),
+                                           _dev_ptr(x, "x"), _dtype_code(x), _dev_ptr(out, "out"),
+                                           _dtype_code(out), N, M, K, int(max_groups), wp, wn, sh)
+        _check(st, "vq_gemm_fp8_blk128_panel_ex")
+    else:
+        st = L.vq_gemm_fp8_blk128_panel(_dev_ptr(panel, "panel"), _dev_ptr(tile_scales, "tile_scales"),
+                                        _dev_ptr(x, "x"), _dtype_code(x), _dev_ptr(out, "out"), _dtype_code(out),
+                                        N, M, K, wp, wn, sh)
+        _check(st, "vq_gemm_fp8_blk128_panel")
+    return out
+
+
 def gemm_fp8_blk128_prefill(w, tile_scales, x, out, *, stream=None):
     """gemm_fp8_blk128 for prompt-sized row counts (the MFMA-tiled kernel):
     w uint8 [M][K] (E4M3FN), tile_scales float32 [ceil(M/128)][K/128], x
@@ -397,8 +455,9 @@ class GroupedCall:
     problems: list of (w, scales, x, out) device tensors, all with the same
     x dtype, out dtype and row count; kind "q4_0" (w uint8 [M][K/2], scales
     float16 [M][K/32]), "fp8" (w uint8 [M][K], scales float32
-    [ceil(M/128)][K/128]) or "q4_0_panel" (w the panel form, scales the
-    integer M).  workspace: a Workspace (grown here to what the group needs),
+    [ceil(M/128)][K/128]), "q4_0_panel" (w the panel form, scales the
+    integer M) or "fp8_panel" (w the FP8 panel form, scales the tile scales;
+    M is out's width).  workspace: a Workspace (grown here to what the group needs),
     "auto" (a new one of that size) or None (one-shot form; not for panels)."""
 
     def __init__(self, kind: str, problems, *, alpha: float = 1.0, workspace="auto"):
@@ -413,7 +472,8 @@ class GroupedCall:
         self._keep = []
         for i, (w, sc, x, out) in enumerate(problems):
             N, K = x.shape
-            M = int(sc) if self.kind == KIND_Q4_0_PANEL else w.shape[0]
+            M = int(sc) if self.kind == KIND_Q4_0_PANEL else out.shape[1] if self.kind == KIND_FP8_PANEL \
+                else w.shape[0]
             if N != self.n_rows or _dtype_code(x) != self.act_dtype or _dtype_code(out) != self.out_dtype:
                 raise ValueError("problem %d: row count and dtypes must match the first problem" % i)
             if self.kind == KIND_Q4_0_PANEL:
@@ -427,6 +487,10 @@ class GroupedCall:
             if self.kind == KIND_Q4_0:
                 _check_2d(w, "w", (M, K // 2))
                 _check_2d(sc, "scales", (M, K // 32))
+            elif self.kind == KIND_FP8_PANEL:
+                if w.numel() < fp8_panel_bytes(M, K):
+                    raise ValueError("problem %d: panel tensor too small" % i)
+                _check_2d(sc, "scales", ((M + 127) // 128, K // 128))
             else:
                 _check_2d(w, "w", (M, K))
                 _check_2d(sc, "scales", ((M + 127) // 128, K // 128))
@@ -437,7 +501,7 @@ class GroupedCall:
         self.count = len(problems)
         need = int(lib().vq_workspace_bytes_grouped(self.kind, self.table, self.count))
         if workspace is None:
-            if self.kind == KIND_Q4_0_PANEL:
+            if self.kind in (KIND_Q4_0_PANEL, KIND_FP8_PANEL):
                 raise ValueError("panel weights need a workspace")
             self.ws = None
         elif isinstance(workspace, Workspace):
@@ -462,6 +526,10 @@ class GroupedCall:
             st = L.vq_gemm_q4_0_panel_grouped(self.table, self.count, self.act_dtype, self.out_dtype,
                                               self.n_rows, self.alpha, wp, wn, sh)
             _check(st, "vq_gemm_q4_0_panel_grouped")
+        elif self.kind == KIND_FP8_PANEL:
+            st = L.vq_gemm_fp8_blk128_panel_grouped(self.table, self.count, self.act_dtype, self.out_dtype,
+                                                    self.n_rows, wp, wn, sh)
+            _check(st, "vq_gemm_fp8_blk128_panel_grouped")
         else:
             st = L.vq_gemm_fp8_blk128_grouped(self.table, self.count, self.act_dtype, self.out_dtype,
                                               self.n_rows, wp, wn, sh)

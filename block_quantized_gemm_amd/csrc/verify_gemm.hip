@@ -501,7 +501,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int TG = T * W;
     constexpr int WB = FP8 ? 2 : 1;
     constexpr int kStepBytes = FP8 ? 128 : 64;
-    constexpr int CH = PANEL ? kPanelSteps : kWalkSteps;
+    constexpr int CH = (PANEL && !FP8) ? kPanelSteps : kWalkSteps;
     constexpr int SIW = FP8 ? 0 : T;       // scale loads per wave per chunk: 16 feature rows x 64 bytes each
     constexpr int kScBuf = SIW * 1024;     // one wave's scale buffer
     constexpr int scrow = 4 * CH;          // scales per feature row in the buffer
@@ -509,9 +509,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int kCoherent = 0x10;        // sc1: agent-coherent, no cache maintenance needed
     static_assert(CH % PF == 0, "chunks hold whole pipeline rounds");
     static_assert(PANEL || scale_pieces(4) * 2 == CH, "scale rows of one chunk");
-    static_assert(!PANEL || (!FP8 && T == kPanelWaveTiles && W == kPanelWaves && CH == kPanelSteps &&
-                             T * kPanelTileScaleBytes == 1024),
-                  "one panel record per chunk, one 1 KiB scale load per wave");
+    static_assert(!PANEL || FP8 ||
+                      (T == kPanelWaveTiles && W == kPanelWaves && CH == kPanelSteps &&
+                       T * kPanelTileScaleBytes == 1024),
+                  "one Q4_0 panel record per chunk, one 1 KiB scale load per wave");
+    static_assert(!PANEL || !FP8 || (T == 1 && W * 16 == kFp8PanelFeatures && CH == kFp8PanelSteps),
+                  "one FP8 panel record per chunk, one tile per wave");
 
     const int lane = threadIdx.x & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
     // The launch constants the first chunk's position needs, loaded as one
@@ -545,13 +548,20 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         src.wrow = FP8 ? K : (K >> 1);
         src.steps = steps_of(FP8, K);
         src.s0 = r.c * CH;
-        if constexpr (PANEL) {  // the chunk's record; tile t of step s at 16 KiB * s + 1 KiB * t
+        if constexpr (PANEL && !FP8) {  // the chunk's record; tile t of step s at 16 KiB * s + 1 KiB * t
             src.rw = make_rsrc(a.w + ((size_t)r.tg * a.cpt + r.c) * kPanelRecordBytes,
                                real ? (uint32_t)kPanelRecordBytes : 0u);
             src.vw = wave * T * 1024 + 16 * lane;
             return src;
         }
         const int fwv = (r.tg * TG + wave * T) * 16;
+        if constexpr (PANEL && FP8) {  // the chunk's record; this wave's step s, half h at 16 KiB * s + 1 KiB * h
+            src.rw = make_rsrc(a.w + ((size_t)r.tg * a.cpt + r.c) * kFp8RecordBytes,
+                               real ? (uint32_t)kFp8RecordBytes : 0u);
+            src.vw = wave * 2048 + 16 * lane;
+            src.ts[0] = static_cast<const float *>(a.scales) + (size_t)(min(fwv, M - 1) >> 7) * src.steps;
+            return src;
+        }
         const int wfeat = real ? max(0, min(M - fwv, T * 16)) : 0;
         src.rw = make_rsrc(a.w + (size_t)min(fwv, M) * src.wrow, (uint32_t)wfeat * (uint32_t)src.wrow);
         src.vw = j * src.wrow + (FP8 ? 32 : 16) * g;
@@ -578,9 +588,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                 // later, which the default policy keeps in L2 (non-temporal: -7%).
                 wb[U.value][t][h] = bload16<(PANEL ? kAuxStream : kAuxCached)>(
                     src.rw,
-                    !ok ? kOut
-                        : PANEL ? src.vw + kPanelTiles * 1024 * st + 1024 * t
-                                : src.vw + kStepBytes * gs + t * 16 * src.wrow + 16 * h,
+                    !ok         ? kOut
+                    : !PANEL    ? src.vw + kStepBytes * gs + t * 16 * src.wrow + 16 * h
+                    : FP8       ? src.vw + (W * 2048) * st + 1024 * h
+                                : src.vw + kPanelTiles * 1024 * st + 1024 * t,
                     0);
             if constexpr (FP8)
                 tsb[U.value][t] = src.ts[t][min(gs, src.steps - 1)];
@@ -597,7 +608,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         stage_act_rows<W, CH / 4>(lds + buf * kActBuf, ra, a.K, s0, min(CH, steps - s0), wave, lane);
     };
     auto scales_for = [&](const ChunkRef &r, const KProblem &a, bool real, int buf) {
-        if constexpr (PANEL) {  // this wave's 1 KiB of the record's scale rows (its T tiles)
+        if constexpr (PANEL && !FP8) {  // this wave's 1 KiB of the record's scale rows (its T tiles)
             const rsrc_t rs = make_rsrc(a.w + ((size_t)r.tg * a.cpt + r.c) * kPanelRecordBytes,
                                         real ? (uint32_t)kPanelRecordBytes : 0u);
             bload16_lds(rs, sc_wave + buf * kScBuf, kPanelCodeBytes + wave * 1024 + 16 * lane);
@@ -894,6 +905,32 @@ __global__ __launch_bounds__(256) void panel_pack_kernel(const uint32_t *codes, 
 }
 
 // ---------------------------------------------------------------------------
+// FP8 panel layout: record (p, c) of a matrix with C records per panel (128
+// features x 8 steps of 128 k) starts at byte (p * C + c) * kFp8RecordBytes;
+// at 16 KiB * s + 2 KiB * w + 1 KiB * h + 16 l it holds the 16 bytes
+// [128 (8c + s) + 32 g + 16 h, +16) of feature 128 p + 16 w + j (g = l / 16,
+// j = l % 16): what lane l of wave w loads for half h of step s when it reads
+// the row-major matrix.  Features past M and steps past K are zeros.  Every
+// thread writes one 16-byte piece.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fp8_panel_pack_kernel(const u32x4 *w, int M, int K, int chunks,
+                                                             int64_t pieces, u32x4 *panel) {
+    constexpr int kPieces = kFp8RecordBytes / 16;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < pieces; i += (int64_t)gridDim.x * 256) {
+        const int64_t rec = i / kPieces;
+        const int in = (int)(i - rec * kPieces);
+        const int p = (int)(rec / chunks), c = (int)(rec - (int64_t)p * chunks);
+        const int s = in >> 10, wv = (in >> 7) & 7, h = (in >> 6) & 1, l = in & 63;
+        const int m = kFp8PanelFeatures * p + 16 * wv + (l & 15);
+        const int k0 = 128 * (kFp8PanelSteps * c + s) + 32 * (l >> 4) + 16 * h;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (m < M && k0 < K)
+            v = w[((size_t)m * K + k0) >> 4];
+        panel[i] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 namespace {
@@ -960,7 +997,7 @@ hipError_t launch_tw(const VerifyLaunch &l) {
         k.K = q.K;
         k.chunk = q.plan.chunk;
         k.ntg = verify_tile_groups(q.M, TG);
-        constexpr int kChunk = PANEL ? kPanelSteps : kWalkSteps;
+        constexpr int kChunk = (PANEL && !FP8) ? kPanelSteps : kWalkSteps;
         k.cpt = (verify_steps(FP8, q.K) + kChunk - 1) / kChunk;
         k.item0 = (int)items;
         items += walk ? (int64_t)k.ntg * k.cpt : k.ntg;
@@ -1029,6 +1066,20 @@ size_t panel_bytes(int M, int K) {
     return (size_t)((M + kPanelFeatures - 1) / kPanelFeatures) * (size_t)panel_chunks(K) * kPanelRecordBytes;
 }
 
+size_t fp8_panel_bytes(int M, int K) {
+    const int64_t chunks = ((int64_t)verify_steps(true, K) + kFp8PanelSteps - 1) / kFp8PanelSteps;
+    return (size_t)((M + kFp8PanelFeatures - 1) / kFp8PanelFeatures) * (size_t)chunks * kFp8RecordBytes;
+}
+
+hipError_t launch_fp8_panel_pack(const void *w, int M, int K, void *panel, hipStream_t stream) {
+    const int chunks = (verify_steps(true, K) + kFp8PanelSteps - 1) / kFp8PanelSteps;
+    const int64_t pieces = (int64_t)(fp8_panel_bytes(M, K) / 16);
+    const int64_t blocks = std::min<int64_t>((pieces + 255) / 256, 65536);
+    hipLaunchKernelGGL(fp8_panel_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const u32x4 *>(w), M, K, chunks, pieces, static_cast<u32x4 *>(panel));
+    return hipGetLastError();
+}
+
 hipError_t launch_panel_pack(const void *codes, const void *scales, int M, int K, void *panel,
                              hipStream_t stream) {
     const int64_t pieces = (int64_t)(panel_bytes(M, K) / 16);
@@ -1044,7 +1095,7 @@ int verify_steps(bool fp8, int K) { return fp8 ? K / 128 : (K / 32 + 3) / 4; }
 int verify_tile_groups(int M, int tiles_per_group) { return verify_tile_groups_dev(M, tiles_per_group); }
 
 int64_t verify_chunks(bool fp8, const VerifyPlan &pl, int M, int K) {
-    const int chunk = pl.panel ? kPanelSteps : kWalkSteps;
+    const int chunk = (pl.panel && !fp8) ? kPanelSteps : kWalkSteps;
     return (int64_t)verify_tile_groups(M, pl.tiles * pl.waves) * ((verify_steps(fp8, K) + chunk - 1) / chunk);
 }
 
@@ -1072,9 +1123,12 @@ size_t verify_walk_workspace(const VerifyPlan &pl, int64_t chunks) {
 bool verify_plan_finish(bool fp8, int M, int K, VerifyPlan &pl) {
     (void)M;
     if (pl.panel) {
-        if (fp8 || pl.tiles != kPanelWaveTiles || pl.waves != kPanelWaves || !pl.walk || pl.groups < 0)
+        if (!pl.walk || pl.groups < 0)
             return false;
-        pl.chunk = kPanelSteps;
+        if (fp8 ? (pl.tiles != 1 || pl.waves * 16 != kFp8PanelFeatures)
+                : (pl.tiles != kPanelWaveTiles || pl.waves != kPanelWaves))
+            return false;
+        pl.chunk = fp8 ? kFp8PanelSteps : kPanelSteps;
         return true;
     }
     if (!(pl.tiles == 1 || pl.tiles == 2 || pl.tiles == 4) || !(pl.waves == 2 || pl.waves == 4 || pl.waves == 8 ||
@@ -1096,7 +1150,16 @@ hipError_t launch_verify(const VerifyLaunch &l) {
     if (l.count < 1 || l.count > kGroupPerLaunch)
         return hipErrorInvalidValue;
     if (l.probs[0].plan.panel) {
-        if (l.fp8 || l.tiles != kPanelWaveTiles || l.waves != kPanelWaves || !l.probs[0].plan.walk)
+        if (!l.probs[0].plan.walk)
+            return hipErrorInvalidValue;
+        if (l.fp8) {
+            constexpr int kW = kFp8PanelFeatures / 16;
+            if (l.tiles != 1 || l.waves != kW)
+                return hipErrorInvalidValue;
+            return l.act_dtype == VQ_DTYPE_BF16 ? launch_tw<VQ_DTYPE_BF16, true, 1, kW, true>(l)
+                                                : launch_tw<VQ_DTYPE_F16, true, 1, kW, true>(l);
+        }
+        if (l.tiles != kPanelWaveTiles || l.waves != kPanelWaves)
             return hipErrorInvalidValue;
         return l.act_dtype == VQ_DTYPE_BF16
                    ? launch_tw<VQ_DTYPE_BF16, false, kPanelWaveTiles, kPanelWaves, true>(l)

@@ -93,6 +93,19 @@ vq::VerifyPlan panel_plan(int max_groups) {
     return pl;
 }
 
+// The plan of a panel-layout FP8 problem: the walk form, one 128-feature
+// record per chunk for a workgroup of 8 waves, one tile per wave.
+vq::VerifyPlan fp8_panel_plan(int max_groups) {
+    vq::VerifyPlan pl;
+    pl.tiles = 1;
+    pl.waves = vq::kFp8PanelFeatures / 16;
+    pl.walk = true;
+    pl.panel = true;
+    pl.groups = max_groups;
+    vq::verify_plan_finish(true, 1, 128, pl);
+    return pl;
+}
+
 int check_panel_problem(const void *w, const void *act, void *out, int64_t m, int64_t k) {
     if (!w || !act || !out)
         return VQ_ERR_NULL_POINTER;
@@ -186,6 +199,32 @@ int run_verify(bool fp8, const void *w, const void *scales, const void *act, int
                            static_cast<hipStream_t>(stream), nullptr);
 }
 
+// FP8 panel weights: the panel form of the codes, the tile scales as they are.
+int run_fp8_panel(const void *w, const void *scales, const void *act, int act_dtype, void *out, int out_dtype,
+                  int64_t n, int64_t m, int64_t k, int max_groups, void *workspace, size_t ws_bytes,
+                  void *stream) {
+    const int st = check_problem(true, w, scales, act, out, m, k);
+    if (st != VQ_OK)
+        return st;
+    if (!float_act(act_dtype) || !out_ok(out_dtype))
+        return VQ_ERR_BAD_DTYPE;
+    if (!dim_ok(n))
+        return VQ_ERR_BAD_SHAPE;
+    if (max_groups < 0)
+        return VQ_ERR_BAD_CONFIG;
+    if (workspace && !aligned16(workspace))
+        return VQ_ERR_MISALIGNED;
+    const vq::VerifyPlan pl = fp8_panel_plan(max_groups);
+    if (!workspace || walk_need(true, pl, m, k) > ws_bytes)
+        return VQ_ERR_WORKSPACE;
+    const int dev = check_device();
+    if (dev != VQ_OK)
+        return dev;
+    const vq::VerifyProblem prob{w, scales, act, out, (int)m, (int)k, pl};
+    return launch_problems(true, &prob, 1, act_dtype, out_dtype, (int)n, 1.0f, workspace,
+                           static_cast<hipStream_t>(stream), nullptr);
+}
+
 int run_panel(const void *w, const void *act, int act_dtype, void *out, int out_dtype, int64_t n, int64_t m,
               int64_t k, float alpha, int max_groups, void *workspace, size_t ws_bytes, void *stream) {
     const int st = check_panel_problem(w, act, out, m, k);
@@ -218,6 +257,13 @@ int plan_group(bool fp8, bool panel, const vq_verify_problem *problems, int coun
                vq::VerifyProblem *out) {
     for (int i = 0; i < count; ++i) {
         const vq_verify_problem &p = problems[i];
+        if (panel && fp8) {
+            const int st = check_problem(true, p.w, p.scales, p.act, p.out, p.m, p.k);
+            if (st != VQ_OK)
+                return st;
+            out[i] = vq::VerifyProblem{p.w, p.scales, p.act, p.out, (int)p.m, (int)p.k, fp8_panel_plan(0)};
+            continue;
+        }
         if (panel) {
             const int st = check_panel_problem(p.w, p.act, p.out, p.m, p.k);
             if (st != VQ_OK)
@@ -426,22 +472,28 @@ int vq_q4_0_rotate_h32(const void *w_codes, const void *w_scales, int64_t m, int
                : VQ_ERR_LAUNCH;
 }
 
+static bool kind_fp8(int kind) { return kind == VQ_KIND_FP8_BLK128 || kind == VQ_KIND_FP8_PANEL; }
+static bool kind_panel(int kind) { return kind == VQ_KIND_Q4_0_PANEL || kind == VQ_KIND_FP8_PANEL; }
+
 static bool query_ok(int kind, int64_t m, int64_t k) {
-    return (kind == VQ_KIND_Q4_0 || kind == VQ_KIND_FP8_BLK128 || kind == VQ_KIND_Q4_0_PANEL) && dim_ok(m) &&
-           dim_ok(k) && k % (kind == VQ_KIND_FP8_BLK128 ? 128 : 32) == 0;
+    return (kind == VQ_KIND_Q4_0 || kind == VQ_KIND_FP8_BLK128 || kind == VQ_KIND_Q4_0_PANEL ||
+            kind == VQ_KIND_FP8_PANEL) &&
+           dim_ok(m) && dim_ok(k) && k % (kind_fp8(kind) ? 128 : 32) == 0;
 }
 
 // The default plan of a query: panel problems have only one.
 static vq::VerifyPlan query_plan(int kind, int64_t m, int64_t k, size_t ws_bytes) {
     if (kind == VQ_KIND_Q4_0_PANEL)
         return panel_plan(0);
+    if (kind == VQ_KIND_FP8_PANEL)
+        return fp8_panel_plan(0);
     return default_plan(kind == VQ_KIND_FP8_BLK128, m, k, ws_bytes);
 }
 
 size_t vq_workspace_bytes(int kind, int64_t m, int64_t k) {
     if (!query_ok(kind, m, k))
         return 0;
-    const bool fp8 = kind == VQ_KIND_FP8_BLK128;
+    const bool fp8 = kind_fp8(kind);
     return walk_need(fp8, query_plan(kind, m, k, SIZE_MAX), m, k);
 }
 
@@ -451,7 +503,7 @@ int vq_default_launch_shape(int kind, int64_t m, int64_t k, size_t workspace_byt
         return VQ_ERR_NULL_POINTER;
     if (!query_ok(kind, m, k))
         return VQ_ERR_BAD_SHAPE;
-    const bool fp8 = kind == VQ_KIND_FP8_BLK128;
+    const bool fp8 = kind_fp8(kind);
     const vq::VerifyPlan pl = query_plan(kind, m, k, workspace_bytes);
     *tiles_per_wave = pl.tiles;
     *waves_per_group = pl.waves;
@@ -477,6 +529,50 @@ int vq_gemm_q4_0_panel_grouped(const vq_verify_problem *problems, int count, int
                                void *stream) {
     return run_group(false, true, problems, count, act_dtype, out_dtype, n_rows, alpha, workspace,
                      workspace_bytes, stream);
+}
+
+int vq_gemm_fp8_blk128_panel_grouped(const vq_verify_problem *problems, int count, int act_dtype, int out_dtype,
+                                     int64_t n_rows, void *workspace, size_t workspace_bytes, void *stream) {
+    return run_group(true, true, problems, count, act_dtype, out_dtype, n_rows, 1.0f, workspace,
+                     workspace_bytes, stream);
+}
+
+size_t vq_fp8_panel_bytes(int64_t m, int64_t k) {
+    if (!dim_ok(m) || !dim_ok(k) || k % 128 != 0)
+        return 0;
+    return vq::fp8_panel_bytes((int)m, (int)k);
+}
+
+int vq_fp8_to_panel(const void *w_e4m3, int64_t m, int64_t k, void *w_panel, size_t panel_bytes, void *stream) {
+    if (!w_e4m3 || !w_panel)
+        return VQ_ERR_NULL_POINTER;
+    if (!dim_ok(m) || !dim_ok(k) || k % 128 != 0)
+        return VQ_ERR_BAD_SHAPE;
+    if (!aligned16(w_e4m3) || !aligned16(w_panel))
+        return VQ_ERR_MISALIGNED;
+    if (panel_bytes < vq::fp8_panel_bytes((int)m, (int)k))
+        return VQ_ERR_BAD_SHAPE;
+    const int dev = check_device();
+    if (dev != VQ_OK)
+        return dev;
+    return vq::launch_fp8_panel_pack(w_e4m3, (int)m, (int)k, w_panel, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? VQ_OK
+               : VQ_ERR_LAUNCH;
+}
+
+int vq_gemm_fp8_blk128_panel(const void *w_panel, const void *w_tile_scales, const void *act, int act_dtype,
+                             void *out, int out_dtype, int64_t n_rows, int64_t m, int64_t k, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    return run_fp8_panel(w_panel, w_tile_scales, act, act_dtype, out, out_dtype, n_rows, m, k, 0, workspace,
+                         workspace_bytes, stream);
+}
+
+int vq_gemm_fp8_blk128_panel_ex(const void *w_panel, const void *w_tile_scales, const void *act, int act_dtype,
+                                void *out, int out_dtype, int64_t n_rows, int64_t m, int64_t k, int max_groups,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    return run_fp8_panel(w_panel, w_tile_scales, act, act_dtype, out, out_dtype, n_rows, m, k, max_groups,
+                         workspace, workspace_bytes, stream);
 }
 
 size_t vq_q4_0_panel_bytes(int64_t m, int64_t k) {
@@ -519,12 +615,13 @@ int vq_gemm_q4_0_panel_ex(const void *w_panel, const void *act, int act_dtype, v
 }
 
 size_t vq_workspace_bytes_grouped(int kind, const vq_verify_problem *problems, int count) {
-    if ((kind != VQ_KIND_Q4_0 && kind != VQ_KIND_FP8_BLK128 && kind != VQ_KIND_Q4_0_PANEL) || !problems ||
-        count < 1 || count > VQ_MAX_GROUP)
+    if ((kind != VQ_KIND_Q4_0 && kind != VQ_KIND_FP8_BLK128 && kind != VQ_KIND_Q4_0_PANEL &&
+         kind != VQ_KIND_FP8_PANEL) ||
+        !problems || count < 1 || count > VQ_MAX_GROUP)
         return 0;
-    const bool fp8 = kind == VQ_KIND_FP8_BLK128;
+    const bool fp8 = kind_fp8(kind);
     std::vector<vq::VerifyProblem> probs(count);
-    if (plan_group(fp8, kind == VQ_KIND_Q4_0_PANEL, problems, count, true, probs.data()) != VQ_OK)
+    if (plan_group(fp8, kind_panel(kind), problems, count, true, probs.data()) != VQ_OK)
         return 0;
     size_t need = 0;
     launch_problems(fp8, probs.data(), count, VQ_DTYPE_BF16, VQ_DTYPE_BF16, 1, 1.0f, nullptr, nullptr, &need);
@@ -610,6 +707,6 @@ const char *vq_status_string(int status) {
     }
 }
 
-int vq_version(void) { return 310; }
+int vq_version(void) { return 400; }
 
 }  // extern "C"

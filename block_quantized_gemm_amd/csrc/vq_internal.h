@@ -21,7 +21,7 @@ struct VerifyPlan {
     bool walk = false;
     int groups = 0;
     int chunk = 0;
-    bool panel = false;  // Q4_0 weights in the panel layout (walk, 2 tiles x 8 waves)
+    bool panel = false;  // weights in the panel layout (walk; Q4_0: 2 tiles x 8 waves, FP8: 1 tile x 8 waves)
 };
 
 // Q4_0 panel layout: records of 256 features x 4 steps of 128 k, the codes of
@@ -36,6 +36,15 @@ constexpr int kPanelSteps = 4;
 constexpr int kPanelCodeBytes = kPanelSteps * kPanelTiles * 1024;
 constexpr int kPanelTileScaleBytes = 16 * 4 * kPanelSteps * 2;
 constexpr int kPanelRecordBytes = kPanelCodeBytes + kPanelTiles * kPanelTileScaleBytes;
+
+// FP8 panel layout: records of 128 features x 8 steps of 128 k (128 KiB), in
+// the order the walk kernel's 8 waves (one 16-feature tile each) load them:
+// for step s, wave (tile) w and half h, the 1 KiB that lane l reads at
+// 16 KiB * s + 2 KiB * w + 1 KiB * h + 16 l.  Tile scales stay in their own
+// array.
+constexpr int kFp8PanelFeatures = 128;
+constexpr int kFp8PanelSteps = 8;
+constexpr int kFp8RecordBytes = kFp8PanelFeatures * kFp8PanelSteps * 128;
 
 // Workspace of a walk launch: arrival counters (one per workgroup and wave,
 // kept at zero between calls) in a fixed region at the start, then two fp32
@@ -101,6 +110,8 @@ hipError_t launch_verify(const VerifyLaunch &launch);
 int64_t panel_chunks(int K);
 size_t panel_bytes(int M, int K);
 hipError_t launch_panel_pack(const void *codes, const void *scales, int M, int K, void *panel, hipStream_t stream);
+size_t fp8_panel_bytes(int M, int K);
+hipError_t launch_fp8_panel_pack(const void *w, int M, int K, void *panel, hipStream_t stream);
 
 // Greedy verification: segments per row of the argmax pass, the workspace
 // (one 8-byte key per row and segment) and the launch of both kernels.

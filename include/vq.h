@@ -71,6 +71,7 @@ extern "C" {
 #define VQ_KIND_Q4_0 0
 #define VQ_KIND_FP8_BLK128 1
 #define VQ_KIND_Q4_0_PANEL 2       /* Q4_0 in the panel layout (vq_q4_0_to_panel) */
+#define VQ_KIND_FP8_PANEL 3        /* E4M3 codes in the FP8 panel layout (vq_fp8_to_panel) */
 
 /* Largest M, K or N accepted by any entry point (indices stay in 32 bits). */
 #define VQ_MAX_DIM (1 << 24)
@@ -348,12 +349,60 @@ int vq_gemm_q4_0_panel_grouped(const vq_verify_problem *problems, int count,
                                int act_dtype, int out_dtype, int64_t n_rows, float alpha,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * FP8 panel layout -- the E4M3 codes of vq_gemm_fp8_blk128 [P3], rearranged
+ * once so that the verify GEMM reads them front to back, 1 KiB per load
+ * instruction, instead of 16 rows x 64 bytes at the row stride; the fp32
+ * tile scales stay as they are.  Per output the arithmetic is that of the
+ * row-major walk form with one tile per wave and eight waves (the same loads
+ * into the same registers, the same order); where no tile group is cut
+ * between workgroups the two return the same bits, where tile groups are cut
+ * they are cut at the same k and the results agree too.
+ *   A panel is 128 consecutive features, a chunk 1024 consecutive k.  With
+ *   P = ceil(M/128) panels and C = ceil(K/1024) chunks, record (p, c) starts
+ *   at byte (p * C + c) * 131072; for step s = 0..7 (128 k each), tile
+ *   w = 0..7 (16 features each), half h = 0..1 and lane l = 0..63 (g = l/16,
+ *   j = l % 16) the 16 bytes at 16384 s + 2048 w + 1024 h + 16 l are the
+ *   codes of k = 1024 c + 128 s + 32 g + 16 h .. +16 of feature
+ *   128 p + 16 w + j.  Features past M and steps past K hold zeros.
+ *
+ * vq_fp8_panel_bytes -- size of the FP8 panel form of an M x K matrix
+ *   (P * C * 131072 bytes; 0 for invalid sizes: K % 128 != 0).
+ * vq_fp8_to_panel -- writes the panel form of w_e4m3 ([M][K], the
+ *   vq_gemm_fp8_blk128 layout) into w_panel (panel_bytes >= the size above,
+ *   else VQ_ERR_BAD_SHAPE).  One kernel on `stream`; the input is only read.
+ * vq_gemm_fp8_blk128_panel -- vq_gemm_fp8_blk128 on panel weights: w_panel
+ *   the panel form, w_tile_scales the [ceil(M/128)][K/128] fp32 array as for
+ *   vq_gemm_fp8_blk128.  The workspace is required (VQ_ERR_WORKSPACE when
+ *   NULL or smaller than vq_workspace_bytes(VQ_KIND_FP8_PANEL, m, k)).
+ * vq_gemm_fp8_blk128_panel_ex -- the same with at most max_groups persistent
+ *   workgroups (0: as many as the device holds); max_groups < 0 gives
+ *   VQ_ERR_BAD_CONFIG.
+ * vq_gemm_fp8_blk128_panel_grouped -- vq_gemm_fp8_blk128_grouped on panel
+ *   weights: problem.w is the panel form, problem.scales the tile scales.
+ *   Needs the workspace vq_workspace_bytes_grouped(VQ_KIND_FP8_PANEL, ...)
+ *   reports.
+ * Sizes and the remaining arguments as for vq_gemm_fp8_blk128.
+ */
+size_t vq_fp8_panel_bytes(int64_t m, int64_t k);
+int vq_fp8_to_panel(const void *w_e4m3, int64_t m, int64_t k, void *w_panel, size_t panel_bytes, void *stream);
+int vq_gemm_fp8_blk128_panel(const void *w_panel, const void *w_tile_scales, const void *act, int act_dtype,
+                             void *out, int out_dtype, int64_t n_rows, int64_t m, int64_t k,
+                             void *workspace, size_t workspace_bytes, void *stream);
+int vq_gemm_fp8_blk128_panel_ex(const void *w_panel, const void *w_tile_scales, const void *act, int act_dtype,
+                                void *out, int out_dtype, int64_t n_rows, int64_t m, int64_t k,
+                                int max_groups, void *workspace, size_t workspace_bytes, void *stream);
+int vq_gemm_fp8_blk128_panel_grouped(const vq_verify_problem *problems, int count,
+                                     int act_dtype, int out_dtype, int64_t n_rows,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* Workspace a grouped call with these problems needs (0 if invalid). */
 size_t vq_workspace_bytes_grouped(int kind, const vq_verify_problem *problems, int count);
 
 /* Workspace bytes the default launch shape of an (M, K) verify GEMM uses
- * (kind VQ_KIND_Q4_0, VQ_KIND_FP8_BLK128 or VQ_KIND_Q4_0_PANEL; independent
- * of N).  0 for invalid arguments or when the shape only runs one-shot. */
+ * (kind VQ_KIND_Q4_0, VQ_KIND_FP8_BLK128, VQ_KIND_Q4_0_PANEL or
+ * VQ_KIND_FP8_PANEL; independent of N).  0 for invalid arguments or when the
+ * shape only runs one-shot. */
 size_t vq_workspace_bytes(int kind, int64_t m, int64_t k);
 
 /*

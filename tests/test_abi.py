@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert vq.lib().vq_version() == 310
+    assert vq.lib().vq_version() == 400
     for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert vq.status_string(st) and vq.status_string(st) != "unknown status"
     assert vq.status_string(-99) == "unknown status"
@@ -246,6 +246,70 @@ def test_panel_workspace_and_shape_queries():
                                                 (5120, 17408))]
     # 2680 chunks, capped at 1024 workgroups
     assert f(vq.KIND_Q4_0_PANEL, _table(layer), 5) == 65536 + 1024 * 2 * 16 * 1024
+
+
+def test_fp8_panel_size_query():
+    f = vq.lib().vq_fp8_panel_bytes
+    # records of 128 features x 1024 k of E4M3 codes (128 KiB)
+    assert f(17408, 5120) == 136 * 5 * 131072 == 17408 * 5120
+    assert f(128, 1024) == 131072
+    assert f(129, 1152) == 2 * 2 * 131072    # ragged M and K round up to whole records
+    assert f(1, 128) == 131072
+    assert f(0, 1024) == 0 and f(128, 1000) == 0 and f(128, 96) == 0 and f(128, (1 << 24) + 128) == 0
+    assert vq.fp8_panel_bytes(5120, 17408) == 40 * 17 * 131072
+
+
+def _fk(w=A, m=128, k=1024, p=C, pb=1 << 20):
+    return vq.lib().vq_fp8_to_panel(w, m, k, p, pb, None)
+
+
+def _fg(w=A, s=B, x=C, xd=vq.DTYPE_BF16, o=D, od=vq.DTYPE_BF16, n=16, m=256, k=1024, groups=0, ws=F,
+        wsb=1 << 30):
+    return vq.lib().vq_gemm_fp8_blk128_panel_ex(w, s, x, xd, o, od, n, m, k, groups, ws, wsb, None)
+
+
+def test_fp8_panel_argument_errors():
+    assert _fk(w=None) == vq.VQ_ERR_NULL_POINTER
+    assert _fk(p=None) == vq.VQ_ERR_NULL_POINTER
+    assert _fk(k=1000) == vq.VQ_ERR_BAD_SHAPE
+    assert _fk(pb=131072 - 16) == vq.VQ_ERR_BAD_SHAPE          # (128, 1024) needs one whole record
+    assert _fk(m=129, pb=2 * 131072 - 16) == vq.VQ_ERR_BAD_SHAPE
+    assert _fk(w=A + 8) == vq.VQ_ERR_MISALIGNED
+    assert _fk(p=C + 8) == vq.VQ_ERR_MISALIGNED
+    assert _fg(w=None) == vq.VQ_ERR_NULL_POINTER
+    assert _fg(s=None) == vq.VQ_ERR_NULL_POINTER
+    assert _fg(xd=vq.DTYPE_I8) == vq.VQ_ERR_BAD_DTYPE
+    assert _fg(od=vq.DTYPE_I8) == vq.VQ_ERR_BAD_DTYPE
+    assert _fg(k=1000) == vq.VQ_ERR_BAD_SHAPE
+    assert _fg(n=0) == vq.VQ_ERR_BAD_SHAPE
+    assert _fg(x=C + 8) == vq.VQ_ERR_MISALIGNED
+    assert _fg(groups=-1) == vq.VQ_ERR_BAD_CONFIG
+    assert _fg(ws=None) == vq.VQ_ERR_WORKSPACE                # panels always walk
+    assert _fg(wsb=64) == vq.VQ_ERR_WORKSPACE
+    assert _fg(ws=F + 4) == vq.VQ_ERR_MISALIGNED
+    g = vq.lib().vq_gemm_fp8_blk128_panel
+    assert g(A, B, C, vq.DTYPE_BF16, D, vq.DTYPE_BF16, 16, 256, 1024, None, 0, None) == vq.VQ_ERR_WORKSPACE
+    h = vq.lib().vq_gemm_fp8_blk128_panel_grouped
+    t = _table([(A, B, C, D, 256, 1024)])
+    assert h(t, 1, vq.DTYPE_BF16, vq.DTYPE_BF16, 16, None, 0, None) == vq.VQ_ERR_WORKSPACE
+    assert h(_table([(A, B, C, D, 256, 1000)]), 1, vq.DTYPE_BF16, vq.DTYPE_BF16, 16, F, 1 << 30,
+             None) == vq.VQ_ERR_BAD_SHAPE
+    assert h(_table([(A, None, C, D, 256, 1024)]), 1, vq.DTYPE_BF16, vq.DTYPE_BF16, 16, F, 1 << 30,
+             None) == vq.VQ_ERR_NULL_POINTER
+
+
+def test_fp8_panel_workspace_and_shape_queries():
+    # any K % 128 == 0 walks; one 128-feature panel of 8 one-tile waves per
+    # workgroup, chunks of 8 steps (one record)
+    for m, k in ((128, 1024), (17408, 5120), (1, 128), (129, 1152), (5120, 17408)):
+        t, w, walk, used = vq.default_launch_shape("fp8_panel", m, k)
+        assert (t, w, walk) == (1, 8, 1)
+        assert used == vq.workspace_bytes("fp8_panel", m, k) == _walk_need(m, k, 1, 8, chunk_steps=8)
+    f = vq.lib().vq_workspace_bytes_grouped
+    layer = [(A, B, C, D, m, k) for m, k in ((8192, 5120), (5120, 8192), (17408, 5120), (17408, 5120),
+                                             (5120, 17408))]
+    # 2 x 680 + 320 + 320 + 680 = 2680 chunks, capped at 1024 workgroups
+    assert f(vq.KIND_FP8_PANEL, _table(layer), 5) == 65536 + 1024 * 2 * 8 * 1024
 
 
 def test_greedy_argument_errors_and_workspace_query():
