@@ -93,11 +93,12 @@ def parse():
                     help="time only the headline form (grouped per layer, 16 rows), so that a kernel trace of "
                          "this run holds the headline's launches alone")
     ap.add_argument("--profile-run", action="store_true",
-                    help="a short run for rocprofv3 counters: a few grouped passes at 16 rows, then a "
-                         "512 MiB device copy that calibrates the byte counters; prints nothing else")
+                    help="a short run for rocprofv3 counters: a few grouped passes at 16 rows (Q4_0 and E4M3, "
+                         "both layouts), then a 512 MiB device copy that calibrates the byte counters; prints "
+                         "nothing else")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="read rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output of --profile-run and store "
-                         "the verify kernel's HBM bytes per launch in profiles/")
+                         "the verify kernels' HBM bytes per launch in profiles/")
     return ap.parse_args()
 
 
@@ -300,6 +301,16 @@ def stream_part(args, dev, stream):
             for _ in range(3):
                 row_major[16].per_layer(stream)
         torch.cuda.synchronize()
+        # the same passes over the stream's shapes in E4M3, in both layouts
+        fmats, facts, fouts = build_fp8_stack(layers, dev, stream)
+        for kind in ("fp8_panel", "fp8"):
+            calls = fp8_layer_calls(vq, kind, fmats, facts, fouts, 16, ws)
+            with torch.cuda.stream(stream):
+                for _ in range(3):
+                    for c in calls:
+                        c(stream)
+        torch.cuda.synchronize()
+        del fmats, facts, fouts
         a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         for _ in range(3):
@@ -331,12 +342,7 @@ def stream_part(args, dev, stream):
     mean16 = t[16]["mean_ms"]
     per_launch_us = mean16 * 1e3 / n_launch
     achieved = alg16 / n_launch / (per_launch_us * 1e-6) / 1e9
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_hash") == kernel_source_hash():
-            traffic = tr.get("panel", {}).get("hbm_bytes_per_launch")
+    traffic = stored_traffic("panel")
     res = {
         "layers": layers,
         "ms_per_step": mean16,
@@ -628,18 +634,14 @@ def prefill_part(args, dev, stream):
     return res
 
 
-def fp8_stream_part(args, dev, stream):
-    """The per-token stream's shapes in FP8 E4M3 with 128 x 128 fp32 tile
-    scales (E4M3 of N(0,1), scales U[1e-3, 1e-2], drawn on the device): 64
-    layers x 5 matrices, 16 bf16 rows per layer, each layer's five GEMMs one
-    grouped call, the step's launches replayed as one HIP graph; also at 1 row
-    and as whole-stack grouped calls.  The codes in the FP8 panel layout
-    (repacked once, before timing) lead; the row-major arrays are timed
-    beside them."""
+def build_fp8_stack(layers, dev, stream):
+    """The stream's shapes in E4M3 with 128 x 128 fp32 tile scales (E4M3 of
+    N(0,1), scales U[1e-3, 1e-2], drawn on the device), each matrix also in
+    the FP8 panel layout: (layer, M, K, codes, tile scales, panel) per
+    matrix, 16-row activations per (layer, K) and outputs per M."""
     import torch
     import block_quantized_gemm_amd as vq
     import workloads as W
-    layers = args.layers
     mats = []
     for layer in range(layers):
         for idx, (m, k) in enumerate(SHAPES):
@@ -653,6 +655,33 @@ def fp8_stream_part(args, dev, stream):
             for l in range(layers) for k in sorted({k for _, k in SHAPES})}
     outs = {m: torch.empty((16, m), dtype=torch.bfloat16, device=dev) for m in {m for m, _ in SHAPES}}
     torch.cuda.synchronize()
+    return mats, acts, outs
+
+
+def fp8_layer_calls(vq, kind, mats, acts, outs, n, ws):
+    """One grouped call per layer over its five matrices at n rows, in the
+    FP8 panel layout (kind "fp8_panel") or on the row-major arrays ("fp8")."""
+    layers = sorted({l for l, *_ in mats})
+    calls = []
+    for L in layers:
+        probs = [(pw if kind == "fp8_panel" else w, ts, acts[(l, k)][:n], outs[m][:n])
+                 for l, m, k, w, ts, pw in mats if l == L]
+        calls.append(vq.GroupedCall(kind, probs, workspace=ws))
+    return calls
+
+
+def fp8_stream_part(args, dev, stream):
+    """The per-token stream's shapes in FP8 E4M3 with 128 x 128 fp32 tile
+    scales (E4M3 of N(0,1), scales U[1e-3, 1e-2], drawn on the device): 64
+    layers x 5 matrices, 16 bf16 rows per layer, each layer's five GEMMs one
+    grouped call, the step's launches replayed as one HIP graph; also at 1 row
+    and as whole-stack grouped calls.  The codes in the FP8 panel layout
+    (repacked once, before timing) lead; the row-major arrays are timed
+    beside them."""
+    import torch
+    import block_quantized_gemm_amd as vq
+    layers = args.layers
+    mats, acts, outs = build_fp8_stack(layers, dev, stream)
     wbytes = sum(m * k + 4 * ((m + 127) // 128) * (k // 128) for _, m, k, _, _, _ in mats)
     res = {"workload": "FP8 E4M3 per-token stream: %d layers x (8192x5120, 5120x8192, 17408x5120 x2, 5120x17408), "
                        "128 x 128 fp32 tile scales, 16-row bf16 block per layer; each layer's 5 GEMMs one grouped "
@@ -688,7 +717,9 @@ def fp8_stream_part(args, dev, stream):
                 if kind == "fp8_panel":
                     res["roofline"] = {"bound": "hbm", "achieved": res["gbs_16_rows"]["median"],
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                       "frac": round(res["gbs_16_rows"]["median"] / HBM_PEAK_GBS, 4)}
+                                       "frac": round(res["gbs_16_rows"]["median"] / HBM_PEAK_GBS, 4),
+                                       "traffic": stored_traffic("fp8_panel"),
+                                       "algorithmic_bytes_per_launch": alg // layers}
         ent["t16_over_t1"] = round(times[16]["median_ms"] / times[1]["median_ms"], 4)
     del mats, acts, outs
     torch.cuda.empty_cache()
@@ -762,23 +793,38 @@ def probe_part(args, dev, stream):
 
 
 def _layout_of(kernel_name):
-    """The weight layout a Q4_0 walk-kernel dispatch ran on, or None for other
-    kernels (FP8 ones included).  The template arguments are the activation
-    type, the FP8 flag, tiles, waves, steps ahead and the panel flag."""
+    """The format and weight layout a walk-kernel dispatch ran on ("panel",
+    "row_major", "fp8_panel", "fp8_row_major"), or None for other kernels.
+    The template arguments are the activation type, the FP8 flag, tiles,
+    waves, steps ahead and the panel flag."""
     if "vq::walk_kernel<" not in kernel_name:
         return None
     targs = [a.strip() for a in kernel_name.split("vq::walk_kernel<", 1)[1].split(">")[0].split(",")]
-    if len(targs) != 6 or targs[1] != "false":
+    if len(targs) != 6:
         return None
-    return "panel" if targs[5] == "true" else "row_major"
+    lay = "panel" if targs[5] == "true" else "row_major"
+    return "fp8_" + lay if targs[1] == "true" else lay
 
 
-def traffic_from(fetch_dir, write_dir):
-    """Per-launch HBM bytes of the verify kernel, per weight layout, from two
+def stored_traffic(layout):
+    """Measured HBM bytes per grouped-layer launch of a layout from the stored
+    counter figure, or None when it is missing or was taken on other kernel
+    sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        tr = json.load(f)
+    if tr.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return tr.get(layout, {}).get("hbm_bytes_per_launch")
+
+
+def traffic_from(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
+    """Per-launch HBM bytes of the verify kernels, per format and layout, from two
     counter runs of --profile-run, each scaled by what the same counter reads
     for the plain copy of COPY_BYTES in that run."""
     def per_kernel(d, counter):
-        vals = {"panel": [], "row_major": [], "copy": []}
+        vals = {"panel": [], "row_major": [], "fp8_panel": [], "fp8_row_major": [], "copy": []}
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(path)):
                 if r["Counter_Name"] != counter:
@@ -794,28 +840,32 @@ def traffic_from(fetch_dir, write_dir):
         # the calibration copies are the largest device-to-device copies of the run
         top = max(vals["copy"])
         cal = [v for v in vals["copy"] if v >= 0.9 * top]
-        avg = {k: sum(v) / len(v) for k, v in vals.items() if k != "copy"}
+        avg = {k: sum(v) / len(v) for k, v in vals.items() if k != "copy" and v}
         return avg, sum(cal) / len(cal)
     fv, fc = per_kernel(fetch_dir, "FETCH_SIZE")
     wv, wc = per_kernel(write_dir, "WRITE_SIZE")
     fetch_scale, write_scale = COPY_BYTES / (fc * 1024), COPY_BYTES / (wc * 1024)
     rec = {
         "kernel_source_hash": kernel_source_hash(),
-        "workload": "grouped per-layer launch, 5 stream matrices, 16 bf16 rows",
+        "workload": "grouped per-layer launch, 5 stream matrices, 16 bf16 rows (Q4_0, and E4M3 with 128 x 128 "
+                    "tile scales)",
         "copy_fetch_kib": fc, "copy_write_kib": wc,
         "fetch_scale": fetch_scale, "write_scale": write_scale,
     }
-    for lay in ("panel", "row_major"):
+    for lay in ("panel", "row_major", "fp8_panel", "fp8_row_major"):
+        if lay not in fv or lay not in wv:
+            continue
         rec[lay] = {
             "hbm_bytes_per_launch": round(fv[lay] * 1024 * fetch_scale + wv[lay] * 1024 * write_scale),
             "read_bytes_per_launch": round(fv[lay] * 1024 * fetch_scale),
             "write_bytes_per_launch": round(wv[lay] * 1024 * write_scale),
             "fetch_kib_raw": fv[lay], "write_kib_raw": wv[lay],
         }
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+    return rec
 
 
 # ---------------------------------------------------------------------------- main
