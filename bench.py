@@ -476,7 +476,9 @@ def ffn_part(args, dev, stream):
 
 def fp8_part(args, dev, stream):
     """FP8 block-scaled verify GEMM at 5120 x 5120 and 17408 x 5120, 1, 4 and
-    16 bf16 rows, bf16 out: one call per matrix over > 2 GB of copies."""
+    16 bf16 rows, bf16 out: one call per matrix over > 2 GB of copies, on the
+    row-major arrays (the vq_gemm_fp8_blk128 entry point) and, under "panel",
+    in the FP8 panel layout."""
     import numpy as np
     import torch
     import block_quantized_gemm_amd as vq
@@ -488,8 +490,10 @@ def fp8_part(args, dev, stream):
         s0 = torch.from_numpy(f["tscales"]).to(dev)
         x = torch.from_numpy(f["act"].view(np.int16).copy()).to(dev).view(torch.bfloat16)
         ws = _copies(w0, m * k)
-        wsp = vq.Workspace(vq.workspace_bytes("fp8", m, k), dev)
-        ent = {"copies": len(ws)}
+        pws = [vq.fp8_to_panel(w, stream=stream) for w in ws]
+        torch.cuda.synchronize()
+        wsp = vq.Workspace(max(vq.workspace_bytes("fp8", m, k), vq.workspace_bytes("fp8_panel", m, k)), dev)
+        ent = {"copies": len(ws), "panel": {}}
         times = {}
         for n in (1, 4, 16):
             per_call = m * k + 4 * ((m + 127) // 128) * (k // 128) + n * k * 2 + n * m * 2
@@ -499,14 +503,20 @@ def fp8_part(args, dev, stream):
             def step(s, xn=xn, out=out):
                 for w in ws:
                     vq.gemm_fp8_blk128(w, s0, xn, out, workspace=wsp, stream=s)
-            t = timed(step, stream, args.reps, args.warmup)
-            times[n] = t
-            ent[str(n)] = {"gbs": rate(t, len(ws) * per_call, 1e9),
-                           "us_per_call": round(t["median_ms"] * 1e3 / len(ws), 3)}
-        ent["t16_over_t1"] = round(times[16]["median_ms"] / times[1]["median_ms"], 4)
-        g16 = ent["16"]["gbs"]["median"]
-        ent["roofline"] = {"bound": "hbm", "achieved": g16, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(g16 / HBM_PEAK_GBS, 4)}
+
+            def pstep(s, xn=xn, out=out):
+                for pw in pws:
+                    vq.gemm_fp8_blk128_panel(pw, s0, xn, out, workspace=wsp, stream=s)
+            for lay, fn, dst in (("row_major", step, ent), ("panel", pstep, ent["panel"])):
+                t = timed(fn, stream, args.reps, args.warmup)
+                times[(lay, n)] = t
+                dst[str(n)] = {"gbs": rate(t, len(ws) * per_call, 1e9),
+                               "us_per_call": round(t["median_ms"] * 1e3 / len(ws), 3)}
+        for lay, dst in (("row_major", ent), ("panel", ent["panel"])):
+            dst["t16_over_t1"] = round(times[(lay, 16)]["median_ms"] / times[(lay, 1)]["median_ms"], 4)
+            g16 = dst["16"]["gbs"]["median"]
+            dst["roofline"] = {"bound": "hbm", "achieved": g16, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(g16 / HBM_PEAK_GBS, 4)}
         if not args.no_cpu_baseline and m == 17408:
             import oracle
             done = {"bytes": 0}
@@ -520,7 +530,7 @@ def fp8_part(args, dev, stream):
                                    "cores": host_info()["threads_used"],
                                    "sample": "16 rows, output features 0..F-1 for F = %s; %.1f s" % (sample, spent)}
         res["%dx%d" % (m, k)] = ent
-        del ws
+        del ws, pws
     return res
 
 
