@@ -39,8 +39,8 @@ constexpr int kPfAStage = kPfRows * 2 * kPfK;    // 16-bit rows, 256 B each
 constexpr int kPfBStage = kPfFeats * kPfK;       // E4M3 codes, 128 B per feature
 constexpr int kPfStage = kPfAStage + kPfBStage;
 constexpr int kPfLds = 2 * kPfStage;
-constexpr int kPfRedBytes = 4 * 2 * kPfFeatTiles * 4 * 64 * 4;  // k-half exchange, half of the row tiles
-static_assert(kPfRedBytes <= kPfLds, "reduction area");
+constexpr int kPfTileBytes = 64 * kPfFeats * 4;  // k-half exchange and half of the output tile (fp32)
+static_assert(kPfTileBytes <= kPfLds, "epilogue area");
 constexpr int kPfOut = 0x7FFFFFF0;  // past every range below: the load returns zeros
 
 template <int ACT>
@@ -155,40 +155,9 @@ __global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *
         __syncthreads();
     }
 
-    // k halves: kh 1 hands its accumulators over through LDS, half of the
-    // row tiles at a time; kh 0 adds them and writes the outputs.
-    float *red = reinterpret_cast<float *>(lds);
-    const int pair = fg + 2 * rg;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        if (kh == 1) {
-#pragma unroll
-            for (int r2 = 0; r2 < 2; ++r2)
-#pragma unroll
-                for (int ft = 0; ft < kPfFeatTiles; ++ft)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        red[(((pair * 2 + r2) * kPfFeatTiles + ft) * 4 + r) * 64 + lane] = acc[2 * h + r2][ft][r];
-        }
-        __syncthreads();
-        if (kh == 0) {
-#pragma unroll
-            for (int r2 = 0; r2 < 2; ++r2)
-#pragma unroll
-                for (int ft = 0; ft < kPfFeatTiles; ++ft) {
-                    const int f = fb + fg * 144 + ft * 16 + j;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = rb + rg * 64 + (2 * h + r2) * 16 + 4 * g + r;
-                        const float v =
-                            acc[2 * h + r2][ft][r] + red[(((pair * 2 + r2) * kPfFeatTiles + ft) * 4 + r) * 64 + lane];
-                        if (row < N && f < M)
-                            store_out(out, out_dtype, (size_t)row * M + f, v);
-                    }
-                }
-        }
-        __syncthreads();
-    }
+    // k halves added in a fixed order (kh 0 + kh 1) and the tile stored as
+    // whole rows
+    prefill_store_tile<kPfFeatTiles>(acc, lds, lane, fg, rg, kh, out, out_dtype, N, M, rb, fb, 1.0f);
 }
 
 template <int ACT>

@@ -272,4 +272,105 @@ __device__ __forceinline__ void store_out(void *out, int out_dtype, size_t idx, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Output tile of a prefill workgroup (128 rows x 2 * FT * 16 features, 8
+// waves: wave = fg + 2 rg + 4 kh holds rows 64 rg .. +64 and features
+// FT * 16 fg .. of the k half kh, as acc[row tile][feature tile]).  Half of
+// the row tiles at a time: kh 1 hands its partials to kh 0 through LDS, kh 0
+// adds them (kh 0 + kh 1, the same order for every N), multiplies by alpha
+// and rounds to the output type (as store_out), the rounded half tile goes
+// through LDS, and all waves store it as 16-byte pieces of whole output rows
+// (one element at a time at a ragged right edge, or where rows are not 16-byte
+// aligned).  Needs 64 * FT * 16 * 4 * 4 bytes of LDS (every operand stage is
+// free by then) and the whole workgroup.  The output type is a template
+// argument so that the loops over elements carry no branches.
+// ---------------------------------------------------------------------------
+template <int FT, int OD>
+__device__ __forceinline__ void prefill_store_tile_od(f32x4 (&acc)[4][FT], uint8_t *lds, int lane, int fg, int rg,
+                                                      int kh, void *out, int N, int M, int rb, int fb, float alpha) {
+    constexpr int kFeats = 2 * FT * 16;
+    constexpr int esz = OD == VQ_DTYPE_F32 ? 4 : 2;
+    constexpr int rowb = kFeats * esz, row_pieces = rowb / 16, per = 16 / esz;
+    const int j = lane & 15, g = lane >> 4, pair = fg + 2 * rg;
+    const bool vec = ((size_t)M * (size_t)esz) % 16 == 0;
+    float *red = reinterpret_cast<float *>(lds);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (kh == 1) {
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        red[(((pair * 2 + r2) * FT + ft) * 4 + r) * 64 + lane] = acc[2 * h + r2][ft][r];
+        }
+        __syncthreads();
+        if (kh == 0) {
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[2 * h + r2][ft][r] =
+                            alpha * (acc[2 * h + r2][ft][r] + red[(((pair * 2 + r2) * FT + ft) * 4 + r) * 64 + lane]);
+        }
+        __syncthreads();  // the partials are read: the area takes the rounded tile
+        if (kh == 0) {
+            // local row rg 32 + r2 16 + 4 g + r of the half, local feature FT 16 fg + 16 ft + j
+            uint8_t *base = lds + (rg * 32 + 4 * g) * rowb + (FT * 16 * fg + j) * esz;
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        uint8_t *dst = base + (r2 * 16 + r) * rowb + 16 * ft * esz;
+                        const float v = acc[2 * h + r2][ft][r];
+                        if constexpr (OD == VQ_DTYPE_F32)
+                            *reinterpret_cast<float *>(dst) = v;
+                        else if constexpr (OD == VQ_DTYPE_BF16)
+                            *reinterpret_cast<__bf16 *>(dst) = static_cast<__bf16>(v);
+                        else
+                            *reinterpret_cast<_Float16 *>(dst) = static_cast<_Float16>(v);
+                    }
+        }
+        __syncthreads();
+        // local row lr is output row rb + 64 (lr / 32) + 16 (2 h + lr / 16 % 2) + lr % 16
+        for (int i = (int)threadIdx.x; i < 64 * row_pieces; i += (int)blockDim.x) {
+            const int lr = i / row_pieces, q = i - lr * row_pieces;
+            const int row = rb + (lr >> 5) * 64 + (2 * h + ((lr >> 4) & 1)) * 16 + (lr & 15);
+            const int f0 = fb + q * per;
+            if (row >= N || f0 >= M)
+                continue;
+            const uint8_t *src = lds + lr * rowb + q * 16;
+            uint8_t *dst = static_cast<uint8_t *>(out) + ((size_t)row * (size_t)M + (size_t)f0) * esz;
+            if (vec && f0 + per <= M) {
+                *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+            } else {
+                for (int e = 0; e < per && f0 + e < M; ++e) {
+                    if constexpr (esz == 4)
+                        reinterpret_cast<uint32_t *>(dst)[e] = reinterpret_cast<const uint32_t *>(src)[e];
+                    else
+                        reinterpret_cast<uint16_t *>(dst)[e] = reinterpret_cast<const uint16_t *>(src)[e];
+                }
+            }
+        }
+        __syncthreads();  // the area is reused by the next half
+    }
+}
+
+template <int FT>
+__device__ __forceinline__ void prefill_store_tile(f32x4 (&acc)[4][FT], uint8_t *lds, int lane, int fg, int rg,
+                                                   int kh, void *out, int out_dtype, int N, int M, int rb, int fb,
+                                                   float alpha) {
+    if (out_dtype == VQ_DTYPE_F32)
+        prefill_store_tile_od<FT, VQ_DTYPE_F32>(acc, lds, lane, fg, rg, kh, out, N, M, rb, fb, alpha);
+    else if (out_dtype == VQ_DTYPE_BF16)
+        prefill_store_tile_od<FT, VQ_DTYPE_BF16>(acc, lds, lane, fg, rg, kh, out, N, M, rb, fb, alpha);
+    else
+        prefill_store_tile_od<FT, VQ_DTYPE_F16>(acc, lds, lane, fg, rg, kh, out, N, M, rb, fb, alpha);
+}
+
 }  // namespace vq

@@ -49,8 +49,8 @@ constexpr int kSxStage = kW4Blocks * kW4Rows * 4;          // fp32 [block][row]
 constexpr int kSwStage = kW4Blocks * kW4Feats * 4;         // fp32 [block][feature]
 constexpr int kStage = kAStage + kBStage + kSxStage + kSwStage;
 constexpr int kW4Lds = 2 * kStage;
-constexpr int kRedBytes = 4 * 2 * kW4FeatTiles * 4 * 64 * 4;  // k-half exchange, one half of the rows
-static_assert(kRedBytes <= kW4Lds, "reduction area");
+constexpr int kTileBytes = 64 * kW4Feats * 4;  // k-half exchange and half of the output tile (fp32)
+static_assert(kTileBytes <= kW4Lds, "epilogue area");
 constexpr int kOutOfRange = 0x7FFFFFF0;  // past every range below: the load returns zeros
 constexpr uint32_t kF16Magic = 0x64646464u;  // fp16 1024 + byte
 constexpr uint32_t kF16Neg1152 = 0xE480E480u;
@@ -215,40 +215,9 @@ __global__ __launch_bounds__(kW4Threads) void w4a8_kernel(const uint8_t *__restr
         __syncthreads();
     }
 
-    // k halves: kh 1 hands its accumulators over through LDS, half of the
-    // row tiles at a time; kh 0 adds them and writes the outputs.
-    float *red = reinterpret_cast<float *>(lds);
-    const int pair = fg + 2 * rg;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        if (kh == 1) {
-#pragma unroll
-            for (int r2 = 0; r2 < 2; ++r2)
-#pragma unroll
-                for (int ft = 0; ft < kW4FeatTiles; ++ft)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        red[(((pair * 2 + r2) * kW4FeatTiles + ft) * 4 + r) * 64 + lane] = acc[2 * h + r2][ft][r];
-        }
-        __syncthreads();
-        if (kh == 0) {
-#pragma unroll
-            for (int r2 = 0; r2 < 2; ++r2)
-#pragma unroll
-                for (int ft = 0; ft < kW4FeatTiles; ++ft) {
-                    const int f = fb + fg * 144 + ft * 16 + j;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = rb + rg * 64 + (2 * h + r2) * 16 + 4 * g + r;
-                        const float v =
-                            acc[2 * h + r2][ft][r] + red[(((pair * 2 + r2) * kW4FeatTiles + ft) * 4 + r) * 64 + lane];
-                        if (row < N && f < M)
-                            store_out(out, out_dtype, (size_t)row * M + f, alpha * v);
-                    }
-                }
-        }
-        __syncthreads();
-    }
+    // k halves added in a fixed order (kh 0 + kh 1), times alpha, and the
+    // tile stored as whole rows
+    prefill_store_tile<kW4FeatTiles>(acc, lds, lane, fg, rg, kh, out, out_dtype, N, M, rb, fb, alpha);
 }
 
 }  // namespace
