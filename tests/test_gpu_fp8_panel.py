@@ -296,6 +296,33 @@ def test_grouped_layer_rows_bit_identical_at_every_width():
         assert np.array_equal(o[5], f[12]), i
 
 
+@pytest.mark.parametrize("act,out", [("bf16", "bf16"), ("f16", "f32")])
+def test_grouped_more_than_16_rows_and_ragged_widths(act, out):
+    """A grouped call over ragged matrices with 37 rows (three groups of 16):
+    every output within the bar of the oracle, and rows 16..31 equal to a
+    16-row call on them."""
+    g = np.random.Generator(np.random.PCG64(520))
+    mats = [_mat(M, K, 521 + i)[0] for i, (M, K) in enumerate(((520, 4096), (130, 1152), (17, 384)))]
+    xs = []
+    for p in mats:
+        x = g.standard_normal((37, p.K))
+        xs.append(W.f32_to_bf16_bits(x) if act == "bf16" else W.f32_to_f16_bits(x))
+    ws = vq.Workspace(16 << 20)
+
+    def call(r0, r1):
+        outs = [torch.empty((r1 - r0, p.M), dtype=TORCH_DT[out], device="cuda") for p in mats]
+        vq.GroupedCall("fp8_panel", [(p.panel, p.ts, to_dev(np.ascontiguousarray(x[r0:r1]), TORCH_DT[act]), o)
+                                     for p, x, o in zip(mats, xs, outs)], workspace=ws)()
+        torch.cuda.synchronize()
+        return outs
+    full = call(0, 37)
+    dt = oracle.BF16 if act == "bf16" else oracle.F16
+    for p, x, y in zip(mats, xs, full):
+        parity(out_to_f64(y), p.oracle(x, dt), out)
+    for y, z in zip(full, call(16, 32)):
+        assert torch.equal(z, y[16:32])
+
+
 def test_grouped_graph_replays_match_eager():
     mats = []
     for i, (M, K) in enumerate(((2048, 5120), (1024, 8192), (520, 17408))):
