@@ -355,9 +355,9 @@ int vq_gemm_q4_0_panel_grouped(const vq_verify_problem *problems, int count,
  * instruction, instead of 16 rows x 64 bytes at the row stride; the fp32
  * tile scales stay as they are.  Per output the arithmetic is that of the
  * row-major walk form with one tile per wave and eight waves (the same loads
- * into the same registers, the same order); where no tile group is cut
- * between workgroups the two return the same bits, where tile groups are cut
- * they are cut at the same k and the results agree too.
+ * into the same registers, the same order): at the same workgroup cap,
+ * vq_gemm_fp8_blk128_ex with tiles_per_wave 1 and waves_per_group 8 cuts tile
+ * groups at the same k and returns the same bits.
  *   A panel is 128 consecutive features, a chunk 1024 consecutive k.  With
  *   P = ceil(M/128) panels and C = ceil(K/1024) chunks, record (p, c) starts
  *   at byte (p * C + c) * 131072; for step s = 0..7 (128 k each), tile
