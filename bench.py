@@ -66,8 +66,9 @@ PARTS = ("stream", "tiny", "ffn", "fp8", "fp8stream", "prefill", "greedy", "prob
 
 
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources' code: comments and whitespace do not count,
-    any other edit invalidates the stored traffic figure."""
+    """Hash of the kernel sources' code and the compiler flags: comments and
+    whitespace do not count, any other edit invalidates the stored traffic
+    figure."""
     import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -76,6 +77,12 @@ def kernel_source_hash() -> str:
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
+    # the compiler flags shape the machine code too (include paths aside)
+    from block_quantized_gemm_amd import build
+    flags = [f for f in build.HIPCC_FLAGS if not f.startswith("-I")]
+    for src in sorted(build.SOURCE_FLAGS):
+        flags += [src, *build.SOURCE_FLAGS[src]]
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 

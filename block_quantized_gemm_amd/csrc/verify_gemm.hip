@@ -79,7 +79,8 @@ struct KGroup {
     KProblem p[kGroupPerLaunch];
     int item0[kGroupPerLaunch];  // p[i].item0, packed for one batch of scalar loads
     int count, items, N, out_dtype;
-    int share, extra;            // walk kernel: items = share * gridDim.x + extra (range arithmetic in 32 bits)
+    int share, extra;            // walk kernel: items = share * grid + extra (range arithmetic in 32 bits); the
+                                 // walk kernel takes these, count and N as scalar arguments
     float alpha;
     float *part;    // pieces: [workgroups][2 sides][TG tiles][64 lanes][4]
     uint32_t *cnt;  // arrival counters: [workgroups][waves], zero between calls
@@ -483,6 +484,9 @@ __device__ __forceinline__ ChunkRef next_chunk(int count, const KProblem &a, Chu
     return r;
 }
 
+// Problems whose first chunk the walk kernel takes as a scalar argument.
+constexpr int kPreloadFirst = 8;
+
 // First chunk of workgroup b's range, floor(b * items / G), and the workgroup
 // whose range holds chunk c.  Ranges hold share or share + 1 chunks, and the
 // longer ones are spread evenly over the logical ids (so over the XCDs, which
@@ -495,8 +499,16 @@ __device__ __forceinline__ int range_owner(const KGroup &grp, int c, int G) {
     return (int)(((int64_t)(c + 1) * G - 1) / grp.items);
 }
 
+// The launch constants that place a workgroup's first chunk come first, as
+// plain scalar arguments: the command processor writes them into SGPRs
+// before the first instruction (kernel-argument preloading, enabled for this
+// file by the build), so the first chunk's problem records are the kernel's
+// first memory round trip.  G is the grid size, i1..i8 the first chunks of
+// problems 1..8 (launches of more than 9 problems load item0 instead).
 template <int ACT, bool FP8, int T, int W, int PF, bool PANEL>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void walk_kernel(const KGroup grp) {
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void walk_kernel(
+    int G, int share, int extra, int count, int nrows, int i1, int i2, int i3, int i4, int i5, int i6, int i7, int i8,
+    const KGroup grp) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int TG = T * W;
     constexpr int WB = FP8 ? 2 : 1;
@@ -517,17 +529,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                   "one FP8 panel record per chunk, one tile per wave");
 
     const int lane = threadIdx.x & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
-    // The launch constants the first chunk's position needs, loaded as one
-    // batch: at kernel start every scalar load is a memory round trip, and the
-    // compiler would otherwise spread them over several.
-    const int G = (int)gridDim.x;
-    const int count = grp.count, share = grp.share, extra = grp.extra, nrows = grp.N;
     float *const part = grp.part;
-    int item0[kGroupPerLaunch];
-#pragma unroll
-    for (int q = 0; q < kGroupPerLaunch; ++q)
-        item0[q] = grp.item0[q];
-    __builtin_amdgcn_sched_barrier(0);
     // Workgroups go to the 8 XCDs in turn (blockIdx % 8); give each XCD a
     // contiguous run of ranges, so that the workgroups sharing an L2 walk
     // neighbouring tile groups and reuse each other's activation chunks.
@@ -661,7 +663,20 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // round of weights.  The first chunk's problem record and the next
     // problem's are read by value, in one round of loads.
     int it = ib;
-    const int pi0 = find_problem(item0, count, it);
+    int pi0;
+    if (count <= kPreloadFirst + 1) {
+        const int first[kPreloadFirst] = {i1, i2, i3, i4, i5, i6, i7, i8};
+        pi0 = 0;
+#pragma unroll
+        for (int q = 1; q <= kPreloadFirst; ++q)
+            pi0 += (q < count && it >= first[q - 1]) ? 1 : 0;
+    } else {
+        int item0[kGroupPerLaunch];
+#pragma unroll
+        for (int q = 0; q < kGroupPerLaunch; ++q)
+            item0[q] = grp.item0[q];
+        pi0 = find_problem(item0, count, it);
+    }
     const KProblem P0 = grp.p[pi0], P1 = grp.p[min(pi0 + 1, count - 1)];
     __builtin_amdgcn_sched_barrier(0);
     ChunkRef cref = chunk_in(P0, pi0, it);
@@ -972,16 +987,15 @@ hipError_t launch_tw(const VerifyLaunch &l) {
     const VerifyPlan &pl = l.probs[0].plan;
     const bool walk = pl.walk;
     const size_t shm = verify_lds_bytes(FP8, T, W, walk);
-    void (*kern)(KGroup) = walk_kernel<ACT, FP8, T, W, walk_depth(FP8, T), PANEL>;
+    const auto wkern = walk_kernel<ACT, FP8, T, W, walk_depth(FP8, T), PANEL>;
+    void (*okern)(KGroup) = nullptr;
     if constexpr (W <= 8 && !PANEL) {  // the one-shot kernel takes 2, 4 or 8 waves
-        if (!walk)
-            kern = oneshot_kernel<ACT, FP8, T, W, pipeline_depth(FP8, T)>;
+        okern = oneshot_kernel<ACT, FP8, T, W, pipeline_depth(FP8, T)>;
     } else if (!walk) {
         return hipErrorInvalidValue;
     }
-    if (shm > 64 * 1024 &&
-        hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)shm) != hipSuccess)
+    const void *kern = walk ? reinterpret_cast<const void *>(wkern) : reinterpret_cast<const void *>(okern);
+    if (shm > 64 * 1024 && hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) != hipSuccess)
         return hipErrorInvalidValue;
     KGroup grp{};
     grp.count = l.count;
@@ -1032,7 +1046,16 @@ hipError_t launch_tw(const VerifyLaunch &l) {
             grp.p[i].act = static_cast<const uint16_t *>(q.act) + (size_t)g0 * 16 * q.K;
             grp.p[i].out = static_cast<char *>(q.out) + (size_t)g0 * 16 * q.M * out_elem_bytes(l.out_dtype);
         }
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * W), shm, l.stream, grp);
+        if (walk) {
+            int first[kPreloadFirst];  // problems past the launch's count are never compared
+            for (int q = 1; q <= kPreloadFirst; ++q)
+                first[q - 1] = q < l.count ? grp.item0[q] : 0x7FFFFFFF;
+            hipLaunchKernelGGL(wkern, dim3(grid), dim3(64 * W), shm, l.stream, grid, grp.share, grp.extra, grp.count,
+                               grp.N, first[0], first[1], first[2], first[3], first[4], first[5], first[6], first[7],
+                               grp);
+        } else {
+            hipLaunchKernelGGL(okern, dim3(grid), dim3(64 * W), shm, l.stream, grp);
+        }
     }
     return hipGetLastError();
 }
