@@ -176,6 +176,98 @@ def host_info():
             "threads_used": threads}
 
 
+def smi_clocks(doc):
+    """Clock readings of rocm-smi --showclocks --json: {card: {clock: speed}}."""
+    if not isinstance(doc, dict):
+        return None
+    return {card: {k.replace(" clock speed:", "").strip(): v for k, v in vals.items() if "clock speed" in k}
+            for card, vals in doc.items() if isinstance(vals, dict) and card.startswith("card")}
+
+
+def smi_other_processes(doc, own_pid):
+    """Processes that rocm-smi --showpids --json lists on the GPU, other than
+    own_pid: [(pid, name)].  Entries look like {"PID123": "python3, 1, ..."}."""
+    if not isinstance(doc, dict):
+        return None
+    found = []
+    for vals in doc.values():
+        if not isinstance(vals, dict):
+            continue
+        for key, val in vals.items():
+            if not key.startswith("PID"):
+                continue
+            try:
+                pid = int(key[3:])
+            except ValueError:
+                continue
+            if pid != own_pid:
+                found.append((pid, str(val).split(",")[0].strip()))
+    return sorted(found)
+
+
+def _smi(flag):
+    import shutil
+    import subprocess
+    tool = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    try:
+        r = subprocess.run([tool, flag, "--json"], capture_output=True, text=True, timeout=30)
+        return json.loads(r.stdout) if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError, ValueError):
+        return None
+
+
+def gpu_state():
+    """The GPU's clocks and the other processes on it, as rocm-smi reports them
+    (the timings assume an exclusive GPU); None for what the tool could not
+    tell (an unprivileged user may not see the process list)."""
+    return {"clocks": smi_clocks(_smi("--showclocks")),
+            "other_processes": smi_other_processes(_smi("--showpids"), os.getpid())}
+
+
+def mhz(text):
+    """'(2100Mhz)' -> 2100.0, else None."""
+    digits = "".join(c for c in str(text) if c.isdigit() or c == ".")
+    try:
+        return float(digits)
+    except ValueError:
+        return None
+
+
+class ClockSampler:
+    """Reads the shader and memory clocks with rocm-smi from a host thread,
+    again and again, while a timed part runs: the clocks the work ran at."""
+
+    def __init__(self, period_s=0.1):
+        import threading
+        self.period = period_s
+        self.samples = {}
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self.stop.is_set():
+            clocks = smi_clocks(_smi("--showclocks")) or {}
+            for card in clocks.values():
+                for name, val in card.items():
+                    v = mhz(val)
+                    if v is not None:
+                        self.samples.setdefault(name, []).append(v)
+            self.stop.wait(self.period)
+
+    def __enter__(self):
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.thread.join(timeout=60)
+
+    def summary(self):
+        import statistics
+        return {name + "_mhz": {"median": statistics.median(v), "min": min(v), "max": max(v), "samples": len(v)}
+                for name, v in sorted(self.samples.items()) if v}
+
+
 def cpu_sample(run_f, f0, f_max, budget_s):
     """Calls run_f(F) for F = f0, 2 f0, ... (at most f_max) until budget_s
     seconds are spent; returns (seconds, [F...])."""
@@ -911,8 +1003,11 @@ def main():
     if args.profile_run:
         stream_part(args, dev, stream)
         return
-    head = stream_part(args, dev, stream)
+    state_before = gpu_state()
+    with ClockSampler() as clocks:
+        head = stream_part(args, dev, stream)
     if args.only == "stream" or args.headline_only:
+        head["clocks_during_timing"] = clocks.summary()
         print(json.dumps(head))
         return
     print("stream timed: %.1f GB/s" % head["gbs_by_rows"]["16"], file=sys.stderr, flush=True)
@@ -958,6 +1053,8 @@ def main():
     result["hbm_probe"] = probe
     result["host"] = host_info()
     result["gpu"] = torch.cuda.get_device_properties(dev).name
+    result["gpu_state"] = {"before": state_before, "after": gpu_state(),
+                           "clocks_during_stream_timing": clocks.summary()}
     result["roofline"] = head["roofline"]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = stream_cpu_baseline(args.cpu_seconds)

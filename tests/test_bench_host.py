@@ -66,3 +66,19 @@ def test_stored_traffic_needs_the_current_sources(tmp_path, monkeypatch):
                                 "panel": {"hbm_bytes_per_launch": 5}}))
     assert bench.stored_traffic("panel") == 5
     assert bench.stored_traffic("fp8_panel") is None
+
+
+def test_gpu_state_parsing():
+    clocks = {"card0": {"fclk clock speed:": "(1600Mhz)", "mclk clock speed:": "(1300Mhz)",
+                        "sclk clock speed:": "(2400Mhz)", "sclk clock level:": "1", "Card Series": "x"},
+              "system": {"note": 1}}
+    assert bench.smi_clocks(clocks) == {"card0": {"fclk": "(1600Mhz)", "mclk": "(1300Mhz)", "sclk": "(2400Mhz)"}}
+    pids = {"system": {"PID77": "python3, 1, 1024, 0, 0", "PID5": "other, 1, 0, 0, 0", "Note": "x"}}
+    assert bench.smi_other_processes(pids, 77) == [(5, "other")]
+    assert bench.smi_other_processes({"system": {}}, 1) == []
+    assert bench.smi_clocks(None) is None and bench.smi_other_processes(None, 1) is None
+
+
+def test_mhz():
+    assert bench.mhz("(2100Mhz)") == 2100.0
+    assert bench.mhz("n/a") is None
