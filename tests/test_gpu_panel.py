@@ -332,3 +332,26 @@ def test_grouped_graph_replays_match_eager():
         call()  # eager work on the same workspace between replays
         torch.cuda.synchronize()
     assert not ws.tensor[:65536].cpu().numpy().any()  # the counters are back at zero
+
+
+@pytest.mark.parametrize("count", [9, 10, 14])
+def test_grouped_many_problems_exact_integers(count):
+    """Grouped calls of 9 problems (every first chunk among the kernel's
+    preloaded arguments) and of 10 and 14 (the kernel reads the first chunks
+    from the launch record): ragged matrices with unit scales and small-integer
+    rows, so every output equals the oracle bit for bit, wherever the
+    workgroups' ranges cut the tile groups."""
+    g = np.random.Generator(np.random.PCG64(430 + count))
+    N = 7
+    mats, outs = [], []
+    for _ in range(count):
+        M, K = int(g.integers(1, 700)), 32 * int(g.integers(1, 100))
+        p = Panel(W.q4_0_codes(M, K, g), np.full((M, K // 32), 0x3C00, dtype=np.uint16))
+        bits = W.f32_to_bf16_bits(g.integers(-4, 5, size=(N, K)).astype(np.float32))
+        mats.append((p, bits, to_dev(bits, torch.bfloat16)))
+        outs.append(torch.empty((N, M), dtype=torch.float32, device="cuda"))
+    vq.GroupedCall("q4_0_panel", [(p.panel, p.M, x, o) for (p, _, x), o in zip(mats, outs)],
+                   workspace=vq.Workspace(64 << 20))()
+    torch.cuda.synchronize()
+    for i, ((p, bits, _), o) in enumerate(zip(mats, outs)):
+        assert np.array_equal(out_to_f64(o), p.oracle(bits)), (i, p.M, p.K)
