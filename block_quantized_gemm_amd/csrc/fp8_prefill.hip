@@ -10,19 +10,20 @@
 // Arithmetic: every E4M3 code converts exactly to bf16 / fp16 (hardware
 // conversion); the MFMA 16x16x32 multiplies it by the activations exactly and
 // sums in fp32.  A 16-feature tile and the 128 k of one chunk lie in one
-// scale tile, so MFMA steps within a chunk accumulate a partial that is added
-// to the output with one fp32 FMA with that tile's scale.
+// scale tile, so the four MFMA steps of a chunk accumulate a partial (from
+// zero) that is added to the output with one fp32 FMA with that tile's
+// scale; each row's arithmetic is independent of N.
 //
-// Tiling: a workgroup of 8 waves computes 128 rows x 288 features (18 MFMA
-// tiles; 17408 features make 61 columns, so a 512-row prompt is one round of
-// 244 workgroups on 256 CUs).  Wave (fg, rg, kh) takes features 144 fg ..
-// +144, rows 64 rg .. +64, and the MFMA steps 2 kh, 2 kh + 1 of every 128-k
-// chunk: for each output tile it sums its two steps on the MFMA and adds that
-// partial, times the chunk's tile scale, with one fp32 FMA; the two k halves
-// are added at the end (kh 0 + kh 1, fixed order), so each row's arithmetic
-// is independent of N.  Chunks (activations 128 rows x 256 B, codes 288
-// features x 128 B) are loaded straight into LDS (16 B per lane, no
-// registers) one chunk ahead, into the other of two stages; 16-byte pieces
+// Tiling: a workgroup of 8 waves computes 128 rows x 320 features (20 MFMA
+// tiles; 17408 features make 55 columns, so a 512-row prompt is one round of
+// 220 workgroups on 256 CUs).  Wave (rg, fg) takes rows 64 rg .. +64 and
+// features 80 fg .. +80 over all of K: per chunk 4 row tiles x 5 feature
+// tiles x 4 steps = 80 MFMAs, each converted weight operand serving the 4
+// row tiles, and one scale FMA per output.  (A 128 x 288 tiling with the
+// chunk's steps split between two waves took two scale FMAs per output and
+// chunk and was about 3% slower.)  Chunks (activations 128 rows x 256 B,
+// codes 320 features x 128 B) are loaded straight into LDS (16 B per lane,
+// no registers) one chunk ahead, into the other of two stages; 16-byte pieces
 // are XOR-swizzled by row and by feature so that the operand reads are free
 // of bank conflicts.
 #include "vq_device.h"
@@ -32,16 +33,72 @@ namespace vq {
 
 namespace {
 
-constexpr int kPfRows = 128, kPfFeats = 288, kPfK = 128;  // per workgroup and chunk
+constexpr int kPfRows = 128, kPfFeats = 320, kPfK = 128;  // per workgroup and chunk
 constexpr int kPfThreads = 512;
-constexpr int kPfFeatTiles = kPfFeats / 2 / 16;  // 9 tiles per wave
+constexpr int kPfFeatTiles = kPfFeats / 4 / 16;  // 5 tiles per wave
 constexpr int kPfAStage = kPfRows * 2 * kPfK;    // 16-bit rows, 256 B each
 constexpr int kPfBStage = kPfFeats * kPfK;       // E4M3 codes, 128 B per feature
 constexpr int kPfStage = kPfAStage + kPfBStage;
 constexpr int kPfLds = 2 * kPfStage;
-constexpr int kPfTileBytes = 64 * kPfFeats * 4;  // k-half exchange and half of the output tile (fp32)
-static_assert(kPfTileBytes <= kPfLds, "epilogue area");
 constexpr int kPfOut = 0x7FFFFFF0;  // past every range below: the load returns zeros
+constexpr int kPfEpiBytes = 64 * kPfFeats * 4;  // half of the output tile (fp32), staged for the stores
+static_assert(kPfEpiBytes <= kPfLds, "epilogue area");
+
+// The output tile, half of the rows at a time: the waves of row group h round
+// their results to the output type into LDS, then all waves store 16-byte
+// pieces of whole output rows (one element at a time at a ragged right edge,
+// or where rows are not 16-byte aligned).  The stages are free by then.
+template <int OD>
+__device__ __forceinline__ void store_tile(f32x4 (&acc)[4][kPfFeatTiles], uint8_t *lds, int lane, int fg, int rg,
+                                               void *out, int N, int M, int rb, int fb) {
+    constexpr int esz = OD == VQ_DTYPE_F32 ? 4 : 2;
+    constexpr int rowb = kPfFeats * esz, row_pieces = rowb / 16, per = 16 / esz;
+    const int j = lane & 15, g = lane >> 4;
+    const bool vec = ((size_t)M * (size_t)esz) % 16 == 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (rg == h) {
+            // local row 16 rt + 4 g + r, local feature 80 fg + 16 ft + j
+            uint8_t *base = lds + (4 * g) * rowb + (80 * fg + j) * esz;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int ft = 0; ft < kPfFeatTiles; ++ft)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        uint8_t *dst = base + (rt * 16 + r) * rowb + 16 * ft * esz;
+                        const float v = acc[rt][ft][r];
+                        if constexpr (OD == VQ_DTYPE_F32)
+                            *reinterpret_cast<float *>(dst) = v;
+                        else if constexpr (OD == VQ_DTYPE_BF16)
+                            *reinterpret_cast<__bf16 *>(dst) = static_cast<__bf16>(v);
+                        else
+                            *reinterpret_cast<_Float16 *>(dst) = static_cast<_Float16>(v);
+                    }
+        }
+        __syncthreads();
+        for (int i = (int)threadIdx.x; i < 64 * row_pieces; i += (int)blockDim.x) {
+            const int lr = i / row_pieces, q = i - lr * row_pieces;
+            const int row = rb + 64 * h + lr;
+            const int f0 = fb + q * per;
+            if (row >= N || f0 >= M)
+                continue;
+            const uint8_t *src = lds + lr * rowb + q * 16;
+            uint8_t *dst = static_cast<uint8_t *>(out) + ((size_t)row * (size_t)M + (size_t)f0) * esz;
+            if (vec && f0 + per <= M) {
+                *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+            } else {
+                for (int e = 0; e < per && f0 + e < M; ++e) {
+                    if constexpr (esz == 4)
+                        reinterpret_cast<uint32_t *>(dst)[e] = reinterpret_cast<const uint32_t *>(src)[e];
+                    else
+                        reinterpret_cast<uint16_t *>(dst)[e] = reinterpret_cast<const uint16_t *>(src)[e];
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
 
 template <int ACT>
 __global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *__restrict__ w,
@@ -52,9 +109,7 @@ __global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *
     using A16 = Act16<ACT>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int lane = threadIdx.x & 63, wave = wave_id(), j = lane & 15, g = lane >> 4;
-    const int fg = wave & 1, rg = (wave >> 1) & 1, kh = wave >> 2;
-    // tiles in column order (the row groups of one feature column are
-    // consecutive), numbered so that each XCD holds a run of whole columns
+    const int rg = wave & 1, fg = wave >> 1;
     const int tile = xcd_run_index((int)blockIdx.x, (int)gridDim.x);
     const int fb = tile / row_groups * kPfFeats, rb = tile % row_groups * kPfRows;
     const int nch = K / kPfK, nft = (M + 127) / 128;
@@ -62,7 +117,11 @@ __global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *
 
     // Ranges: activation rows in groups of 32, codes in groups of 64
     // features (each below 2^30 bytes); rows past N and features past M read
-    // zeros.  A wave load covers 4 rows x 256 B or 8 features x 128 B.
+    // zeros.  A wave load covers 4 rows x 256 B or 8 features x 128 B:
+    // activation load i = wave + 8 m covers rows 4 i .. 4 i + 3 (row 4 wave +
+    // lane / 16 of range m), code load i = wave + 8 m features 8 i .. 8 i + 7
+    // (8 wave + lane / 8 of range m).  The swizzle terms depend on the row or
+    // feature mod 16 only, the same for every m.
     rsrc_t ra[4], rw[5];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -70,12 +129,6 @@ __global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *
 #pragma unroll
     for (int m = 0; m < 5; ++m)
         rw[m] = make_rsrc(w + (size_t)(fb + 64 * m) * K, (uint32_t)max(0, min(64, feats - 64 * m)) * (uint32_t)K);
-    // Lane offsets of the chunk loads (the chunk's k offset goes in the
-    // wave-uniform part).  Activation load i = wave + 8 m covers rows 4 i ..
-    // 4 i + 3 of range m (row 4 wave + lane / 16 there); code load i = wave +
-    // 8 m (< 36) covers features 8 i .. 8 i + 7 of range m (8 wave + lane / 8).
-    // The swizzle terms depend on the row or feature mod 16 only, the same
-    // for every m.
     const int a_row = 4 * wave + (lane >> 4), b_feat = 8 * wave + (lane >> 3);
     const int a_voff = a_row * K * 2 + 16 * ((lane & 15) ^ (a_row & 15));
     const int b_voff = b_feat * K + 16 * ((lane & 7) ^ ((b_feat >> 1) & 7));
@@ -87,8 +140,7 @@ __global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *
             bload16_lds(ra[m], st + 1024 * (wave + 8 * m), a_voff, 2 * k0);
 #pragma unroll
         for (int m = 0; m < 5; ++m)
-            if (wave + 8 * m < 36)
-                bload16_lds(rw[m], st + kPfAStage + 1024 * (wave + 8 * m), b_voff, k0);
+            bload16_lds(rw[m], st + kPfAStage + 1024 * (wave + 8 * m), b_voff, k0);
     };
 
     f32x4 acc[4][kPfFeatTiles];
@@ -98,13 +150,13 @@ __global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *
         for (int ft = 0; ft < kPfFeatTiles; ++ft)
             acc[rt][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    // Tile scales: lane ft (< 9) of each wave loads the chunk's scale of the
+    // Tile scales: lane ft (< 5) of each wave loads the chunk's scale of the
     // wave's feature tile ft (its 128-feature scale tile, clamped: tiles past
     // M multiply zeros), one chunk ahead like the operands; the FMAs read it
     // back with a lane read.  (A scalar load here would share its wait
     // counter with the LDS reads and stall every one of them.)
     const rsrc_t rts = make_rsrc(ts, (uint32_t)nft * (uint32_t)nch * 4u);
-    const int ts_off = lane < kPfFeatTiles ? min((fb + fg * 144 + lane * 16) >> 7, nft - 1) * nch * 4 : kPfOut;
+    const int ts_off = lane < kPfFeatTiles ? min((fb + fg * 80 + lane * 16) >> 7, nft - 1) * nch * 4 : kPfOut;
     const int b_sw = (j >> 1) & 7;
 
     issue(0, 0);
@@ -119,45 +171,48 @@ __global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *
         }
         const uint8_t *st = lds + (c & 1) * kPfStage;
         const uint8_t *as = st + (rg * 64 + j) * 256;
-        const uint8_t *bs = st + kPfAStage + (fg * 144 + j) * 128 + 8 * (g & 1);
-        u32x4 a[4][2];
+        const uint8_t *bs = st + kPfAStage + (fg * 80 + j) * 128 + 8 * (g & 1);
+        u32x4 a[4][4];  // the wave's 4 row tiles, 4 steps
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)  // step 2 kh + s2: bytes 64 step + 16 g
-                a[rt][s2] = *reinterpret_cast<const u32x4 *>(as + rt * 16 * 256 + 16 * ((4 * (2 * kh + s2) + g) ^ j));
-        float sc[kPfFeatTiles];  // the chunk's tile scale of each feature tile
+            for (int s = 0; s < 4; ++s)  // step s: bytes 64 s + 16 g
+                a[rt][s] = *reinterpret_cast<const u32x4 *>(as + rt * 16 * 256 + 16 * ((4 * s + g) ^ j));
+        float sc[kPfFeatTiles];
 #pragma unroll
         for (int ft = 0; ft < kPfFeatTiles; ++ft)
             sc[ft] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(scale_bits, ft));
 #pragma unroll
         for (int ft = 0; ft < kPfFeatTiles; ++ft) {
-            u32x4 b[2];
+            f32x4 part[4] = {zero4, zero4, zero4, zero4};  // this chunk's partial, from zero
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {  // bytes 32 step + 8 g
-                const u32x2 wv = *reinterpret_cast<const u32x2 *>(bs + ft * 16 * 128 +
-                                                                  16 * ((2 * (2 * kh + s2) + (g >> 1)) ^ b_sw));
-                b[s2] = u32x4{A16::template fp8x2<false>(wv[0]), A16::template fp8x2<true>(wv[0]),
-                              A16::template fp8x2<false>(wv[1]), A16::template fp8x2<true>(wv[1])};
+            for (int s = 0; s < 4; ++s) {  // bytes 32 s + 8 g
+                const u32x2 wv =
+                    *reinterpret_cast<const u32x2 *>(bs + ft * 16 * 128 + 16 * ((2 * s + (g >> 1)) ^ b_sw));
+                const u32x4 b = u32x4{A16::template fp8x2<false>(wv[0]), A16::template fp8x2<true>(wv[0]),
+                                      A16::template fp8x2<false>(wv[1]), A16::template fp8x2<true>(wv[1])};
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    part[rt] = A16::mfma(a[rt][s], b, part[rt]);
             }
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const f32x4 part = A16::mfma(a[rt][1], b[1], A16::mfma(a[rt][0], b[0], zero4));
+            for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    acc[rt][ft][r] = __builtin_fmaf(sc[ft], part[r], acc[rt][ft][r]);
-            }
+                    acc[rt][ft][r] = __builtin_fmaf(sc[ft], part[rt][r], acc[rt][ft][r]);
         }
         // unconditional (nothing is outstanding after the last chunk): a
-        // branch here let the compiler sink the scale FMAs past it, keeping
-        // every partial tile live at once
+        // branch here let the compiler sink the scale FMAs past it
         wait_vmcnt<0>();
         __syncthreads();
     }
 
-    // k halves added in a fixed order (kh 0 + kh 1) and the tile stored as
-    // whole rows
-    prefill_store_tile<kPfFeatTiles>(acc, lds, lane, fg, rg, kh, out, out_dtype, N, M, rb, fb, 1.0f);
+    if (out_dtype == VQ_DTYPE_F32)
+        store_tile<VQ_DTYPE_F32>(acc, lds, lane, fg, rg, out, N, M, rb, fb);
+    else if (out_dtype == VQ_DTYPE_BF16)
+        store_tile<VQ_DTYPE_BF16>(acc, lds, lane, fg, rg, out, N, M, rb, fb);
+    else
+        store_tile<VQ_DTYPE_F16>(acc, lds, lane, fg, rg, out, N, M, rb, fb);
 }
 
 template <int ACT>
