@@ -19,7 +19,8 @@
 // 220 workgroups on 256 CUs).  Wave (rg, fg) takes rows 64 rg .. +64 and
 // features 80 fg .. +80 over all of K: per chunk 4 row tiles x 5 feature
 // tiles x 4 steps = 80 MFMAs, each converted weight operand serving the 4
-// row tiles, and one scale FMA per output.  (A 128 x 288 tiling with the
+// row tiles, and one scale FMA per output.  A lane reads 16 codes of a
+// feature (two MFMA steps) with one 16-byte LDS read.  (A 128 x 288 tiling with the
 // chunk's steps split between two waves took two scale FMAs per output and
 // chunk and was about 3% slower.)  Chunks (activations 128 rows x 256 B,
 // codes 320 features x 128 B) are loaded straight into LDS (16 B per lane,
@@ -171,13 +172,19 @@ __global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *
         }
         const uint8_t *st = lds + (c & 1) * kPfStage;
         const uint8_t *as = st + (rg * 64 + j) * 256;
-        const uint8_t *bs = st + kPfAStage + (fg * 80 + j) * 128 + 8 * (g & 1);
+        const uint8_t *bs = st + kPfAStage + (fg * 80 + j) * 128;
+        // The k order of the MFMA steps: lane group g of step s takes k = 16 (4
+        // (s / 2) + g) + 8 (s % 2) .. +8, so that one 16-byte read of a
+        // feature's codes (k = 16 (4 pr + g) .. +16) feeds steps 2 pr and
+        // 2 pr + 1; the activations follow the same order (the MFMA sums its
+        // 32 products in any k order both operands share).
         u32x4 a[4][4];  // the wave's 4 row tiles, 4 steps
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int s = 0; s < 4; ++s)  // step s: bytes 64 s + 16 g
-                a[rt][s] = *reinterpret_cast<const u32x4 *>(as + rt * 16 * 256 + 16 * ((4 * s + g) ^ j));
+            for (int s = 0; s < 4; ++s)  // 16-byte piece 8 (s / 2) + 2 g + s % 2 of the row
+                a[rt][s] = *reinterpret_cast<const u32x4 *>(
+                    as + rt * 16 * 256 + 16 * ((8 * (s >> 1) + 2 * g + (s & 1)) ^ j));
         float sc[kPfFeatTiles];
 #pragma unroll
         for (int ft = 0; ft < kPfFeatTiles; ++ft)
@@ -186,14 +193,18 @@ __global__ __launch_bounds__(kPfThreads) void fp8_prefill_kernel(const uint8_t *
         for (int ft = 0; ft < kPfFeatTiles; ++ft) {
             f32x4 part[4] = {zero4, zero4, zero4, zero4};  // this chunk's partial, from zero
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {  // bytes 32 s + 8 g
-                const u32x2 wv =
-                    *reinterpret_cast<const u32x2 *>(bs + ft * 16 * 128 + 16 * ((2 * s + (g >> 1)) ^ b_sw));
-                const u32x4 b = u32x4{A16::template fp8x2<false>(wv[0]), A16::template fp8x2<true>(wv[0]),
-                                      A16::template fp8x2<false>(wv[1]), A16::template fp8x2<true>(wv[1])};
+            for (int pr = 0; pr < 2; ++pr) {  // codes k = 16 (4 pr + g) .. +16: steps 2 pr, 2 pr + 1
+                const u32x4 wv =
+                    *reinterpret_cast<const u32x4 *>(bs + ft * 16 * 128 + 16 * ((4 * pr + g) ^ b_sw));
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    part[rt] = A16::mfma(a[rt][s], b, part[rt]);
+                for (int h = 0; h < 2; ++h) {
+                    const u32x4 b = u32x4{A16::template fp8x2<false>(wv[2 * h]), A16::template fp8x2<true>(wv[2 * h]),
+                                          A16::template fp8x2<false>(wv[2 * h + 1]),
+                                          A16::template fp8x2<true>(wv[2 * h + 1])};
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt)
+                        part[rt] = A16::mfma(a[rt][2 * pr + h], b, part[rt]);
+                }
             }
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
