@@ -49,12 +49,13 @@ def test_dtype_combinations_parity(act, out):
     parity(y, oracle.gemm_fp8_blk128(f["w"], f["tscales"], x, ORACLE_DT[act], N, M, K), out)
 
 
-def test_integer_case_bit_exact():
+@pytest.mark.parametrize("N,M,K", [(160, 256, 768), (130, 700, 384), (257, 961, 256)])
+def test_integer_case_bit_exact(N, M, K):
     """E4M3 codes of small integers, power-of-two tile scales and integer rows:
     every partial sum is an exact fp32 integer multiple, so the output equals
-    the exact oracle bit for bit."""
-    g = np.random.Generator(np.random.PCG64(811))
-    N, M, K = 160, 256, 768
+    the exact oracle bit for bit (one ragged workgroup tile, and several
+    320-feature tiles with ragged last ones in both directions)."""
+    g = np.random.Generator(np.random.PCG64(811 + M))
     ints = {0x38: 1.0, 0x40: 2.0, 0x44: 3.0, 0x48: 4.0, 0xB8: -1.0, 0xC0: -2.0, 0x00: 0.0}
     w = g.choice(np.array(list(ints), dtype=np.uint8), size=(M, K))
     ts = np.ldexp(1.0, g.integers(-3, 3, size=((M + 127) // 128, K // 128))).astype(np.float32)
