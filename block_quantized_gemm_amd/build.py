@@ -33,18 +33,18 @@ HIPCC_FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments arrive in SGPRs, written by the command
+    # processor before the first instruction (at most 16 user SGPRs: the
+    # kernel-argument pointer and up to 14 argument dwords), which saves the
+    # memory round trip that reading them would cost at kernel start
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I" + INCLUDE,
     "-I" + CSRC,
 ]
 
 
-# Per-source additions.  The walk kernel's leading scalar arguments are
-# preloaded into SGPRs by the command processor (at most 16 user SGPRs: the
-# kernel-argument pointer and 13 arguments), which saves the memory round trip
-# that reading them would cost at kernel start.
-SOURCE_FLAGS = {
-    "verify_gemm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=13"],
-}
+# Per-source additions (none at present).
+SOURCE_FLAGS = {}
 
 
 def hipcc() -> str:
