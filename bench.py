@@ -869,8 +869,8 @@ def probe_part(args, dev, stream):
     """The library's HBM read probe over 2 GiB: one workgroup per 64 KiB, and
     one persistent workgroup per CU in contiguous shares and as a sweeping
     window, with the default and the non-temporal cache policy; then the
-    rate of L2 hits (each workgroup re-reading its 64 KiB), kept out of
-    best_gbs."""
+    rate of L2 hits (each workgroup re-reading its 64 KiB) and the LDS read
+    rate per CU, kept out of best_gbs."""
     import torch
     import block_quantized_gemm_amd as vq
     nbytes = 1 << 31
@@ -894,6 +894,12 @@ def probe_part(args, dev, stream):
                                           stream=s), stream, args.reps, args.warmup, inner=32)
     res["reread_l2_%d_w8_d8" % cus] = rate(t, small.numel() * vq.PROBE_REREAD_PASSES, 1e9)
     res["reread_l2_gbs_per_cu"] = round(res["reread_l2_%d_w8_d8" % cus]["median"] / cus, 1)
+    # the LDS read rate: every workgroup reads 32 MiB from its 64 KiB of LDS
+    lds_bytes = 32 << 20
+    t = timed(lambda s: vq.hbm_read_probe(buf[:lds_bytes], sink, mode="lds", groups=cus, waves_per_group=8,
+                                          depth=8, stream=s), stream, args.reps, args.warmup, inner=4)
+    res["lds_read_%d_w8_d8" % cus] = rate(t, cus * lds_bytes, 1e9)
+    res["lds_read_gbs_per_cu"] = round(res["lds_read_%d_w8_d8" % cus]["median"] / cus, 1)
     del buf
     return res
 

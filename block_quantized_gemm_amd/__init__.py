@@ -38,8 +38,10 @@ PROBE_BLOCKS = 0
 PROBE_SHARES = 1
 PROBE_WINDOW = 2
 PROBE_REREAD = 3
+PROBE_LDS = 4
 PROBE_REREAD_PASSES = 16
-_PROBES = {"blocks": PROBE_BLOCKS, "shares": PROBE_SHARES, "window": PROBE_WINDOW, "reread": PROBE_REREAD}
+_PROBES = {"blocks": PROBE_BLOCKS, "shares": PROBE_SHARES, "window": PROBE_WINDOW, "reread": PROBE_REREAD,
+           "lds": PROBE_LDS}
 
 DTYPE_F16 = 1
 DTYPE_BF16 = 2
@@ -657,7 +659,10 @@ def hbm_read_probe(buf, sink, *, mode: str = "blocks", groups: int = 0, waves_pe
     (`groups` persistent workgroups, contiguous shares), "window" (`groups`
     persistent workgroups sweeping 64 KiB blocks) or "reread" (as "shares",
     each share read PROBE_REREAD_PASSES times within the launch: the rate of
-    L2 hits once a share fits in L2); nontemporal: the loads' cache policy."""
+    L2 hits once a share fits in L2) or "lds" (`groups` workgroups each copy
+    the first 64 KiB into LDS and read the buffer's byte count from LDS: the
+    LDS read rate per CU; nontemporal False); nontemporal: the loads' cache
+    policy."""
     if mode not in _PROBES:
         raise ValueError("mode must be one of %s" % sorted(_PROBES))
     if sink.numel() * sink.element_size() < 4:

@@ -17,7 +17,11 @@
 //   window  -- `groups` persistent workgroups reading 64 KiB blocks b, b + G,
 //              b + 2G, ... (the whole grid sweeps one contiguous window);
 //   reread  -- as shares, each share read VQ_PROBE_REREAD_PASSES times over
-//              in the launch (after the first pass, from L2 if it fits).
+//              in the launch (after the first pass, from L2 if it fits);
+//   lds     -- `groups` workgroups each stage the buffer's first 64 KiB in
+//              LDS and read `bytes` from it (16 bytes per lane, consecutive
+//              lanes on consecutive 16 bytes): the LDS read rate of a CU,
+//              for the prefill GEMMs' budgets.
 // Each wave keeps `depth` loads in flight.  The loads use the default cache
 // policy or the non-temporal one (a stream read once: on gfx950 the latter
 // reaches a higher read rate).
@@ -82,6 +86,56 @@ __global__ __launch_bounds__(64 * W) void hbm_probe_kernel(const ProbeArgs a) {
         a.sink[0] = x;
 }
 
+constexpr int kLdsProbeBytes = 64 * 1024;
+
+// D reads of 1 KiB per wave and iteration, from D distinct rows of the wave's
+// 16 KiB window (four windows, each shared by the waves w with the same w % 4).
+// Each read's 16 bytes are handed to an empty asm statement and one of its
+// words goes into the XOR: one VALU instruction per read, so that the reads,
+// not the folding (four XORs per read would take as many VALU cycles per CU
+// as the LDS takes to deliver the bytes), set the rate.
+template <int W, int D>
+__global__ __launch_bounds__(64 * W) void lds_probe_kernel(const ProbeArgs a) {
+    static_assert(D % 2 == 0 && D <= 16, "pairs of reads, at most 16 rows");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const rsrc_t r = make_rsrc(a.buf, kLdsProbeBytes);
+    for (int i = (int)threadIdx.x; i < kLdsProbeBytes / 16; i += 64 * W)
+        *reinterpret_cast<u32x4 *>(lds + 16 * i) = bload16<kAuxCached>(r, 16 * i, 0);
+    __syncthreads();
+    // every read is below 3 * 16 KiB + 15 KiB + 1 KiB = 64 KiB
+    const uint8_t *win = lds + (wave & 3) * 16384 + 16 * lane;
+    const int iters = (int)(a.bytes / kPiece) / (W * D);
+    u32x4 acc = {0u, 0u, 0u, 0u};  // only acc[0] is used
+    int off = 0;
+    for (int it = 0; it < iters; ++it) {
+        asm volatile("" : "+v"(off));  // off stays 0, but the compiler cannot see the reads repeat
+        u32x4 v[D];
+#pragma unroll
+        for (int q = 0; q < D; ++q)
+            v[q] = *reinterpret_cast<const u32x4 *>(win + off + kPiece * q);
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+            asm volatile("" ::"v"(v[q]));  // all 16 bytes are used: the reads stay 16-byte reads
+            acc[0] ^= v[q][q & 3];
+        }
+    }
+    const uint32_t x = acc[0];
+    if (x == a.sentinel)
+        a.sink[0] = x;
+}
+
+template <int W>
+hipError_t launch_lds(const ProbeArgs &a, int grid, int depth, hipStream_t s) {
+    switch (depth) {
+    case 4: hipLaunchKernelGGL((lds_probe_kernel<W, 4>), dim3(grid), dim3(64 * W), kLdsProbeBytes, s, a); break;
+    case 8: hipLaunchKernelGGL((lds_probe_kernel<W, 8>), dim3(grid), dim3(64 * W), kLdsProbeBytes, s, a); break;
+    case 16: hipLaunchKernelGGL((lds_probe_kernel<W, 16>), dim3(grid), dim3(64 * W), kLdsProbeBytes, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <int W, int AUX, bool RR>
 hipError_t launch_rr(const ProbeArgs &a, int grid, int depth, hipStream_t s) {
     switch (depth) {
@@ -114,6 +168,14 @@ hipError_t launch_aux(const ProbeArgs &a, int grid, int waves, int depth, hipStr
 hipError_t launch_hbm_probe(const void *buf, size_t bytes, int mode, int groups, int waves, int depth,
                             bool nontemporal, uint32_t *sink, hipStream_t stream) {
     ProbeArgs a{static_cast<const uint8_t *>(buf), (uint32_t)bytes, mode, 0u, 0x9E3779B9u, sink};
+    if (mode == VQ_PROBE_LDS) {
+        switch (waves) {
+        case 4: return launch_lds<4>(a, groups, depth, stream);
+        case 8: return launch_lds<8>(a, groups, depth, stream);
+        case 16: return launch_lds<16>(a, groups, depth, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
     if (mode == VQ_PROBE_SHARES || mode == VQ_PROBE_REREAD)
         a.share = (uint32_t)(bytes / (size_t)groups);
     const int grid = mode == VQ_PROBE_BLOCKS ? (int)(bytes / kBlock) : groups;

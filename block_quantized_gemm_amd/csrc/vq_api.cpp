@@ -665,7 +665,8 @@ int vq_hbm_read_probe(const void *buf, size_t bytes, int mode, int groups, int w
         return VQ_ERR_MISALIGNED;
     if (bytes < 65536 || bytes > ((size_t)1 << 31) || bytes % 65536 != 0)
         return VQ_ERR_BAD_SHAPE;
-    if (mode != VQ_PROBE_BLOCKS && mode != VQ_PROBE_SHARES && mode != VQ_PROBE_WINDOW && mode != VQ_PROBE_REREAD)
+    if (mode != VQ_PROBE_BLOCKS && mode != VQ_PROBE_SHARES && mode != VQ_PROBE_WINDOW && mode != VQ_PROBE_REREAD &&
+        mode != VQ_PROBE_LDS)
         return VQ_ERR_BAD_CONFIG;
     if ((waves_per_group != 4 && waves_per_group != 8 && waves_per_group != 16) ||
         (depth != 4 && depth != 8 && depth != 16))
@@ -674,6 +675,10 @@ int vq_hbm_read_probe(const void *buf, size_t bytes, int mode, int groups, int w
         return VQ_ERR_BAD_CONFIG;
     if (nontemporal != 0 && nontemporal != 1)
         return VQ_ERR_BAD_CONFIG;
+    if (mode == VQ_PROBE_LDS && nontemporal != 0)  // LDS reads have no cache policy
+        return VQ_ERR_BAD_CONFIG;
+    if (mode == VQ_PROBE_LDS && bytes % ((size_t)waves_per_group * (size_t)depth * 1024) != 0)
+        return VQ_ERR_BAD_SHAPE;
     if ((mode == VQ_PROBE_SHARES || mode == VQ_PROBE_REREAD) &&
         bytes % ((size_t)groups * (size_t)waves_per_group * 1024) != 0)
         return VQ_ERR_BAD_SHAPE;

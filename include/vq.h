@@ -493,6 +493,14 @@ size_t vq_greedy_workspace_bytes(int64_t n_rows, int64_t vocab);
  *                    `bytes` (the rate of L2 hits per CU, not of HBM);
  *                    bytes / (groups * waves_per_group * 1024) must be a
  *                    power of two;
+ *   VQ_PROBE_LDS     `groups` workgroups each copy the first 64 KiB of `buf`
+ *                    into LDS, then read `bytes` from LDS (`depth` reads of
+ *                    16 bytes per lane in flight per wave, consecutive lanes
+ *                    on consecutive 16 bytes): the launch reads groups *
+ *                    bytes from LDS and 64 KiB per workgroup from memory,
+ *                    the LDS read rate per CU that the prefill GEMMs'
+ *                    budgets use; nontemporal must be 0 and bytes % (1024 *
+ *                    waves_per_group * depth) == 0;
  * waves_per_group 4, 8 or 16; depth (loads in flight per wave) 4, 8 or 16;
  * nontemporal 0 (default cache policy) or 1 (non-temporal loads, the policy
  * of a stream read once); 65536 <= bytes <= 2^31, bytes % 65536 == 0;
@@ -503,6 +511,7 @@ size_t vq_greedy_workspace_bytes(int64_t n_rows, int64_t vocab);
 #define VQ_PROBE_SHARES 1
 #define VQ_PROBE_WINDOW 2
 #define VQ_PROBE_REREAD 3
+#define VQ_PROBE_LDS 4
 #define VQ_PROBE_REREAD_PASSES 16
 int vq_hbm_read_probe(const void *buf, size_t bytes, int mode, int groups, int waves_per_group, int depth,
                       int nontemporal, uint32_t *sink, void *stream);

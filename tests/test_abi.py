@@ -369,7 +369,9 @@ def test_hbm_probe_argument_errors():
     assert probe(nbytes=65536 + 1024) == vq.VQ_ERR_BAD_SHAPE
     assert probe(nbytes=0) == vq.VQ_ERR_BAD_SHAPE
     assert probe(nbytes=(1 << 31) + 65536) == vq.VQ_ERR_BAD_SHAPE
-    assert probe(mode=4) == vq.VQ_ERR_BAD_CONFIG
+    assert probe(mode=5) == vq.VQ_ERR_BAD_CONFIG
+    assert probe(mode=vq.PROBE_LDS, groups=0) == vq.VQ_ERR_BAD_CONFIG
+    assert probe(mode=vq.PROBE_LDS, groups=16, nt=1) == vq.VQ_ERR_BAD_CONFIG  # LDS reads have no cache policy
     assert probe(mode=vq.PROBE_REREAD, groups=0) == vq.VQ_ERR_BAD_CONFIG
     assert probe(mode=vq.PROBE_REREAD, groups=3) == vq.VQ_ERR_BAD_SHAPE  # 1 MiB is not 3 equal shares
     assert probe(nbytes=3 << 20, mode=vq.PROBE_REREAD, groups=1) == vq.VQ_ERR_BAD_SHAPE  # 384 pieces per wave
@@ -384,6 +386,7 @@ def test_hbm_probe_argument_errors():
     if not torch.cuda.is_available():
         assert probe(mode=vq.PROBE_SHARES, groups=16) == vq.VQ_ERR_DEVICE
         assert probe(nbytes=3 << 20, mode=vq.PROBE_REREAD, groups=3) == vq.VQ_ERR_DEVICE  # 128 pieces per wave
+        assert probe(mode=vq.PROBE_LDS, groups=3) == vq.VQ_ERR_DEVICE
 
 
 def test_noalloc_argument_errors():
