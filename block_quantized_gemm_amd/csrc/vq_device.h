@@ -155,10 +155,12 @@ __device__ __forceinline__ uint32_t bload2(rsrc_t r, int voff, int soff) {
 // 16 bytes per lane from a buffer straight into LDS (no registers): lane l's
 // bytes land at lds_dst + 16 l, whatever its source offset (voff + the
 // wave-uniform soff); out-of-range offsets deliver zeros.  lds_dst must be wave-uniform.  The load counts in
-// vmcnt like any other: wait for it before the LDS is read.
+// vmcnt like any other: wait for it before the LDS is read.  AUX: the cache
+// policy, as for bload16.
+template <int AUX = kAuxCached>
 __device__ __forceinline__ void bload16_lds(rsrc_t r, void *lds_dst, int voff, int soff = 0) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_dst, 16, voff, soff, 0,
-                                             0);
+                                             AUX);
 }
 
 // s_waitcnt that waits until at most n vector-memory operations are
