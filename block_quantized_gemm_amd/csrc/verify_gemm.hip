@@ -716,7 +716,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         // weights, on every path: the compiler's waits for those weights
         // then never include the staging.
         act_for(nref, grp.p[nref.pi], it + 1 < ie, par ^ 1);
-        scales_for(nref, grp.p[nref.pi], it + 1 < ie, par ^ 1);
+        if constexpr (PANEL && !FP8)  // nref's scale rows, through the resource nxt already holds for its record
+            bload16_lds<kAuxStream>(nxt.rw, sc_wave + (par ^ 1) * kScBuf, kPanelCodeBytes + wave * 1024 + 16 * lane);
+        else
+            scales_for(nref, grp.p[nref.pi], it + 1 < ie, par ^ 1);
         const KProblem &ca = grp.p[cref.pi];
         const uint8_t *abuf = row + par * kActBuf;
         const uint16_t *sc0 = reinterpret_cast<const uint16_t *>(sc_wave + par * kScBuf) + j * scrow;
